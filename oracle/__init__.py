@@ -1,0 +1,30 @@
+"""CPU reference (test infrastructure only).
+
+Plain, slow, obviously correct float64 NumPy code for what the paged decode
+path computes. Only the test suite, the smoke entry point and the benchmark's
+CPU-baseline leg may import this package; the library under
+``paged_kv_cache_156_amd`` never does, and this package imports nothing from it.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against figures the
+pages print, closed forms, library routines (torch's fp64 SDPA on the CPU) or
+brute force. No function here is "parity unpinned".
+"""
+from .accounting import (  # noqa: F401
+    kv_cache_bytes,
+    kv_bytes_per_token,
+    ragged_kv_cache_bytes,
+    block_bytes,
+    blocks_for,
+    block_capacity,
+    empty_slots,
+)
+from .paged_decode import (  # noqa: F401
+    upcast,
+    slot_address,
+    slot_mapping,
+    gather_sequence,
+    attention_weights,
+    decode_attention,
+    decode_attention_seq,
+    kv_append,
+)

@@ -1,0 +1,148 @@
+"""Paged decode attention and KV append, as plain float64 NumPy.
+
+Test infrastructure only (see the package docstring). The computation is the
+plain definition: gather the sequence's cached K/V through its block table into
+contiguous arrays, then run dense softmax attention for the single new query.
+
+Storage conventions shared with the inputs (not with the GPU code):
+  * caches are raw arrays of shape [num_blocks, num_kv_heads, block_size,
+    head_dim] (HND), element type float32 ("f32"), float16 ("f16") or uint16
+    holding bfloat16 bits ("bf16");
+  * q is [num_seqs, num_heads, head_dim], k/v of the new token are
+    [num_seqs, num_kv_heads, head_dim], in the same raw storage;
+  * context_lens[b] counts the tokens attended by sequence b, the newest one
+    included (the query at position n-1 sees positions 0..n-1).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def upcast(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact conversion of stored values to float64 (every f32/f16/bf16 value
+    is representable in float64)."""
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(raw, dtype=np.float16).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(raw, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def slot_address(position: int, table_row: Sequence[int], block_size: int):
+    """Two-level slot addressing of one token.
+
+    Page "Understanding KV Cache" (steinslab.io), §3.3 "Slot addressing":
+    logical block = floor(i / block_size), offset = i mod block_size,
+    physical block = block_table[logical block], and the flat slot number is
+    physical block x block_size + offset. Returns all four.
+    """
+    lb = position // block_size
+    off = position % block_size
+    pb = int(table_row[lb])
+    return lb, off, pb, pb * block_size + off
+
+
+def slot_mapping(block_tables: np.ndarray, positions: Sequence[int], block_size: int) -> np.ndarray:
+    """Slot of each sequence's token at ``positions[b]``; a negative position
+    (a padding entry) maps to slot -1, which the append skips."""
+    out = np.empty(len(positions), dtype=np.int64)
+    for b, pos in enumerate(positions):
+        pos = int(pos)
+        out[b] = -1 if pos < 0 else slot_address(pos, block_tables[b], block_size)[3]
+    return out
+
+
+def gather_sequence(cache: np.ndarray, dtype: str, table_row: Sequence[int], n: int,
+                    kv_head: int, block_size: int) -> np.ndarray:
+    """Contiguous float64 [n, head_dim] copy of one KV head of one sequence.
+
+    The attention kernel collects K/V from the physical blocks the block table
+    names, in logical order (page "KV Cache and Inference Optimization",
+    section "PagedAttention: manage the KV cache like virtual memory"); token i
+    lives at (physical block, offset) from ``slot_address``.
+    """
+    head_dim = cache.shape[-1]
+    out = np.empty((n, head_dim), dtype=np.float64)
+    for i in range(n):
+        _, off, pb, _ = slot_address(i, table_row, block_size)
+        out[i] = upcast(cache[pb, kv_head, off], dtype)
+    return out
+
+
+def attention_weights(q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax over the scaled scores of one query against n keys.
+
+    alpha_j = exp(q.K_j * scale) / sum_l exp(q.K_l * scale): the attention
+    weights of §1.1 of the page "The KV Cache Problem of Traditional Attention"
+    (pyllm.pages.dev) with scale = 1/sqrt(d_k), and the softmax of §1.2 of the
+    page "Understanding KV Cache". The maximum score is subtracted before
+    exponentiating; that leaves every ratio unchanged and keeps exp finite.
+    """
+    s = (K @ q) * scale
+    e = np.exp(s - s.max())
+    return e / e.sum()
+
+
+def decode_attention_seq(q_b: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                         table_row: Sequence[int], n: int, scale: float, num_kv_heads: int,
+                         block_size: int, dtype: str) -> np.ndarray:
+    """Output [num_heads, head_dim] (float64) of one sequence's decode step.
+
+    Query head h reads KV head h // (num_heads / num_kv_heads): consecutive
+    query heads share one KV head (page "KV Cache and Inference Optimization",
+    section "Three attention layouts", GQA diagram). Decode at position n-1 is
+    row n-1 of causal attention: the mask lets it see positions 0..n-1 (§1.2
+    and §2.2 of the page "Understanding KV Cache"). n = 0 yields zeros.
+    """
+    num_heads, head_dim = q_b.shape
+    if num_heads % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    group = num_heads // num_kv_heads
+    out = np.zeros((num_heads, head_dim), dtype=np.float64)
+    if n == 0:
+        return out
+    qf = upcast(q_b, dtype)
+    for j in range(num_kv_heads):
+        K = gather_sequence(k_cache, dtype, table_row, n, j, block_size)
+        V = gather_sequence(v_cache, dtype, table_row, n, j, block_size)
+        for h in range(j * group, (j + 1) * group):
+            alpha = attention_weights(qf[h], K, scale)
+            out[h] = alpha @ V
+    return out
+
+
+def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                     block_tables: np.ndarray, context_lens: Sequence[int], scale: float,
+                     num_kv_heads: int, block_size: int, dtype: str,
+                     seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Output [num_seqs, num_heads, head_dim] float64. With ``seqs`` only
+    those sequences are computed and the other rows are NaN."""
+    B, Hq, D = q.shape
+    out = np.full((B, Hq, D), np.nan, dtype=np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        out[b] = decode_attention_seq(q[b], k_cache, v_cache, block_tables[b], int(context_lens[b]),
+                                      scale, num_kv_heads, block_size, dtype)
+    return out
+
+
+def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+              slots: Sequence[int], block_size: int) -> None:
+    """Write each new token's K and V (all KV heads) into its slot, in place.
+
+    The cache is an append-only log: each generated token adds one K/V record
+    (§1.3 of the page "Understanding KV Cache"); slot s is offset s mod
+    block_size of physical block s // block_size (§3.3). Slot -1 is skipped.
+    Raw bytes are copied, so the write is exact.
+    """
+    for i, s in enumerate(slots):
+        s = int(s)
+        if s < 0:
+            continue
+        pb, off = s // block_size, s % block_size
+        k_cache[pb, :, off, :] = k_new[i]
+        v_cache[pb, :, off, :] = v_new[i]
