@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of libpkv on one MI355X.
+
+One step = for every layer: append the new token's K/V (kv_append), then
+paged decode attention over the whole cache (partition kernel + LSE merge).
+Default workload: Llama-3-70B shape (64 query / 8 KV heads, head_dim 128,
+bf16), batch 32, context 4096, 80 layers looped, each layer with its own
+K/V pool (40 GiB resident) and one block table shared by the layers, built
+by libpkv's block pool from a seeded permutation.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--layers L]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth, decimal GB/s
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_156_amd", "csrc", "pkv_kernels.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pool_assignment(cfg, lens, pkv, wl):
+    """Block lists, slot mapping and tables from libpkv's host block pool."""
+    bs = cfg.block_size
+    B = len(lens)
+    n_pref = cfg.shared_prefix_tokens // bs
+    share = [min(n_pref, (int(n) - 1) // bs) if (n_pref and n > 0) else 0 for n in lens]
+    need = (n_pref if any(share) else 0) + sum(-(-int(n) // bs) - s for n, s in zip(lens, share))
+    pool = pkv.BlockPool(max(need, 1), bs, max_seqs=B + 1, seed=cfg.seed)
+    owner = B  # bookkeeping sequence that holds the shared prefix blocks
+    if any(share):
+        pool.grow(owner, n_pref * bs)
+    for b, n in enumerate(lens):
+        if share[b]:
+            pool.share_prefix(b, owner, share[b] * bs)
+        pool.grow(b, int(n))
+    blocks = [pool.seq_info(b)[1] for b in range(B)]
+    shared_ids = pool.seq_info(owner)[1] if any(share) else np.zeros(0, np.int32)
+    poison = max(need, 1)  # one extra block past the pool: NaN, target of table padding
+    slots = pool.slot_mapping(np.arange(B), np.asarray(lens) - 1)
+    asg = wl.BlockAssignment(blocks, poison + 1, poison, shared_ids.astype(np.int32), share)
+    return asg, slots, pool.stats()
+
+
+def cpu_samples(wkd, max_seqs=32):
+    """Host copies of layer 0's first sequences, taken before any append, for
+    timing the CPU reference."""
+    import torch
+    from paged_kv_cache_156_amd import workloads as wl
+    cfg = wkd.cfg
+    dt = cfg.dtype
+    samples = []
+    for b in range(len(wkd.context_lens)):
+        blocks = wkd.assignment.blocks[b]
+        idx = torch.from_numpy(blocks.astype(np.int64)).to(wkd.k_cache[0].device)
+        samples.append(dict(
+            kc=wl.torch_to_raw(wkd.k_cache[0].index_select(0, idx), dt),
+            vc=wl.torch_to_raw(wkd.v_cache[0].index_select(0, idx), dt),
+            q=wl.torch_to_raw(wkd.q[0][b:b + 1], dt), kn=wl.torch_to_raw(wkd.k_new[0][b:b + 1], dt),
+            vn=wl.torch_to_raw(wkd.v_new[0][b:b + 1], dt), n=int(wkd.context_lens[b]),
+            table=np.arange(len(blocks), dtype=np.int32)[None, :]))
+        if len(samples) >= max_seqs:
+            break
+    return samples
+
+
+def run_cpu_baseline(samples, cfg, budget_s):
+    """Time the CPU reference, one thread, until ``budget_s`` of work is done."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _run_cpu(samples, cfg, budget_s, oracle)
+
+
+def _run_cpu(samples, cfg, budget_s, oracle):
+    done, kv_bytes, t_total = 0, 0, 0.0
+    for s in samples:
+        t0 = time.perf_counter()
+        kc, vc = s["kc"].copy(), s["vc"].copy()
+        slots = oracle.slot_mapping(s["table"], [s["n"] - 1], cfg.block_size)
+        oracle.kv_append(kc, vc, s["kn"], s["vn"], slots, cfg.block_size)
+        oracle.decode_attention(s["q"], kc, vc, s["table"], [s["n"]], cfg.scale, cfg.num_kv_heads, cfg.block_size,
+                                cfg.dtype)
+        t_total += time.perf_counter() - t0
+        done += 1
+        kv_bytes += 2 * cfg.num_kv_heads * cfg.head_dim * (4 if cfg.dtype == "f32" else 2) * s["n"]
+        if t_total >= budget_s:
+            break
+    return done, kv_bytes, t_total
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama3_70b")
+    ap.add_argument("--layers", type=int, default=0, help="layers to loop (0 = the configuration's count)")
+    ap.add_argument("--partition-blocks", type=int, default=0, help="blocks per partition (0 = library choice)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU-reference work (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (no multi-GPU path exists)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_156_amd import binding as pkv
+    from paged_kv_cache_156_amd import workloads as wl
+
+    pkv.load()
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIG_BY_NAME[args.config]
+    L = args.layers or cfg.num_layers
+    _, _, r_len = wl.streams(cfg.seed)
+    lens = wl.draw_context_lens(cfg, r_len)
+    B, Hq, Hkv, D, bs = len(lens), cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    esz = wl.DTYPE_BYTES[cfg.dtype]
+
+    log(f"config {cfg.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} {cfg.dtype} layers={L} sum(ctx)={int(lens.sum())}")
+    asg, slots, pool_stats = pool_assignment(cfg, lens, pkv, wl)
+    log(f"block pool: {pool_stats}")
+    t0 = time.time()
+    wkd = wl.make_device_workload(cfg, dev, layers=L, context_lens=lens, assignment=asg,
+                                  progress=lambda l: (l % 20 == 0) and log(f"  drew layer {l}/{L}"))
+    torch.cuda.synchronize()
+    log(f"device workload ready in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
+
+    samples = cpu_samples(wkd) if args.cpu_budget > 0 else []
+
+    max_blocks = wkd.block_tables.shape[1]
+    pb = args.partition_blocks or pkv.decode_partition_blocks(B, Hq, Hkv, max_blocks)
+    ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables, pb)
+    slots_d = torch.from_numpy(slots).to(dev)
+    outs = [torch.empty_like(wkd.q[l]) for l in range(L)]
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for l in range(L):
+            pkv.kv_append(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_cache[l], wkd.v_cache[l])
+            if events is not None:
+                events[l][0].record(stream)
+            pkv.decode_partitions(wkd.q[l], wkd.k_cache[l], wkd.v_cache[l], wkd.block_tables, wkd.context_lens_dev,
+                                  cfg.scale, outs[l], ws, pb)
+            if events is not None:
+                events[l][1].record(stream)
+            pkv.decode_merge(wkd.q[l], wkd.k_cache[l], wkd.v_cache[l], wkd.block_tables, wkd.context_lens_dev,
+                             outs[l], ws, pb)
+
+    log(f"warmup {args.warmup} steps (partition_blocks={pb}, workspace {0 if ws is None else ws.numel()} B)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(o).all().item() for o in outs[:2]), "non-finite attention output"
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+              for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(events[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    part_ms = [ev[l][0].elapsed_time(ev[l][1]) for ev in events for l in range(L)]
+    part_avg_ms = float(np.mean(part_ms))
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; partition kernel avg {part_avg_ms * 1e3:.1f} us")
+
+    # algorithmic bytes
+    sum_n = int(lens.sum())
+    kv_layer = 2 * Hkv * D * esz * sum_n
+    q_out = 2 * B * Hq * D * esz
+    tables = 4 * sum(-(-int(n) // bs) for n in lens) + 4 * B
+    part_alg = kv_layer + q_out + tables
+    step_kv = kv_layer * L
+    gbs = step_kv / (ms_per_step * 1e-3) / 1e9
+    achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"decode_partition_{cfg.name}_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_sha() and tr.get("partition_blocks") == pb:
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if samples:
+        done, cpu_bytes, cpu_t = run_cpu_baseline(samples, cfg, args.cpu_budget)
+        seq_layer_s = cpu_t / done
+        cpu = {"value": round(cpu_bytes / cpu_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seqs_per_s": round(1.0 / (seq_layer_s * L), 4),
+               "sample": f"{done} sequence(s) x 1 layer of {cfg.name} (append + attention, fp64 NumPy, one "
+                         f"thread), {cpu_t:.1f}s; seqs/s extrapolated to {L} layers"}
+        log(f"cpu baseline: {cpu}")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2**20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b2 = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b2.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration_mib} MiB device-to-device copy done")
+
+    result = {
+        "metric": "paged decode attention K/V-read GB/s (% of HBM peak) and seqs/s at 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: batch {B}, context {'ragged' if cfg.context_len_range else int(lens[0])}, "
+                               f"{Hq} query / {Hkv} KV heads, head_dim {D}, block 16, {L} layers, one decode step "
+                               f"(append + attention) per layer",
+                   "global_batch": B, "seq_len": int(lens.max()), "layers": L, "partition_blocks": pb},
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "seqs_per_s": round(B / (ms_per_step * 1e-3), 2),
+        "kv_bytes_per_step": step_kv,
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": part_alg,
+                     "avg_launch_us": round(part_avg_ms * 1e3, 2), "kernel_sha": kernel_sha()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

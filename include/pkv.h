@@ -1,0 +1,275 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged KV-cache decode attention for MI355X (gfx950).
+ *
+ * The operation: for each sequence b and query head h, the newest query
+ * q[b,h,:] is scored against every cached key of KV head h / (Hq/Hkv),
+ * scores are scaled (normally by 1/sqrt(head_dim)), passed through a softmax,
+ * and the output is the weighted sum of the cached values:
+ *
+ *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . K_b[t,:]) V_b[t,:],
+ *   t = 0 .. context_lens[b]-1,
+ *
+ * which is the attention formula of §1.1 of the page "The KV Cache Problem
+ * of Traditional Attention" (pyllm.pages.dev) and §1.2 of "Understanding KV
+ * Cache: Attention, P/D Disaggregation and vLLM's Paged Memory Management"
+ * (steinslab.io), evaluated for the last row of the causal mask (§2.2,
+ * "Decode"). K_b and V_b are gathered through a per-sequence block table that
+ * maps logical 16-token blocks to physical blocks of a shared pool (page "KV
+ * Cache and Inference Optimization", note.yj-dis.top, section "PagedAttention:
+ * manage the KV cache like virtual memory"; slot rule of "Understanding KV
+ * Cache" §3.3).
+ *
+ * Conventions shared by every call:
+ *  - Pointers named "device" are GPU memory owned by the caller; the library
+ *    never allocates, frees or keeps device memory (the allocator below is a
+ *    host-side bookkeeping object that hands out block ids, not memory).
+ *  - Cache layout (HND, "Understanding KV Cache" §3.2): k_cache and v_cache
+ *    are each [num_blocks, num_kv_heads, block_size, head_dim], contiguous,
+ *    in the element type `dtype`.
+ *  - q and out: [num_seqs, num_heads, head_dim]; new k and v:
+ *    [num_tokens, num_kv_heads, head_dim]; contiguous, element type `dtype`.
+ *  - Query head h uses KV head h / (num_heads / num_kv_heads): consecutive
+ *    query heads share a KV head (GQA diagram of "KV Cache and Inference
+ *    Optimization", section "Three attention layouts").
+ *  - Supported: dtype f32/f16/bf16, head_dim 64 or 128, block_size 16.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Device calls are
+ *    asynchronous: a PKV_OK return means the work was enqueued; kernel faults
+ *    surface at the next synchronising HIP call.
+ *  - No call throws; each returns a pkv_status.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,       /* null pointer, bad shape, Hq % Hkv != 0, bad dtype     */
+  PKV_ERANGE = 2,       /* length beyond table capacity, id out of range          */
+  PKV_ENOMEM = 3,       /* block pool exhausted                                    */
+  PKV_EBUSY = 4,        /* write into a shared block, or two writes to one slot   */
+  PKV_EUNSUPPORTED = 5, /* head_dim / block_size / dtype this build does not cover */
+  PKV_EHIP = 6,         /* the HIP runtime reported an error at launch             */
+  PKV_ESMALL = 7        /* caller-provided workspace or output buffer too small    */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_status_string(pkv_status s);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t pkv_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device calls                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * pkv_kv_append -- write each new token's K and V into its cache slot.
+ *
+ * The cache is an append-only log ("Understanding KV Cache" §1.3); token i's
+ * slot s = slot_mapping[i] is offset s % block_size of physical block
+ * s / block_size (§3.3). For every KV head j:
+ *   k_cache[s / bs, j, s % bs, :] = k[i, j, :]   (likewise v)
+ * The copy is bit-exact. slot_mapping[i] < 0 marks a padding token: skipped.
+ *
+ *   k, v          device, [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping  device int64 [num_tokens]
+ *   k_cache, v_cache  device, written in place
+ *   num_blocks    pool size (bounds every slot)
+ *
+ * Slots must be distinct and must not lie in a block shared by several
+ * sequences (the host builder guarantees both). A slot >= num_blocks *
+ * block_size is skipped on the device rather than written out of bounds.
+ * Errors: EINVAL (null/shape/dtype), EUNSUPPORTED, EHIP. num_tokens == 0 is a
+ * no-op returning PKV_OK.
+ */
+pkv_status pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                         void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_decode_partition_blocks -- blocks per context partition the library
+ * picks for a launch of this shape (the split-context work unit). Each
+ * partition covers this many 16-token blocks of one sequence and one KV head;
+ * partial results are merged exactly with a log-sum-exp combine.
+ */
+int32_t pkv_decode_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq);
+
+/*
+ * pkv_decode_workspace_bytes -- device scratch that pkv_paged_decode_attention
+ * needs for this shape with `partition_blocks` (0 = the library's choice):
+ * num_seqs * num_heads * P * (head_dim + 1) * 4 bytes rounded up, where
+ * P = ceil(max_blocks_per_seq / partition_blocks). Returns 0 when every
+ * sequence fits one partition (no merge needed).
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_blocks);
+
+/*
+ * pkv_paged_decode_attention -- one decode step of attention over the paged
+ * cache, for all sequences and query heads.
+ *
+ *   q             device [num_seqs, num_heads, head_dim]
+ *   k_cache, v_cache  device [num_blocks, num_kv_heads, block_size, head_dim]
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]: entry [b][i]
+ *                 is the physical block of logical block i of sequence b;
+ *                 entries past ceil(context_lens[b] / block_size) are never
+ *                 read (any value)
+ *   context_lens  device int32 [num_seqs]: tokens attended, the newest one
+ *                 included; 0 gives an all-zero output row
+ *   scale         multiplies q . k (1/sqrt(head_dim) for standard attention)
+ *   out           device [num_seqs, num_heads, head_dim], same dtype as q;
+ *                 rounded from fp32 to the output type to nearest-even
+ *   workspace     device scratch of >= pkv_decode_workspace_bytes(...) bytes
+ *                 (may be NULL when that is 0); contents on entry ignored
+ *   partition_blocks  blocks per partition, 0 = the library's choice
+ *
+ * Accumulation is fp32. Preconditions the device does not check at full
+ * cost: context_lens[b] <= max_blocks_per_seq * block_size and table entries
+ * in [0, num_blocks); the kernel clamps lengths to the table capacity and
+ * skips out-of-range block ids instead of reading outside the pool, so a bad
+ * table gives a wrong result, never a fault (pkv_validate_tables checks them
+ * on the host).
+ * Errors: EINVAL (null/shape/dtype/Hq % Hkv), EUNSUPPORTED (head_dim,
+ * block_size), ESMALL (workspace), EHIP. num_seqs == 0 is a no-op.
+ */
+pkv_status pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                      void* workspace, size_t workspace_bytes, int32_t partition_blocks,
+                                      void* stream);
+
+/*
+ * The two phases of pkv_paged_decode_attention, for callers that schedule or
+ * time them separately (pkv_paged_decode_attention == partitions, then merge,
+ * on one stream).
+ *
+ * pkv_decode_partitions -- same arguments and errors as
+ * pkv_paged_decode_attention. Each (sequence, KV head, context partition)
+ * work unit attends over its partition; a sequence that fits one partition
+ * gets its final output row written to `out`, the others leave per-partition
+ * results o_p (normalised, fp32) and lse_p (log2 of the partition's softmax
+ * denominator plus its running maximum, in log2 units of scale * q.k) in the
+ * workspace.
+ *
+ * pkv_decode_merge -- exact log-sum-exp combine of those partials:
+ * out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M), M = max_p lse_p, for
+ * every sequence with more than one partition; rows of single-partition
+ * sequences are left as written. Arguments must match the preceding
+ * pkv_decode_partitions call. Errors: EINVAL, ESMALL, EHIP.
+ */
+pkv_status pkv_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 float scale, void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 int32_t partition_blocks, void* stream);
+pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_blocks, void* out,
+                            pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block pool, block tables and slot mapping                            */
+/* ------------------------------------------------------------------------ */
+/*
+ * A pool of num_blocks equal physical blocks and per-sequence block lists
+ * (block lifecycle of "Understanding KV Cache" §3.5: allocate from the free
+ * pool, use through the block table, return on finish). Host memory only; not
+ * thread-safe (one owner, like a scheduler). Sequence ids are dense integers
+ * in [0, max_seqs).
+ */
+typedef struct pkv_pool pkv_pool;
+
+typedef struct pkv_pool_stats {
+  int64_t num_blocks;       /* pool size                                          */
+  int64_t free_blocks;      /* blocks on the free list                            */
+  int64_t used_blocks;      /* distinct blocks held by at least one sequence      */
+  int64_t shared_blocks;    /* blocks held by more than one sequence              */
+  int64_t live_seqs;        /* sequences with at least one token                  */
+  int64_t payload_tokens;   /* sum of sequence lengths (logical tokens)           */
+  int64_t capacity_tokens;  /* sum over sequences of blocks x block_size          */
+} pkv_pool_stats;
+
+/* Create a pool. seed != 0 shuffles the free list with a seeded Fisher-Yates
+ * permutation (xorshift64* generator); seed == 0 keeps ids in ascending order.
+ * Errors: EINVAL (sizes <= 0, null out). */
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs, uint64_t seed,
+                           pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Grow sequence `seq` to new_len tokens, taking ceil(new_len / block_size)
+ * minus its current block count from the free list. Shrinking is ERANGE.
+ * ENOMEM if the pool runs dry (the sequence is left unchanged). */
+pkv_status pkv_seq_grow(pkv_pool* pool, int32_t seq, int32_t new_len);
+
+/* Make empty sequence `dst` share the first floor(n_tokens / block_size) FULL
+ * blocks of `src` (reference counts + 1); dst's length becomes that many
+ * blocks' worth of tokens. Only full blocks are shared, matching block-
+ * granular prefix reuse ("KV Cache and Inference Optimization", sections
+ * "PagedAttention" and "APC"). EINVAL if dst is not empty, ERANGE if n_tokens
+ * exceeds src's length. */
+pkv_status pkv_seq_share_prefix(pkv_pool* pool, int32_t dst, int32_t src, int32_t n_tokens);
+
+/* Release all blocks of `seq` (a block returns to the free list when its
+ * reference count reaches 0). EINVAL if `seq` holds nothing (double free). */
+pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
+
+/* Current length and block list of one sequence. `blocks` may be NULL to
+ * query only the count; otherwise capacity must hold the count (ESMALL). */
+pkv_status pkv_seq_info(const pkv_pool* pool, int32_t seq, int32_t* length, int32_t* num_blocks,
+                        int32_t* blocks, int32_t capacity);
+
+/* Dense block table [n, max_blocks] (row-major int32) for sequences seqs[0..n),
+ * padded with `pad`. ERANGE if a sequence has more than max_blocks blocks. */
+pkv_status pkv_build_block_tables(const pkv_pool* pool, const int32_t* seqs, int32_t n,
+                                  int32_t max_blocks, int32_t pad, int32_t* out);
+
+/* Slot of token positions[i] of sequence seqs[i]: physical block x block_size
+ * + offset ("Understanding KV Cache" §3.3). positions[i] < 0 gives -1 (a
+ * padding token). ERANGE if a position is at or beyond the sequence's length;
+ * EBUSY if the slot's block is shared (its writer would change another
+ * sequence) or if two entries name the same slot. */
+pkv_status pkv_build_slot_mapping(const pkv_pool* pool, const int32_t* seqs, const int32_t* positions,
+                                  int32_t n, int64_t* out);
+
+/* Stateless variant for callers that keep their own tables: slot of token
+ * positions[i] of row i of a dense int32 table [n, max_blocks] (row-major).
+ * positions[i] < 0 gives -1. ERANGE if positions[i] / block_size >=
+ * max_blocks or the table entry is negative; EBUSY if two entries name the
+ * same slot. */
+pkv_status pkv_slot_mapping_from_tables(const int32_t* block_tables, int32_t max_blocks, const int32_t* positions,
+                                        int32_t n, int32_t block_size, int64_t* out);
+
+/* Accounting snapshot (payload vs capacity, as in the block-accounting
+ * example of "Why does a request use more memory the longer it generates?",
+ * section "Paging changes allocation, not a token's representation"). */
+pkv_status pkv_pool_get_stats(const pkv_pool* pool, pkv_pool_stats* out);
+
+/* ceil(n / block_size) and the empty slots left in the last block. */
+int64_t pkv_blocks_for(int64_t n, int32_t block_size);
+int64_t pkv_empty_slots(int64_t n, int32_t block_size);
+
+/* Host-side check of decode inputs: every context length within the table
+ * capacity and every table entry a sequence actually reads in [0, num_blocks).
+ * ERANGE on the first violation, with its sequence index in *bad_seq (may be
+ * NULL). Inputs are HOST arrays. */
+pkv_status pkv_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                               int32_t num_blocks, int32_t* bad_seq);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

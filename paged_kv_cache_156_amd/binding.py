@@ -1,0 +1,305 @@
+"""ctypes binding of libpkv (argument marshalling only).
+
+Every compute step runs in the HIP library. torch tensors are accepted for
+device buffers and streams; the functions check dtype, shape, contiguity and
+device, pass raw pointers, and turn a non-OK status into ``PkvError``.
+Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+_lib = None
+
+PKV_OK, PKV_EINVAL, PKV_ERANGE, PKV_ENOMEM, PKV_EBUSY, PKV_EUNSUPPORTED, PKV_EHIP, PKV_ESMALL = range(8)
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_ERANGE", 3: "PKV_ENOMEM", 4: "PKV_EBUSY",
+                5: "PKV_EUNSUPPORTED", 6: "PKV_EHIP", 7: "PKV_ESMALL"}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+# every symbol include/pkv.h declares: (name, restype, argtypes)
+_c = ctypes
+_vp, _i32, _i64, _u64, _f32, _sz = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_uint64, _c.c_float, _c.c_size_t
+_pi32, _pi64 = _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int64)
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [(n, _c.c_int64) for n in ("num_blocks", "free_blocks", "used_blocks", "shared_blocks",
+                                          "live_seqs", "payload_tokens", "capacity_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+SIGNATURES = [
+    ("pkv_status_string", _c.c_char_p, [_i32]),
+    ("pkv_version", _i32, []),
+    ("pkv_kv_append", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    ("pkv_decode_partition_blocks", _i32, [_i32, _i32, _i32, _i32]),
+    ("pkv_decode_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    ("pkv_paged_decode_attention", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_decode_partitions", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_decode_merge", _i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
+    ("pkv_pool_destroy", None, [_vp]),
+    ("pkv_seq_grow", _i32, [_vp, _i32, _i32]),
+    ("pkv_seq_share_prefix", _i32, [_vp, _i32, _i32, _i32]),
+    ("pkv_seq_free", _i32, [_vp, _i32]),
+    ("pkv_seq_info", _i32, [_vp, _i32, _pi32, _pi32, _pi32, _i32]),
+    ("pkv_build_block_tables", _i32, [_vp, _pi32, _i32, _i32, _i32, _pi32]),
+    ("pkv_build_slot_mapping", _i32, [_vp, _pi32, _pi32, _i32, _pi64]),
+    ("pkv_slot_mapping_from_tables", _i32, [_pi32, _i32, _pi32, _i32, _i32, _pi64]),
+    ("pkv_pool_get_stats", _i32, [_vp, _c.POINTER(PoolStats)]),
+    ("pkv_blocks_for", _i64, [_i64, _i32]),
+    ("pkv_empty_slots", _i64, [_i64, _i32]),
+    ("pkv_validate_tables", _i32, [_pi32, _i32, _pi32, _i32, _i32, _i32, _pi32]),
+]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Open libpkv.so (once). Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libpkv.so not built at {_LIB_PATH}; run `python -m paged_kv_cache_156_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+def _np_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(_pi32)
+
+
+# ---------------------------------------------------------------------------
+# host accounting helpers
+# ---------------------------------------------------------------------------
+def blocks_for(n: int, block_size: int) -> int:
+    return int(load().pkv_blocks_for(n, block_size))
+
+
+def empty_slots(n: int, block_size: int) -> int:
+    return int(load().pkv_empty_slots(n, block_size))
+
+
+def validate_tables(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int, num_blocks: int):
+    """Host check of decode inputs; returns (status, bad_seq)."""
+    t = _np_i32(block_tables)
+    lens = _np_i32(context_lens)
+    bad = ctypes.c_int32(-1)
+    st = load().pkv_validate_tables(_ptr32(t), t.shape[1] if t.ndim == 2 else 0, _ptr32(lens), len(lens),
+                                    block_size, num_blocks, ctypes.byref(bad))
+    return st, bad.value
+
+
+def slot_mapping_from_tables(block_tables: np.ndarray, positions: Sequence[int], block_size: int) -> np.ndarray:
+    """Slots of positions[i] in row i of a dense host table (libpkv's builder)."""
+    t = _np_i32(block_tables)
+    p = _np_i32(positions)
+    if t.ndim != 2 or t.shape[0] != len(p):
+        raise ValueError("block_tables must be [n, max_blocks] with one position per row")
+    out = np.empty(len(p), np.int64)
+    _check(load().pkv_slot_mapping_from_tables(_ptr32(t), t.shape[1], _ptr32(p), len(p), block_size,
+                                               out.ctypes.data_as(_pi64)), "pkv_slot_mapping_from_tables")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# host block pool
+# ---------------------------------------------------------------------------
+class BlockPool:
+    """Host block pool with per-sequence block lists (libpkv's allocator)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, max_seqs: int = 1024, seed: int = 0):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check(self._lib.pkv_pool_create(num_blocks, block_size, max_seqs, seed, ctypes.byref(h)), "pkv_pool_create")
+        self._h = h
+        self.num_blocks, self.block_size, self.max_seqs = num_blocks, block_size, max_seqs
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def grow(self, seq: int, new_len: int):
+        _check(self._lib.pkv_seq_grow(self._h, seq, new_len), "pkv_seq_grow")
+
+    def share_prefix(self, dst: int, src: int, n_tokens: int):
+        _check(self._lib.pkv_seq_share_prefix(self._h, dst, src, n_tokens), "pkv_seq_share_prefix")
+
+    def free(self, seq: int):
+        _check(self._lib.pkv_seq_free(self._h, seq), "pkv_seq_free")
+
+    def seq_info(self, seq: int):
+        length, nb = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pkv_seq_info(self._h, seq, ctypes.byref(length), ctypes.byref(nb), None, 0), "pkv_seq_info")
+        out = np.zeros(max(nb.value, 1), np.int32)
+        _check(self._lib.pkv_seq_info(self._h, seq, None, None, _ptr32(out), len(out)), "pkv_seq_info")
+        return length.value, out[: nb.value].copy()
+
+    def block_tables(self, seqs: Sequence[int], max_blocks: int, pad: int = -1) -> np.ndarray:
+        s = _np_i32(seqs)
+        out = np.empty((len(s), max_blocks), np.int32)
+        _check(self._lib.pkv_build_block_tables(self._h, _ptr32(s), len(s), max_blocks, pad, _ptr32(out)),
+               "pkv_build_block_tables")
+        return out
+
+    def slot_mapping(self, seqs: Sequence[int], positions: Sequence[int]) -> np.ndarray:
+        s, p = _np_i32(seqs), _np_i32(positions)
+        if len(s) != len(p):
+            raise ValueError("seqs and positions differ in length")
+        out = np.empty(len(s), np.int64)
+        _check(self._lib.pkv_build_slot_mapping(self._h, _ptr32(s), _ptr32(p), len(s),
+                                                out.ctypes.data_as(_pi64)), "pkv_build_slot_mapping")
+        return out
+
+    def stats(self) -> dict:
+        st = PoolStats()
+        _check(self._lib.pkv_pool_get_stats(self._h, ctypes.byref(st)), "pkv_pool_get_stats")
+        return st.as_dict()
+
+
+# ---------------------------------------------------------------------------
+# device calls (torch tensors for device memory and streams)
+# ---------------------------------------------------------------------------
+def _torch_dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """k, v: [T, Hkv, D]; slot_mapping int64 [T]; caches [NB, Hkv, bs, D]."""
+    import torch
+    code = _torch_dtype_code(k_cache)
+    T, Hkv, D = k.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv, D) != (Hkv2, D2) or tuple(v.shape) != tuple(k.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between k/v and the caches")
+    if tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = load().pkv_kv_append(_dev(k, "k", k_cache.dtype), _dev(v, "v", k_cache.dtype),
+                              _dev(slot_mapping, "slot_mapping", torch.int64), T,
+                              _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
+                              NB, Hkv, D, bs, code, _stream_ptr(stream))
+    _check(st, "pkv_kv_append")
+
+
+def decode_partition_blocks(num_seqs: int, num_heads: int, num_kv_heads: int, max_blocks: int) -> int:
+    return int(load().pkv_decode_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks))
+
+
+def decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, partition_blocks=0) -> int:
+    return int(load().pkv_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks,
+                                                 partition_blocks))
+
+
+def alloc_workspace(q, k_cache, block_tables, partition_blocks=0):
+    """Device scratch for ``paged_decode_attention`` (a torch uint8 tensor, or None)."""
+    import torch
+    B, Hq, D = q.shape
+    nbytes = decode_workspace_bytes(B, Hq, k_cache.shape[1], D, block_tables.shape[1], partition_blocks)
+    return torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace):
+    import torch
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, maxNB] and context_lens [B]")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    return dict(q=_dev(q, "q"), k=_dev(k_cache, "k_cache", q.dtype), v=_dev(v_cache, "v_cache", q.dtype),
+                t=_dev(block_tables, "block_tables", torch.int32), mb=block_tables.shape[1],
+                lens=_dev(context_lens, "context_lens", torch.int32), B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB,
+                out=_dev(out, "out", q.dtype), code=_torch_dtype_code(q), ws=ws_ptr, wsb=ws_bytes)
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                           workspace=None, partition_blocks: int = 0, stream=None):
+    """q, out: [B, Hq, D]; caches [NB, Hkv, bs, D]; block_tables int32 [B, maxNB];
+    context_lens int32 [B]; workspace: uint8 device tensor or None."""
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    st = load().pkv_paged_decode_attention(a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"], a["B"], a["Hq"],
+                                           a["Hkv"], a["D"], a["bs"], a["NB"], float(scale), a["out"], a["code"],
+                                           a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+    _check(st, "pkv_paged_decode_attention")
+    return out
+
+
+def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                      workspace=None, partition_blocks: int = 0, stream=None):
+    """First phase of ``paged_decode_attention`` (see pkv_decode_partitions)."""
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    st = load().pkv_decode_partitions(a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"], a["B"], a["Hq"],
+                                      a["Hkv"], a["D"], a["bs"], a["NB"], float(scale), a["out"], a["code"],
+                                      a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+    _check(st, "pkv_decode_partitions")
+
+
+def decode_merge(q, k_cache, v_cache, block_tables, context_lens, out, workspace=None, partition_blocks: int = 0,
+                 stream=None):
+    """Second phase: log-sum-exp merge of the partition results into ``out``."""
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    st = load().pkv_decode_merge(a["ws"], a["wsb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["mb"], a["bs"],
+                                 int(partition_blocks), a["out"], a["code"], _stream_ptr(stream))
+    _check(st, "pkv_decode_merge")

@@ -318,3 +318,85 @@ def poison_device_pool(k_cache, v_cache, context_lens, assignment: BlockAssignme
         k_cache[pb, :, off:, :].fill_(nan)
         v_cache[pb, :, off:, :].fill_(nan)
     return k_cache, v_cache
+
+
+# ---------------------------------------------------------------------------
+# raw host arrays <-> torch device tensors (bit-preserving)
+# ---------------------------------------------------------------------------
+def raw_to_torch(raw: np.ndarray, dtype: str, device):
+    import torch
+    raw = np.ascontiguousarray(raw)
+    if dtype == "bf16":
+        t = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(raw)
+    return t.to(device)
+
+
+def torch_to_raw(t, dtype: str) -> np.ndarray:
+    import torch
+    t = t.detach().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@dataclasses.dataclass
+class DeviceWorkload:
+    """One decode step's inputs resident in device memory, for ``layers``
+    layers that share one block table (each layer has its own K/V pools)."""
+
+    cfg: DecodeConfig
+    context_lens: np.ndarray
+    assignment: BlockAssignment
+    q: list  # per layer [B, Hq, D]
+    k_new: list
+    v_new: list
+    k_cache: list  # per layer [NB, Hkv, bs, D]
+    v_cache: list
+    block_tables: object  # device int32 [B, maxNB]
+    context_lens_dev: object  # device int32 [B]
+
+    @property
+    def layers(self) -> int:
+        return len(self.k_cache)
+
+
+def value_generator(seed: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    # the values stream of the config's seed, reduced to a torch seed
+    g.manual_seed(int(streams(seed)[0].integers(0, 2 ** 62)))
+    return g
+
+
+def make_device_workload(cfg: DecodeConfig, device, layers: int = 1, seed: Optional[int] = None,
+                         context_lens: Optional[np.ndarray] = None,
+                         assignment: Optional[BlockAssignment] = None, progress=None) -> DeviceWorkload:
+    """Structure on the host (numpy) unless given, values drawn on the device
+    (torch). ``assignment`` lets a caller supply block lists built elsewhere
+    (e.g. by a block allocator) for ``context_lens``."""
+    import torch
+    seed = cfg.seed if seed is None else seed
+    if assignment is None:
+        lens, asg = make_structure(cfg, seed)
+    else:
+        lens, asg = np.asarray(context_lens, np.int32), assignment
+    gen = value_generator(seed, device)
+    tdt = torch_dtype(cfg.dtype)
+    B, Hq, Hkv, D, bs = len(lens), cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    qs, kns, vns, kcs, vcs = [], [], [], [], []
+    for _ in range(layers):
+        kc = fill_pool_device(torch.empty((asg.num_blocks, Hkv, bs, D), dtype=tdt, device=device), gen)
+        vc = fill_pool_device(torch.empty((asg.num_blocks, Hkv, bs, D), dtype=tdt, device=device), gen)
+        poison_device_pool(kc, vc, lens, asg, bs)
+        kcs.append(kc)
+        vcs.append(vc)
+        qs.append(fill_pool_device(torch.empty((B, Hq, D), dtype=tdt, device=device), gen))
+        kns.append(fill_pool_device(torch.empty((B, Hkv, D), dtype=tdt, device=device), gen))
+        vns.append(fill_pool_device(torch.empty((B, Hkv, D), dtype=tdt, device=device), gen))
+        if progress is not None:
+            progress(len(kcs))
+    tables = torch.from_numpy(asg.table()).to(device)
+    lens_dev = torch.from_numpy(lens.astype(np.int32)).to(device)
+    return DeviceWorkload(cfg, lens, asg, qs, kns, vns, kcs, vcs, tables, lens_dev)

@@ -1,0 +1,210 @@
+"""CPU tests of libpkv's C ABI: the library loads, exports every symbol the
+header declares, the host pool / builders behave, and argument checks on the
+device entry points fail before any GPU work is attempted."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_156_amd import binding as pkv
+from paged_kv_cache_156_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkv.load()
+    names = header_functions()
+    assert len(names) == len(pkv.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding declares a signature for every exported function
+    assert sorted(n for n, _, _ in pkv.SIGNATURES) == names
+
+
+def test_status_strings_and_version():
+    lib = pkv.load()
+    for code in range(8):
+        assert lib.pkv_status_string(code).decode().startswith(pkv.STATUS_NAMES[code])
+    assert lib.pkv_version() == 100
+
+
+def test_block_accounting_matches_oracle():
+    for bs in (4, 16, 256):
+        for n in list(range(0, 70)) + [300, 4096, 32768]:
+            assert pkv.blocks_for(n, bs) == oracle.blocks_for(n, bs)
+            assert pkv.empty_slots(n, bs) == oracle.empty_slots(n, bs)
+    assert pkv.blocks_for(-1, 16) == -1 and pkv.blocks_for(5, 0) == -1
+
+
+def test_pool_is_seeded_permutation():
+    for seed in (0, 1, 156):
+        pool = pkv.BlockPool(100, 16, max_seqs=1, seed=seed)
+        pool.grow(0, 100 * 16)
+        _, blocks = pool.seq_info(0)
+        assert sorted(blocks.tolist()) == list(range(100))
+        if seed == 0:
+            assert blocks.tolist() == list(range(100))
+        else:
+            assert blocks.tolist() != list(range(100))
+        again = pkv.BlockPool(100, 16, max_seqs=1, seed=seed)
+        again.grow(0, 1600)
+        assert np.array_equal(again.seq_info(0)[1], blocks)
+        with pytest.raises(pkv.PkvError) as e:
+            pool.grow(0, 1601)
+        assert e.value.status == pkv.PKV_ENOMEM
+
+
+def test_pool_lifecycle_and_stats(golden_dir):
+    """18 and 33 positions in 16-slot blocks: 2 and 3 blocks, 14 and 15 empty
+    slots (payload vs capacity of the block-accounting example)."""
+    pool = pkv.BlockPool(8, 16, max_seqs=4, seed=7)
+    pool.grow(0, 18)
+    pool.grow(1, 33)
+    st = pool.stats()
+    assert st["used_blocks"] == 5 and st["free_blocks"] == 3
+    assert st["payload_tokens"] == 51 and st["capacity_tokens"] == 80
+    assert st["capacity_tokens"] - st["payload_tokens"] == 14 + 15
+    # growth inside the last block takes nothing new; crossing a boundary does
+    pool.grow(0, 32)
+    assert pool.stats()["used_blocks"] == 5
+    pool.grow(0, 33)
+    assert pool.stats()["used_blocks"] == 6
+    with pytest.raises(pkv.PkvError) as e:
+        pool.grow(0, 10)
+    assert e.value.status == pkv.PKV_ERANGE
+    # free returns the blocks; double free is refused
+    pool.free(1)
+    assert pool.stats()["free_blocks"] == 5
+    with pytest.raises(pkv.PkvError) as e:
+        pool.free(1)
+    assert e.value.status == pkv.PKV_EINVAL
+    # freed blocks are reused (FIFO after the initial order)
+    pool.grow(2, 16 * 5)
+    assert pool.stats()["free_blocks"] == 0
+
+
+def test_prefix_sharing_refcounts_and_busy():
+    pool = pkv.BlockPool(32, 16, max_seqs=4, seed=3)
+    pool.grow(0, 40)  # 3 blocks, the last one partial
+    pool.share_prefix(1, 0, 40)  # shares the 2 full blocks only
+    length, blocks1 = pool.seq_info(1)
+    assert length == 32 and blocks1.tolist() == pool.seq_info(0)[1][:2].tolist()
+    st = pool.stats()
+    assert st["shared_blocks"] == 2 and st["used_blocks"] == 3
+    pool.grow(1, 45)  # private third block
+    _, b1 = pool.seq_info(1)
+    assert b1[2] != pool.seq_info(0)[1][2]
+    # appending into a shared block is refused; into private blocks it is fine
+    with pytest.raises(pkv.PkvError) as e:
+        pool.slot_mapping([0], [5])
+    assert e.value.status == pkv.PKV_EBUSY
+    s = pool.slot_mapping([0, 1], [39, 44])
+    assert s.tolist() == [pool.seq_info(0)[1][2] * 16 + 7, b1[2] * 16 + 12]
+    with pytest.raises(pkv.PkvError) as e:
+        pool.slot_mapping([0, 0], [39, 39])  # same slot twice
+    assert e.value.status == pkv.PKV_EBUSY
+    with pytest.raises(pkv.PkvError) as e:
+        pool.slot_mapping([0], [40])  # beyond the length
+    assert e.value.status == pkv.PKV_ERANGE
+    # freeing one sharer keeps the blocks alive for the other
+    pool.free(0)
+    st = pool.stats()
+    assert st["shared_blocks"] == 0 and st["used_blocks"] == 3
+    with pytest.raises(pkv.PkvError):
+        pool.share_prefix(1, 2, 0)  # dst not empty
+
+
+def test_slot_mapping_matches_oracle():
+    rng = np.random.default_rng(11)
+    pool = pkv.BlockPool(400, 16, max_seqs=16, seed=99)
+    lens = rng.integers(1, 300, size=16)
+    for s, n in enumerate(lens):
+        pool.grow(s, int(n))
+    seqs = np.arange(16)
+    table = pool.block_tables(seqs, 20, pad=-1)
+    for trial in range(5):
+        pos = np.array([rng.integers(0, n) for n in lens], np.int32)
+        pos[trial] = -1
+        got = pool.slot_mapping(seqs, pos)
+        want = oracle.slot_mapping(table, pos, 16)
+        assert np.array_equal(got, want)
+        assert np.array_equal(pkv.slot_mapping_from_tables(table, pos, 16), want)
+    # the worked example: block size 4, table [7, 3, 12], token 6 -> slot 14
+    assert pkv.slot_mapping_from_tables(np.array([[7, 3, 12]]), [6], 4).tolist() == [14]
+    with pytest.raises(pkv.PkvError):
+        pkv.slot_mapping_from_tables(np.array([[7, 3, 12]]), [12], 4)  # logical block 3 >= 3
+    with pytest.raises(pkv.PkvError):
+        pkv.slot_mapping_from_tables(np.array([[7, -1, 12]]), [5], 4)
+
+
+def test_block_tables_padding_and_range():
+    pool = pkv.BlockPool(16, 16, max_seqs=2, seed=0)
+    pool.grow(0, 17)
+    pool.grow(1, 48)
+    t = pool.block_tables([0, 1], 4, pad=15)
+    assert t.tolist() == [[0, 1, 15, 15], [2, 3, 4, 15]]
+    with pytest.raises(pkv.PkvError) as e:
+        pool.block_tables([1], 2)
+    assert e.value.status == pkv.PKV_ERANGE
+
+
+def test_validate_tables():
+    table = np.array([[3, 1, 9], [0, 2, 2]], np.int32)
+    assert pkv.validate_tables(table, np.array([33, 20]), 16, 10) == (pkv.PKV_OK, -1)
+    assert pkv.validate_tables(table, np.array([49, 20]), 16, 10) == (pkv.PKV_ERANGE, 0)
+    assert pkv.validate_tables(table, np.array([33, 20]), 16, 9) == (pkv.PKV_ERANGE, 0)
+    table[1, 1] = -4
+    assert pkv.validate_tables(table, np.array([0, 20]), 16, 10) == (pkv.PKV_ERANGE, 1)
+    assert pkv.validate_tables(table, np.array([0, 16]), 16, 10) == (pkv.PKV_OK, -1)
+
+
+def test_device_entry_points_reject_bad_arguments_without_gpu():
+    """Argument checks return before any HIP call, so they run on the CPU."""
+    lib = pkv.load()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call fails validation
+    # append
+    assert lib.pkv_kv_append(None, None, None, 0, None, None, 4, 2, 64, 16, 2, None) == pkv.PKV_OK  # no-op
+    assert lib.pkv_kv_append(None, fake, fake, 1, fake, fake, 4, 2, 64, 16, 2, None) == pkv.PKV_EINVAL
+    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 64, 16, 7, None) == pkv.PKV_EINVAL
+    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 4, 16, 2, None) == pkv.PKV_EUNSUPPORTED
+    assert lib.pkv_kv_append(fake, fake, fake, -1, fake, fake, 4, 2, 64, 16, 2, None) == pkv.PKV_EINVAL
+
+    def attn(**kw):
+        a = dict(q=fake, k=fake, v=fake, t=fake, mb=4, lens=fake, B=2, Hq=4, Hkv=2, D=64, bs=16, NB=8, scale=0.125,
+                 out=fake, dt=2, ws=None, wsb=0, pb=0)
+        a.update(kw)
+        return lib.pkv_paged_decode_attention(a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"], a["B"], a["Hq"],
+                                              a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"], a["out"], a["dt"],
+                                              a["ws"], a["wsb"], a["pb"], None)
+
+    assert attn(B=0) == pkv.PKV_OK  # empty batch: no launch
+    assert attn(Hq=6, Hkv=4) == pkv.PKV_EINVAL
+    assert attn(D=96) == pkv.PKV_EUNSUPPORTED
+    assert attn(bs=32) == pkv.PKV_EUNSUPPORTED
+    assert attn(dt=3) == pkv.PKV_EINVAL
+    assert attn(q=None) == pkv.PKV_EINVAL
+    assert attn(pb=65) == pkv.PKV_EINVAL
+    # a launch that needs a workspace but gets none (4 blocks in partitions of 1)
+    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4, 1) > 0
+    assert attn(pb=1) == pkv.PKV_ESMALL
+    assert attn(pb=1, ws=fake, wsb=16) == pkv.PKV_ESMALL
+
+
+def test_workspace_and_partition_choice():
+    # one partition for every sequence -> no workspace
+    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 3, 16) == 0
+    pb = pkv.decode_partition_blocks(32, 64, 8, 256)
+    assert 8 <= pb <= 64 and (pb & (pb - 1)) == 0
+    parts = -(-256 // pb)
+    rows = 32 * 64 * parts
+    assert pkv.decode_workspace_bytes(32, 64, 8, 128, 256, 0) >= rows * 129 * 4
