@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layers to loop (0 = the configuration's count)")
     ap.add_argument("--partition-blocks", type=int, default=0, help="blocks per partition (0 = library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU-reference work (0 = skip)")
+    ap.add_argument("--mode", choices=("fused", "split"), default="fused",
+                    help="fused: one decode_step launch per layer (append + attention + merge); "
+                         "split: kv_append, decode_partitions, decode_merge")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -152,13 +155,25 @@ def main():
 
     max_blocks = wkd.block_tables.shape[1]
     pb = args.partition_blocks or pkv.decode_partition_blocks(B, Hq, Hkv, max_blocks)
-    ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables, pb)
+    fused = args.mode == "fused"
+    if fused:
+        ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables, pb)
+    else:
+        ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables, pb)
     slots_d = torch.from_numpy(slots).to(dev)
     outs = [torch.empty_like(wkd.q[l]) for l in range(L)]
     stream = torch.cuda.current_stream()
 
     def step(events=None):
         for l in range(L):
+            if fused:
+                if events is not None:
+                    events[l][0].record(stream)
+                pkv.decode_step(wkd.q[l], wkd.k_new[l], wkd.v_new[l], wkd.k_cache[l], wkd.v_cache[l],
+                                wkd.block_tables, wkd.context_lens_dev, cfg.scale, outs[l], ws, pb)
+                if events is not None:
+                    events[l][1].record(stream)
+                continue
             pkv.kv_append(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_cache[l], wkd.v_cache[l])
             if events is not None:
                 events[l][0].record(stream)
@@ -195,13 +210,14 @@ def main():
     kv_layer = 2 * Hkv * D * esz * sum_n
     q_out = 2 * B * Hq * D * esz
     tables = 4 * sum(-(-int(n) // bs) for n in lens) + 4 * B
-    part_alg = kv_layer + q_out + tables
+    append = 4 * B * Hkv * D * esz  # new K/V read and written (fused step only)
+    part_alg = kv_layer + q_out + tables + (append if fused else 0)
     step_kv = kv_layer * L
     gbs = step_kv / (ms_per_step * 1e-3) / 1e9
     achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
 
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"decode_partition_{cfg.name}_traffic.json")
+    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}_{cfg.name}_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
@@ -244,11 +260,13 @@ def main():
         "config": {"workload": f"{cfg.name}: batch {B}, context {'ragged' if cfg.context_len_range else int(lens[0])}, "
                                f"{Hq} query / {Hkv} KV heads, head_dim {D}, block 16, {L} layers, one decode step "
                                f"(append + attention) per layer",
-                   "global_batch": B, "seq_len": int(lens.max()), "layers": L, "partition_blocks": pb},
+                   "global_batch": B, "seq_len": int(lens.max()), "layers": L, "partition_blocks": pb,
+                   "mode": args.mode},
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(B / (ms_per_step * 1e-3), 2),
         "kv_bytes_per_step": step_kv,
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel<" + ("step" if fused else "split") + ">",
+                     "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": part_alg,
                      "avg_launch_us": round(part_avg_ms * 1e3, 2), "kernel_sha": kernel_sha()},

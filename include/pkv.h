@@ -179,6 +179,37 @@ pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const
                             int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_blocks, void* out,
                             pkv_dtype dtype, void* stream);
 
+/*
+ * pkv_decode_step -- one whole decode step for one layer in a single launch:
+ * append the newest token of every sequence, then attend over the cache.
+ * Equivalent to pkv_kv_append with slot_mapping[b] = the slot of position
+ * context_lens[b] - 1 (block_tables[b][(n-1)/bs] * bs + (n-1) % bs, the rule
+ * of "Understanding KV Cache" §3.3) followed by pkv_paged_decode_attention.
+ * The kernel writes the new K/V into its slot and uses them from registers;
+ * a sequence split into several partitions is merged by whichever of its
+ * partitions finishes last (device-scope arrival counter), so no second
+ * launch is needed.
+ *
+ *   k_new, v_new  device [num_seqs, num_heads_kv, head_dim]: token at
+ *                 position context_lens[b] - 1 (sequences with length 0
+ *                 append nothing)
+ *   workspace     >= pkv_decode_step_workspace_bytes(...) bytes. It holds
+ *                 partition results and arrival counters: it must be
+ *                 zero-filled before its first use, and every completed call
+ *                 leaves the counters at zero again. Calls that share one
+ *                 workspace must not run concurrently.
+ * Every other argument as pkv_paged_decode_attention. The newest token's
+ * block must be private to its sequence (the host pool's slot builder checks
+ * this; here it is a precondition).
+ */
+size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_blocks);
+pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                           void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block pool, block tables and slot mapping                            */
 /* ------------------------------------------------------------------------ */

@@ -46,6 +46,9 @@ SIGNATURES = [
     ("pkv_decode_partitions", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_decode_merge", _i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    ("pkv_decode_step_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    ("pkv_decode_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
     ("pkv_seq_grow", _i32, [_vp, _i32, _i32]),
@@ -303,3 +306,31 @@ def decode_merge(q, k_cache, v_cache, block_tables, context_lens, out, workspace
     st = load().pkv_decode_merge(a["ws"], a["wsb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["mb"], a["bs"],
                                  int(partition_blocks), a["out"], a["code"], _stream_ptr(stream))
     _check(st, "pkv_decode_merge")
+
+
+def decode_step_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, partition_blocks=0) -> int:
+    return int(load().pkv_decode_step_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks,
+                                                      partition_blocks))
+
+
+def alloc_step_workspace(q, k_cache, block_tables, partition_blocks=0):
+    """Zero-filled device workspace for ``decode_step`` (or None if not needed)."""
+    import torch
+    B, Hq, D = q.shape
+    nbytes = decode_step_workspace_bytes(B, Hq, k_cache.shape[1], D, block_tables.shape[1], partition_blocks)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                workspace=None, partition_blocks: int = 0, stream=None):
+    """Fused append of each sequence's newest token (position context_lens-1)
+    and paged decode attention, one launch (see pkv_decode_step)."""
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    B, Hkv, D = a["B"], a["Hkv"], a["D"]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new / v_new must be [B, Hkv, D]")
+    st = load().pkv_decode_step(a["q"], _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype), a["k"], a["v"],
+                                a["t"], a["mb"], a["lens"], B, a["Hq"], Hkv, D, a["bs"], a["NB"], float(scale),
+                                a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+    _check(st, "pkv_decode_step")
+    return out

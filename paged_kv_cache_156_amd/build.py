@@ -21,8 +21,10 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are disabled for all device code.
+# MFMA accumulators stay in VGPRs: the online softmax rescales them with VALU
+# ops, and AGPR-resident accumulators would be copied out on every block.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall", "-Wextra"]
 
@@ -46,18 +48,20 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link libpkv; ``extra_flags`` go to the HIP compile (e.g.
+    ``-DPKV_AHEAD_16BIT=3``), ``out`` names the shared library."""
+    os.makedirs(build_dir, exist_ok=True)
     hipcc = _hipcc()
     cxx = shutil.which("g++") or "g++"
-    k_obj = os.path.join(BUILD, "pkv_kernels.o")
-    p_obj = os.path.join(BUILD, "pkv_pool.o")
-    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "pkv_kernels.hip"), "-o", k_obj], verbose)
+    k_obj = os.path.join(build_dir, "pkv_kernels.o")
+    p_obj = os.path.join(build_dir, "pkv_pool.o")
+    _run([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, "pkv_kernels.hip"), "-o", k_obj], verbose)
     _run([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, "pkv_pool.cpp"), "-o", p_obj], verbose)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", k_obj, p_obj, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -55,8 +55,20 @@ using s16x4 = short __attribute__((ext_vector_type(4)));
 using f16x4 = _Float16 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockSize = 16;
+
+// K/V blocks kept in flight per wave ahead of the one being consumed
+#ifndef PKV_AHEAD_16BIT
+#define PKV_AHEAD_16BIT 2
+#endif
+#ifndef PKV_AHEAD_32BIT
+#define PKV_AHEAD_32BIT 1
+#endif
+#ifndef PKV_RING_ROTATIONS
+#define PKV_RING_ROTATIONS 3
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;  // weights are kept <= 2^8 between rescales
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -115,17 +127,30 @@ __device__ __forceinline__ f32x4 mfma_pv16<_Float16>(u32x2 a, u32x2 b, f32x4 c) 
                                                 0);
 }
 
+// K/V tiles are read through buffer resources whose record count covers only
+// the tile's valid rows: rows past the sequence end (NaN padding) and whole
+// blocks past the partition end read as zeros with no memory traffic, so the
+// load stream needs no branches. The loads carry the nontemporal hint: K/V are
+// read exactly once per step, and streaming them without cache allocation
+// measured ~6.9 TB/s vs ~6.1 TB/s for plain loads (permuted 4 KiB tiles).
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
+constexpr int kCacheNT = 2;               // nontemporal cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), static_cast<short>(0), bytes, kBufferWord3);
+}
+
 template <int NDW>
-__device__ __forceinline__ void load_dwords(unsigned (&dst)[NDW], const char* src) {
+__device__ __forceinline__ void load_dwords(unsigned (&dst)[NDW], __amdgpu_buffer_rsrc_t rs, int off) {
   if constexpr (NDW == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCacheNT);
     dst[0] = v[0];
     dst[1] = v[1];
   } else {
     static_assert(NDW % 4 == 0, "row slice must be 8 bytes or a multiple of 16");
 #pragma unroll
     for (int w = 0; w < NDW; w += 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + w * 4);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + w * 4, 0, kCacheNT);
       dst[w] = v[0];
       dst[w + 1] = v[1];
       dst[w + 2] = v[2];
@@ -165,14 +190,21 @@ struct BlockRegs {
   unsigned v[4][Shape<T, D>::kVDW];
 };
 
+// Load one block's K tile (MFMA A-operand layout) and V tile (row layout);
+// only the first `rows` token rows are fetched, the rest read as zero.
 template <typename T, int D>
-__device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const char* kt, const char* vt, int q4, int ln) {
+__device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const char* kt, const char* vt, int rows, int q4,
+                                           int ln) {
   using S = Shape<T, D>;
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows * S::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows * S::kRowBytes);
 #pragma unroll
-  for (int c = 0; c < S::kNK; ++c)
-    r.k[c] = *reinterpret_cast<const u32x4*>(kt + ln * S::kRowBytes + (4 * c + q4) * 16);
+  for (int c = 0; c < S::kNK; ++c) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * S::kRowBytes + (4 * c + q4) * 16, 0, kCacheNT);
+    r.k[c] = u32x4{v[0], v[1], v[2], v[3]};
+  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_dwords<S::kVDW>(r.v[i], vt + (4 * q4 + i) * S::kRowBytes + ln * S::kE * S::kElt);
+  for (int i = 0; i < 4; ++i) load_dwords<S::kVDW>(r.v[i], rv, (4 * q4 + i) * S::kRowBytes + ln * S::kE * S::kElt);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,9 +228,20 @@ struct DecodeArgs {
   int32_t pb_per_part;  // blocks per partition (<= 64)
   int32_t num_parts;    // P
   float qk_scale;       // scale * log2(e)
+  // fused decode step only
+  const char* k_new;    // [B, Hkv, D]: newest token's K (written at position n-1)
+  const char* v_new;
+  char* k_cache_w;      // the caches, writable
+  char* v_cache_w;
+  int32_t* counters;    // [B, Hkv, head_groups] arrival counters, zero between calls
 };
 
-template <typename T, int D>
+// kStep = false: one partition of attention (a split sequence leaves partials
+// for merge_kernel). kStep = true: the fused decode step -- the partition that
+// holds position n-1 also appends the newest token's K/V (written to its slot
+// and patched into its registers, never read back), and the last partition of
+// a split sequence to finish merges all partitions (arrival counter).
+template <typename T, int D, bool kStep>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
   constexpr bool k16 = sizeof(T) == 2;
@@ -240,21 +283,79 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const size_t head_off = static_cast<size_t>(j) * S::kTileBytes;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * S::kTileBytes;
 
+  // fused append: the partition holding position n-1 takes the new token's
+  // K/V from k_new/v_new (row layout), in the same per-lane chunks the tiles use
+  const bool has_new = kStep && n > 0 && p == nparts - 1;
+  const int new_t = has_new ? (n - 1) / kBlockSize - blk0 : -1;  // block index inside the partition
+  const int new_row = (n - 1) % kBlockSize;
+  u32x4 kn[S::kNK];
+  unsigned vn[S::kVDW];
+  if constexpr (kStep) {
+    if (has_new) {
+      const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + j) * S::kRowBytes;
+#pragma unroll
+      for (int c = 0; c < S::kNK; ++c) kn[c] = *reinterpret_cast<const u32x4*>(a.k_new + src + (4 * c + q4) * 16);
+      const char* vsrc = a.v_new + src + ln * S::kE * S::kElt;
+      if constexpr (S::kVDW == 2) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
+        vn[0] = w[0];
+        vn[1] = w[1];
+      } else {
+#pragma unroll
+        for (int w = 0; w < S::kVDW; w += 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(vsrc + w * 4);
+          vn[w] = x[0];
+          vn[w + 1] = x[1];
+          vn[w + 2] = x[2];
+          vn[w + 3] = x[3];
+        }
+      }
+      // write it into its slot (one head group writes; the others only read)
+      const int id = __builtin_amdgcn_readlane(my_id, new_t);
+      if (hg == 0 && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) {
+        const size_t dst = static_cast<size_t>(id) * block_stride + head_off + new_row * S::kRowBytes;
+        if (ln == 0) {
+#pragma unroll
+          for (int c = 0; c < S::kNK; ++c) *reinterpret_cast<u32x4*>(a.k_cache_w + dst + (4 * c + q4) * 16) = kn[c];
+        }
+        if (q4 == 0) store_dwords<S::kVDW>(a.v_cache_w + dst + ln * S::kE * S::kElt, vn);
+      }
+    }
+  }
+
   f32x4 acc[S::kE];
 #pragma unroll
   for (int mt = 0; mt < S::kE; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf;  // running max of scaled scores (log2 units)
   float l_run = 0.f;      // this lane's share of the running denominator
 
-  auto block_ptr = [&](int t, bool& ok) -> size_t {
-    int id = __builtin_amdgcn_readlane(my_id, t);
-    ok = static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
+  // Tile offset of the partition's block t and how many of its token rows to
+  // fetch: 0 past the partition end or for an out-of-range id (nothing is
+  // read then), else the block's tokens below n.
+  auto block_src = [&](int t, int& rows) -> size_t {
+    const int id = __builtin_amdgcn_readlane(my_id, min(t, 63));
+    const bool ok = t < nblk && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
+    rows = ok ? min(kBlockSize, n - (blk0 + t) * kBlockSize) : 0;
+    if (kStep && t == new_t) rows = new_row;  // the new row comes from registers
     return (ok ? static_cast<size_t>(id) : 0) * block_stride + head_off;
   };
 
-  auto process = [&](BlockRegs<T, D>& r, int t, bool ok) {
-    const int tok0 = (blk0 + t) * kBlockSize;
-    const int valid = ok ? min(kBlockSize, n - tok0) : 0;  // tokens of this block in range
+  auto process = [&](BlockRegs<T, D>& r, int valid, int t) {  // valid: token rows of this block in range
+    if constexpr (kStep) {
+      if (t == new_t) {  // wave-uniform: patch in the appended token
+        valid = new_row + 1;
+        if (ln == new_row) {
+#pragma unroll
+          for (int c = 0; c < S::kNK; ++c) r.k[c] = kn[c];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * q4 + i == new_row) {
+#pragma unroll
+            for (int w = 0; w < S::kVDW; ++w) r.v[i][w] = vn[w];
+          }
+      }
+    }
     // scores
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (k16) {
@@ -270,29 +371,32 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = s[i] * a.qk_scale;
-    if (valid < kBlockSize) {  // wave-uniform: only the last block of a sequence, or a bad id
+    if (valid < kBlockSize) {  // wave-uniform: the last block of a sequence, or a bad id
+      // rows past `valid` were not fetched (K and V read as zero), so no NaN
+      // padding enters the MFMAs; their scores are selected out here
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool in = 4 * q4 + i < valid;
-        sc[i] = in ? sc[i] : kNegInf;
-        if (!in) {
-#pragma unroll
-          for (int w = 0; w < S::kVDW; ++w) r.v[i][w] = 0u;  // select, never multiply, NaN padding
-        }
-      }
+      for (int i = 0; i < 4; ++i) sc[i] = 4 * q4 + i < valid ? sc[i] : kNegInf;
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, xor_shuffle(mx, 16));
     mx = fmaxf(mx, xor_shuffle(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // Lazy rescaling: the reference maximum m_run only moves when a head's
+    // block maximum exceeds it by more than kRescaleSlack (log2 units), so the
+    // weights stay <= 2^kRescaleSlack and the accumulator is rescaled rarely.
+    // Any reference gives the same softmax; this one keeps exp2 in range.
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+      const float m_new = grow ? mx : m_run;
+      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int mt = 0; mt < S::kE; ++mt) acc[mt] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
-#pragma unroll
-    for (int mt = 0; mt < S::kE; ++mt) acc[mt] *= alpha;
     if constexpr (k16) {
       // P^T operand: each weight is split into a 16-bit head plus a 16-bit
       // residual (two MFMAs against the same V tile), so the weights carry
@@ -303,7 +407,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         ph[i] = to_bits16<T>(pr[i]);
         pl[i] = to_bits16<T>(pr[i] - from_bits16<T>(ph[i]));
       }
-      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       const u32x2 pw_hi = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
       const u32x2 pw_lo = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)};
 #pragma unroll
@@ -315,7 +419,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         acc[mt] = mfma_pv16<T>(av, pw_lo, acc[mt]);
       }
     } else {
-      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -324,25 +428,35 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // stream the partition's blocks, one block of loads in flight ahead
-  BlockRegs<T, D> r0, r1;
-  bool ok0 = false, ok1 = false;
-  if (nblk > 0) {
-    const size_t off = block_ptr(0, ok0);
-    load_block<T, D>(r0, a.k_cache + off, a.v_cache + off, q4, ln);
-  }
-  for (int t = 0; t < nblk; t += 2) {
-    if (t + 1 < nblk) {
-      const size_t off = block_ptr(t + 1, ok1);
-      load_block<T, D>(r1, a.k_cache + off, a.v_cache + off, q4, ln);
+  // Stream the partition's blocks through a register ring that keeps kAhead
+  // blocks of K/V loads in flight while the oldest block is consumed. Loads
+  // are issued unconditionally (past the partition end they fetch nothing, see
+  // load_block) so that every iteration issues the same loads and the compiler
+  // can wait on a precise outstanding-load count.
+  constexpr int kAhead = sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT;
+  constexpr int kRing = kAhead + 1;
+  BlockRegs<T, D> ring[kRing];
+  int ring_rows[kRing];
+  if (nblk > 0) {  // wave-uniform; nblk == 0 only for an empty sequence
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const size_t off = block_src(u, ring_rows[u]);
+      load_block<T, D>(ring[u], a.k_cache + off, a.v_cache + off, ring_rows[u], q4, ln);
     }
-    process(r0, t, ok0);
-    if (t + 1 >= nblk) break;
-    if (t + 2 < nblk) {
-      const size_t off = block_ptr(t + 2, ok0);
-      load_block<T, D>(r0, a.k_cache + off, a.v_cache + off, q4, ln);
+    // several ring rotations per loop iteration: only the first block after
+    // the back-edge may see a conservative wait
+    constexpr int kUnroll = kRing * PKV_RING_ROTATIONS;
+    for (int t0 = 0; t0 < nblk; t0 += kUnroll) {
+#pragma unroll
+      for (int uu = 0; uu < kUnroll; ++uu) {
+        const int u = uu % kRing;
+        const int slot = (u + kAhead) % kRing;
+        const size_t off = block_src(t0 + uu + kAhead, ring_rows[slot]);
+        load_block<T, D>(ring[slot], a.k_cache + off, a.v_cache + off, ring_rows[slot], q4, ln);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
+        if (t0 + uu < nblk) process(ring[u], ring_rows[u], t0 + uu);
+      }
     }
-    process(r1, t + 1, ok1);
   }
 
   // combine the four lanes' partial denominators of each head
@@ -351,27 +465,33 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   if (!head_ok) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 
-  if (nparts == 1) {
+  // this lane's 4 x E output values (d = (4*q4 + i) * E + mt), scaled, to `out`
+  auto write_out = [&](float scale_by) {
     char* orow = a.out + (static_cast<size_t>(b) * a.num_heads + hq) * S::kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = (4 * q4 + i) * S::kE;
+      unsigned w[S::kVDW];
       if constexpr (k16) {
-        unsigned w[S::kVDW];
 #pragma unroll
         for (int mt = 0; mt < S::kE; mt += 2)
-          w[mt >> 1] = to_bits16<T>(acc[mt][i] * inv) | (to_bits16<T>(acc[mt + 1][i] * inv) << 16);
-        store_dwords<S::kVDW>(orow + d0 * S::kElt, w);
+          w[mt >> 1] = to_bits16<T>(acc[mt][i] * scale_by) | (to_bits16<T>(acc[mt + 1][i] * scale_by) << 16);
       } else {
-        unsigned w[S::kVDW];
 #pragma unroll
-        for (int mt = 0; mt < S::kE; ++mt) w[mt] = __float_as_uint(acc[mt][i] * inv);
-        store_dwords<S::kVDW>(orow + d0 * S::kElt, w);
+        for (int mt = 0; mt < S::kE; ++mt) w[mt] = __float_as_uint(acc[mt][i] * scale_by);
       }
+      store_dwords<S::kVDW>(orow + d0 * S::kElt, w);
     }
-  } else {
-    const size_t row = (static_cast<size_t>(b) * a.num_heads + hq) * a.num_parts + p;
-    float* o = a.ws_o + row * D;
+  };
+
+  if (nparts == 1) {
+    write_out(inv);
+    return;
+  }
+  if constexpr (!kStep) {
+    // partials for merge_kernel: [B, Hq, P, D] and [B, Hq, P]
+    const size_t row0 = (static_cast<size_t>(b) * a.num_heads + hq) * a.num_parts;
+    float* o = a.ws_o + (row0 + p) * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = (4 * q4 + i) * S::kE;
@@ -380,7 +500,55 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         *reinterpret_cast<f32x4*>(o + d0 + mt) =
             f32x4{acc[mt][i] * inv, acc[mt + 1][i] * inv, acc[mt + 2][i] * inv, acc[mt + 3][i] * inv};
     }
-    if (q4 == 0) a.ws_lse[row] = m_run + __builtin_amdgcn_logf(l_tot);
+    if (q4 == 0) a.ws_lse[row0 + p] = m_run + __builtin_amdgcn_logf(l_tot);
+  } else {
+    // Fused merge. Partials are stored lane-major per work unit (each store
+    // instruction writes 64 consecutive floats) with device-coherent stores
+    // that write through the XCD's L2, then the wave drains its stores and
+    // counts its arrival. The last partition of the sequence to arrive reads
+    // all partials back with device-coherent loads, combines them (exact
+    // log-sum-exp merge) and resets the counter for the next call. No L2
+    // write-back or invalidate is needed.
+    const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * a.head_groups + hg;
+    constexpr int kVals = 4 * S::kE;  // floats per lane
+    float* ob = a.ws_o + (unit * a.num_parts) * (64 * kVals);
+    float* lb = a.ws_lse + (unit * a.num_parts) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int mt = 0; mt < S::kE; ++mt)
+        __hip_atomic_store(ob + p * (64 * kVals) + (i * S::kE + mt) * 64 + lane, acc[mt][i] * inv, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (q4 == 0)
+      __hip_atomic_store(lb + p * 16 + ln, m_run + __builtin_amdgcn_logf(l_tot), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // every store above has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int32_t* ctr = a.counters + unit;
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0 is always active here (head 0 of the group)
+    if (prev != nparts - 1) return;
+    float M = kNegInf;
+    for (int pp = 0; pp < nparts; ++pp)
+      M = fmaxf(M, __hip_atomic_load(lb + pp * 16 + ln, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int mt = 0; mt < S::kE; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int pp = 0; pp < nparts; ++pp) {
+      const float w = __builtin_amdgcn_exp2f(
+          __hip_atomic_load(lb + pp * 16 + ln, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
+      L += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt)
+          acc[mt][i] += w * __hip_atomic_load(ob + pp * (64 * kVals) + (i * S::kE + mt) * 64 + lane,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    write_out(1.0f / L);
+    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -471,20 +639,27 @@ int32_t auto_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_k
   if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads <= 0 || max_blocks <= 0) return 16;
   const int64_t group = num_heads / num_kv_heads;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * ceil_div64(group, 16);
-  // enough single-wave workgroups to keep every CU streaming (256 CUs x 16)
-  const int64_t target = 4096;
+  // Long partitions amortise each wave's start-up (table and Q loads, then the
+  // first dependent K/V loads) and the merge; about four single-wave
+  // workgroups per CU (256 CUs) keep enough loads in flight.
+  const int64_t target = 1024;
   int32_t pb = 64;
   while (pb > 8 && units * ceil_div64(max_blocks, pb) < target) pb /= 2;
   return pb;
 }
 
-enum Phase : unsigned { kPartitions = 1u, kMerge = 2u };
+enum Phase : unsigned { kPartitions = 1u, kMerge = 2u, kFusedStep = 4u };
 
 template <typename T, int D>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
+  if (phases & kFusedStep) {
+    dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, true>), grid, dim3(64), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+  }
   if (phases & kPartitions) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, false>), grid, dim3(64), 0, stream, a);
   }
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
@@ -500,13 +675,31 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim
   return static_cast<size_t>(ceil_div64(rows * head_dim * 4, 256) * 256 + ceil_div64(rows * 4, 256) * 256);
 }
 
+// The fused step keeps its partials per work unit (sequence, KV head, head
+// group, partition) in the lane-major layout of the kernel: 64 lanes x 4*(D/16)
+// floats, then 16 lse values per unit, then one arrival counter per
+// (sequence, KV head, head group).
+struct StepLayout {
+  size_t o_bytes, lse_bytes, ctr_bytes;
+  size_t total() const { return o_bytes + lse_bytes + ctr_bytes; }
+};
+StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int64_t parts) {
+  if (parts <= 1) return {0, 0, 0};
+  const int64_t groups = ceil_div64(num_heads / num_kv_heads, 16);
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * groups;
+  return {static_cast<size_t>(ceil_div64(units * parts * 64 * (head_dim / 4) * 4, 256) * 256),
+          static_cast<size_t>(ceil_div64(units * parts * 16 * 4, 256) * 256),
+          static_cast<size_t>(ceil_div64(units * 4, 256) * 256)};
+}
+
 // Validate, fill DecodeArgs and launch the requested phases. Pointers the
 // chosen phases never read may be null (the merge needs no q or caches).
 pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                         void* out, pkv_dtype dtype, const void* workspace, size_t workspace_bytes,
-                        int32_t partition_blocks, unsigned phases, void* stream) {
+                        int32_t partition_blocks, unsigned phases, void* stream, const void* k_new = nullptr,
+                        const void* v_new = nullptr) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
   if ((phases & kPartitions) && num_blocks <= 0) return PKV_EINVAL;
   if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
@@ -515,7 +708,8 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   if (partition_blocks < 0 || partition_blocks > 64) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!context_lens || !out) return PKV_EINVAL;
-  if ((phases & kPartitions) && (!q || !k_cache || !v_cache || !block_tables)) return PKV_EINVAL;
+  if ((phases & (kPartitions | kFusedStep)) && (!q || !k_cache || !v_cache || !block_tables)) return PKV_EINVAL;
+  if ((phases & kFusedStep) && (!k_new || !v_new)) return PKV_EINVAL;
   if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;  // every length clamps to 0 -> zero rows
 
   DecodeArgs a{};
@@ -537,13 +731,25 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, a.pb_per_part));
   a.qk_scale = scale * kLog2e;
   if (static_cast<int64_t>(num_kv_heads) * a.head_groups > 65535 || num_seqs > 65535) return PKV_EINVAL;
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.k_cache_w = const_cast<char*>(static_cast<const char*>(k_cache));
+  a.v_cache_w = const_cast<char*>(static_cast<const char*>(v_cache));
   if (a.num_parts > 1) {
-    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, a.num_parts);
-    if (!workspace || workspace_bytes < need) return PKV_ESMALL;
-    const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * a.num_parts;
     char* ws = const_cast<char*>(static_cast<const char*>(workspace));
-    a.ws_o = reinterpret_cast<float*>(ws);
-    a.ws_lse = reinterpret_cast<float*>(ws + ceil_div64(rows * head_dim * 4, 256) * 256);
+    if (phases & kFusedStep) {
+      const StepLayout L = step_layout(num_seqs, num_heads, num_kv_heads, head_dim, a.num_parts);
+      if (!workspace || workspace_bytes < L.total()) return PKV_ESMALL;
+      a.ws_o = reinterpret_cast<float*>(ws);
+      a.ws_lse = reinterpret_cast<float*>(ws + L.o_bytes);
+      a.counters = reinterpret_cast<int32_t*>(ws + L.o_bytes + L.lse_bytes);
+    } else {
+      const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, a.num_parts);
+      if (!workspace || workspace_bytes < need) return PKV_ESMALL;
+      const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads * a.num_parts;
+      a.ws_o = reinterpret_cast<float*>(ws);
+      a.ws_lse = reinterpret_cast<float*>(ws + ceil_div64(rows * head_dim * 4, 256) * 256);
+    }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
@@ -634,6 +840,24 @@ pkv_status pkv_decode_partitions(const void* q, const void* k_cache, const void*
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
                       partition_blocks, kPartitions, stream);
+}
+
+size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t partition_blocks) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
+  const int32_t pb = partition_blocks > 0 ? partition_blocks
+                                          : auto_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+  return step_layout(num_seqs, num_heads, num_kv_heads, head_dim, ceil_div64(max_blocks_per_seq, pb)).total();
+}
+
+pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                           void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
+                      partition_blocks, kFusedStep, stream, k_new, v_new);
 }
 
 pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

@@ -300,3 +300,120 @@ def test_phases_equal_fused_call(torch_dev):
         pkv.decode_merge(q, kc, vc, t, lens, b, ws, pb)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# fused decode step: append + attention + merge in one launch
+# ---------------------------------------------------------------------------
+def gpu_fused_step(torch, dev, wk, partition_blocks=0, reps=2):
+    """Run decode_step `reps` times on one workspace (the append is
+    idempotent); returns the raw outputs of every call and the final caches."""
+    cfg = wk.cfg
+    dt = cfg.dtype
+    q = wl.raw_to_torch(wk.q, dt, dev)
+    kc = wl.raw_to_torch(wk.k_cache, dt, dev)
+    vc = wl.raw_to_torch(wk.v_cache, dt, dev)
+    kn = wl.raw_to_torch(wk.k_new, dt, dev)
+    vn = wl.raw_to_torch(wk.v_new, dt, dev)
+    t = torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev)
+    lens = torch.from_numpy(wk.context_lens.astype(np.int32)).to(dev)
+    ws = pkv.alloc_step_workspace(q, kc, t, partition_blocks)
+    outs = []
+    for _ in range(reps):
+        out = torch.full_like(q, float("nan"))
+        pkv.decode_step(q, kn, vn, kc, vc, t, lens, cfg.scale, out, ws, partition_blocks)
+        torch.cuda.synchronize()
+        outs.append(wl.torch_to_raw(out, dt))
+    return outs, wl.torch_to_raw(kc, dt), wl.torch_to_raw(vc, dt)
+
+
+def fused_parity(torch, dev, wk, pb, what):
+    outs, kc, vc = gpu_fused_step(torch, dev, wk, pb)
+    key = id(wk)
+    if key not in _ORACLE_CACHE or _ORACLE_CACHE[key][0] is not wk:
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = (wk, oracle_step(wk))
+    ref, kc_o, vc_o, _ = _ORACLE_CACHE[key][1]
+    assert kc.tobytes() == kc_o.tobytes(), f"{what}: K pool after the fused append is not bit-identical"
+    assert vc.tobytes() == vc_o.tobytes(), f"{what}: V pool after the fused append is not bit-identical"
+    for o in outs:
+        check_close(oracle.upcast(o, wk.cfg.dtype), ref, wk.cfg.dtype, what)
+    assert all(o.tobytes() == outs[0].tobytes() for o in outs), f"{what}: repeated call differs"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fused_step_shapes_and_edge_lengths(torch_dev, dtype, shape):
+    torch, dev = torch_dev
+    Hq, Hkv, D = shape
+    cfg = wl.DecodeConfig("edge", 0, 1, len(EDGE_LENS), Hq, Hkv, D, 16, dtype, context_lens=EDGE_LENS)
+    wk = wl.make_host_workload(cfg, seed=2000 + Hq * 7 + Hkv + D)
+    for pb in (0, 1, 3, 8, 64):
+        note(f"fused step {dtype} Hq={Hq} Hkv={Hkv} D={D} partition_blocks={pb}")
+        fused_parity(torch, dev, wk, pb, f"fused {dtype} {shape} pb={pb}")
+
+
+def test_fused_step_tiny_config_and_shared_prefix(torch_dev):
+    torch, dev = torch_dev
+    note("fused step: tiny fp32 config")
+    wk = wl.make_host_workload(wl.CONFIGS[0])
+    for pb in (0, 1, 2):
+        fused_parity(torch, dev, wk, pb, f"fused tiny pb={pb}")
+    cfg = wl.DecodeConfig("prefix_share", 4, 1, 8, 28, 4, 128, 16, "bf16",
+                          context_lens=(1, 16, 17, 100, 511, 512, 513, 2000), shared_prefix_tokens=512)
+    wk = wl.make_host_workload(cfg)
+    for pb in (0, 2, 8):
+        note(f"fused step: shared prefix pb={pb}")
+        fused_parity(torch, dev, wk, pb, "fused shared prefix")
+
+
+def test_fused_step_zero_length_and_counters_reset(torch_dev):
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("zero", 0, 1, 4, 16, 2, 128, 16, "bf16", context_lens=(0, 300, 0, 33))
+    wk = wl.make_host_workload(cfg)
+    note("fused step: zero-length rows, 3 calls on one workspace")
+    outs, _, _ = gpu_fused_step(torch, dev, wk, 2, reps=3)
+    o = oracle.upcast(outs[-1], "bf16")
+    assert not o[0].any() and not o[2].any()
+    ref, _, _, _ = oracle_step(wk)
+    check_close(o, ref, "bf16", "fused zero-length")
+    # after the calls the arrival counters (workspace tail) are back to zero
+    q = wl.raw_to_torch(wk.q, "bf16", dev)
+    kc = wl.raw_to_torch(wk.k_cache, "bf16", dev)
+    t = torch.from_numpy(wk.block_tables).to(dev)
+    ws = pkv.alloc_step_workspace(q, kc, t, 2)
+    lens = torch.from_numpy(wk.context_lens).to(dev)
+    out = torch.empty_like(q)
+    for _ in range(2):
+        pkv.decode_step(q, wl.raw_to_torch(wk.k_new, "bf16", dev), wl.raw_to_torch(wk.v_new, "bf16", dev), kc,
+                        wl.raw_to_torch(wk.v_cache, "bf16", dev), t, lens, cfg.scale, out, ws, 2)
+    torch.cuda.synchronize()
+    # counters occupy the last 256-byte-rounded region: 4 seqs x 2 KV heads x 1 group
+    assert not ws[-256:].any(), "arrival counters not reset"
+
+
+@pytest.mark.parametrize("cfg_index", [1, 3, 4])
+def test_fused_step_full_size_sampled(torch_dev, cfg_index):
+    torch, dev = torch_dev
+    cfg = wl.CONFIGS[cfg_index]
+    note(f"fused step, full-size config {cfg.name}")
+    wkd = wl.make_device_workload(cfg, dev, layers=1)
+    lens = wkd.context_lens
+    order = np.argsort(lens)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(lens) // 2])})
+    ref = sampled_reference(torch, wkd, seqs)
+    out = torch.full_like(wkd.q[0], float("nan"))
+    ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables)
+    pkv.decode_step(wkd.q[0], wkd.k_new[0], wkd.v_new[0], wkd.k_cache[0], wkd.v_cache[0], wkd.block_tables,
+                    wkd.context_lens_dev, cfg.scale, out, ws)
+    torch.cuda.synchronize()
+    o = oracle.upcast(wl.torch_to_raw(out, cfg.dtype), cfg.dtype)
+    assert np.isfinite(o).all()
+    for b, r in ref.items():
+        check_close(o[b], r, cfg.dtype, f"fused {cfg.name} seq {b}")
+    # the appended token landed in its slot, bit for bit
+    for b in seqs:
+        n = int(lens[b])
+        pb = int(wkd.assignment.blocks[b][(n - 1) // 16])
+        got_k = wl.torch_to_raw(wkd.k_cache[0][pb, :, (n - 1) % 16], cfg.dtype)
+        assert got_k.tobytes() == wl.torch_to_raw(wkd.k_new[0][b], cfg.dtype).tobytes()
