@@ -267,6 +267,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const bool head_ok = hin < a.group;
   const int hq = j * a.group + (head_ok ? hin : 0);
 
+  // physical ids of this partition's blocks: lane i holds block blk0 + i
+  // (loaded first: the first K/V loads wait on it, the queries can arrive later)
+  int my_id = 0;
+  if (lane < nblk) my_id = a.block_tables[static_cast<size_t>(b) * a.max_blocks + blk0 + lane];
+
   // Q as the B operand, same chunk permutation as K
   u32x4 qv[S::kNK];
   {
@@ -275,10 +280,6 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     for (int c = 0; c < S::kNK; ++c)
       qv[c] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + q4) * 16) : u32x4{0, 0, 0, 0};
   }
-
-  // physical ids of this partition's blocks: lane i holds block blk0 + i
-  int my_id = 0;
-  if (lane < nblk) my_id = a.block_tables[static_cast<size_t>(b) * a.max_blocks + blk0 + lane];
 
   const size_t head_off = static_cast<size_t>(j) * S::kTileBytes;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * S::kTileBytes;
