@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of libpkv on one MI355X.
 
-One step = for every layer: append the new token's K/V (kv_append), then
-paged decode attention over the whole cache (partition kernel + LSE merge).
+One step = for every layer: append the new token's K/V, then paged decode
+attention over the whole cache. Default (--mode fused): one pkv_decode_step
+launch per layer (append + attention + merge); --mode split: kv_append,
+decode_partitions and decode_merge as three launches.
 Default workload: Llama-3-70B shape (64 query / 8 KV heads, head_dim 128,
 bf16), batch 32, context 4096, 80 layers looped, each layer with its own
 K/V pool (40 GiB resident) and one block table shared by the layers, built
@@ -126,7 +128,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 (no multi-GPU path exists)",
+        print("bench.py: the decode path runs on one GPU; --gpus must be 1 (there is no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
 

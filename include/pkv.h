@@ -53,7 +53,7 @@ typedef enum pkv_status {
   PKV_ERANGE = 2,       /* length beyond table capacity, id out of range          */
   PKV_ENOMEM = 3,       /* block pool exhausted                                    */
   PKV_EBUSY = 4,        /* write into a shared block, or two writes to one slot   */
-  PKV_EUNSUPPORTED = 5, /* head_dim / block_size / dtype this build does not cover */
+  PKV_EUNSUPPORTED = 5, /* head_dim / block_size the kernels do not implement       */
   PKV_EHIP = 6,         /* the HIP runtime reported an error at launch             */
   PKV_ESMALL = 7        /* caller-provided workspace or output buffer too small    */
 } pkv_status;

@@ -103,7 +103,7 @@ def full_parity(torch, dev, wk, partition_blocks=0, what=""):
 @pytest.mark.parametrize("partition_blocks", [0, 1, 2])
 def test_tiny_fp32_config(torch_dev, partition_blocks):
     torch, dev = torch_dev
-    cfg = wl.CONFIGS[0]
+    cfg = wl.CONFIG_BY_NAME["tiny_fp32"]
     note(f"tiny fp32 config, partition_blocks={partition_blocks}")
     wk = wl.make_host_workload(cfg)
     assert wk.assignment.num_blocks == 16 and wk.context_lens.tolist() == [18, 33]
@@ -113,7 +113,7 @@ def test_tiny_fp32_config(torch_dev, partition_blocks):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_tiny_config_16bit(torch_dev, dtype):
     torch, dev = torch_dev
-    base = wl.CONFIGS[0]
+    base = wl.CONFIG_BY_NAME["tiny_fp32"]
     cfg = wl.DecodeConfig("tiny_" + dtype, 0, 1, 2, 4, 2, 64, 16, dtype, context_lens=(18, 33), pool_blocks=16)
     note(f"tiny config in {dtype}")
     wk = wl.make_host_workload(cfg, seed=base.seed)
@@ -250,10 +250,10 @@ def sampled_reference(torch, wkd, seqs, layer=0):
     return out
 
 
-@pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
-def test_full_size_config_sampled(torch_dev, cfg_index):
+@pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "mha_contrast", "llama3_70b", "qwen25_7b_ragged"])
+def test_full_size_config_sampled(torch_dev, cfg_name):
     torch, dev = torch_dev
-    cfg = wl.CONFIGS[cfg_index]
+    cfg = wl.CONFIG_BY_NAME[cfg_name]
     note(f"full-size config {cfg.name}: drawing one layer on the device")
     wkd = wl.make_device_workload(cfg, dev, layers=1)
     lens = wkd.context_lens
@@ -356,7 +356,7 @@ def test_fused_step_shapes_and_edge_lengths(torch_dev, dtype, shape):
 def test_fused_step_tiny_config_and_shared_prefix(torch_dev):
     torch, dev = torch_dev
     note("fused step: tiny fp32 config")
-    wk = wl.make_host_workload(wl.CONFIGS[0])
+    wk = wl.make_host_workload(wl.CONFIG_BY_NAME["tiny_fp32"])
     for pb in (0, 1, 2):
         fused_parity(torch, dev, wk, pb, f"fused tiny pb={pb}")
     cfg = wl.DecodeConfig("prefix_share", 4, 1, 8, 28, 4, 128, 16, "bf16",
@@ -392,10 +392,10 @@ def test_fused_step_zero_length_and_counters_reset(torch_dev):
     assert not ws[-256:].any(), "arrival counters not reset"
 
 
-@pytest.mark.parametrize("cfg_index", [1, 3, 4])
-def test_fused_step_full_size_sampled(torch_dev, cfg_index):
+@pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "llama3_70b", "qwen25_7b_ragged"])
+def test_fused_step_full_size_sampled(torch_dev, cfg_name):
     torch, dev = torch_dev
-    cfg = wl.CONFIGS[cfg_index]
+    cfg = wl.CONFIG_BY_NAME[cfg_name]
     note(f"fused step, full-size config {cfg.name}")
     wkd = wl.make_device_workload(cfg, dev, layers=1)
     lens = wkd.context_lens
