@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--mode", choices=("fused", "split"), default="fused",
                     help="fused: one decode_step launch per layer (append + attention + merge); "
                          "split: kv_append, decode_partitions, decode_merge")
+    ap.add_argument("--kv", choices=("native", "fp8"), default="native",
+                    help="native: K/V cached in the configuration's dtype; fp8: E4M3 codes + fp32 per-row scales")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -149,27 +151,48 @@ def main():
     asg, slots, pool_stats = pool_assignment(cfg, lens, pkv, wl)
     log(f"block pool: {pool_stats}")
     t0 = time.time()
-    wkd = wl.make_device_workload(cfg, dev, layers=L, context_lens=lens, assignment=asg,
-                                  progress=lambda l: (l % 20 == 0) and log(f"  drew layer {l}/{L}"))
+    fp8 = args.kv == "fp8"
+    if fp8:
+        wkd = wl.make_device_workload_fp8(cfg, dev, layers=L, context_lens=lens, assignment=asg)
+    else:
+        wkd = wl.make_device_workload(cfg, dev, layers=L, context_lens=lens, assignment=asg,
+                                      progress=lambda l: (l % 20 == 0) and log(f"  drew layer {l}/{L}"))
     torch.cuda.synchronize()
     log(f"device workload ready in {time.time() - t0:.1f}s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
 
-    samples = cpu_samples(wkd) if args.cpu_budget > 0 else []
+    samples = cpu_samples(wkd) if (args.cpu_budget > 0 and not fp8) else []
 
     max_blocks = wkd.block_tables.shape[1]
     pb = args.partition_blocks or pkv.decode_partition_blocks(B, Hq, Hkv, max_blocks)
     fused = args.mode == "fused"
+    kcache0 = wkd.k_codes[0] if fp8 else wkd.k_cache[0]
     if fused:
-        ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables, pb)
+        ws = pkv.alloc_step_workspace(wkd.q[0], kcache0, wkd.block_tables, pb)
     else:
-        ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables, pb)
+        ws = pkv.alloc_workspace(wkd.q[0], kcache0, wkd.block_tables, pb)
     slots_d = torch.from_numpy(slots).to(dev)
     outs = [torch.empty_like(wkd.q[l]) for l in range(L)]
     stream = torch.cuda.current_stream()
 
     def step(events=None):
         for l in range(L):
+            if fp8:
+                if events is not None:
+                    events[l][0].record(stream)
+                if fused:
+                    pkv.decode_step_fp8(wkd.q[l], wkd.k_new[l], wkd.v_new[l], wkd.k_codes[l], wkd.v_codes[l],
+                                        wkd.k_scales[l], wkd.v_scales[l], wkd.block_tables, wkd.context_lens_dev,
+                                        cfg.scale, outs[l], ws, pb)
+                else:
+                    pkv.kv_append_fp8(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_codes[l], wkd.v_codes[l],
+                                      wkd.k_scales[l], wkd.v_scales[l])
+                    pkv.paged_decode_attention_fp8(wkd.q[l], wkd.k_codes[l], wkd.v_codes[l], wkd.k_scales[l],
+                                                   wkd.v_scales[l], wkd.block_tables, wkd.context_lens_dev,
+                                                   cfg.scale, outs[l], ws, pb)
+                if events is not None:
+                    events[l][1].record(stream)
+                continue
             if fused:
                 if events is not None:
                     events[l][0].record(stream)
@@ -221,17 +244,18 @@ def main():
 
     # algorithmic bytes
     sum_n = int(lens.sum())
-    kv_layer = 2 * Hkv * D * esz * sum_n
+    # K/V bytes read per layer: codes + one fp32 scale per row for FP8
+    kv_layer = 2 * Hkv * (D + 4) * sum_n if fp8 else 2 * Hkv * D * esz * sum_n
     q_out = 2 * B * Hq * D * esz
     tables = 4 * sum(-(-int(n) // bs) for n in lens) + 4 * B
-    append = 4 * B * Hkv * D * esz  # new K/V read and written (fused step only)
+    append = 2 * B * Hkv * D * esz + (2 * B * Hkv * (D + 4) if fp8 else 2 * B * Hkv * D * esz)  # fused step only
     part_alg = kv_layer + q_out + tables + (append if fused else 0)
     step_kv = kv_layer * L
     gbs = step_kv / (ms_per_step * 1e-3) / 1e9
     achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
 
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}_{cfg.name}_traffic.json")
+    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}{'_fp8' if fp8 else ''}_{cfg.name}_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
@@ -270,13 +294,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": (f"e4m3 K/V + f32 row scales, {cfg.dtype} q/out" if fp8 else cfg.dtype),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: batch {B}, context {'ragged' if cfg.context_len_range else int(lens[0])}, "
                                f"{Hq} query / {Hkv} KV heads, head_dim {D}, block 16, {L} layers, one decode step "
                                f"(append + attention) per layer",
                    "global_batch": B, "seq_len": int(lens.max()), "layers": L, "partition_blocks": pb,
-                   "mode": args.mode},
+                   "mode": args.mode, "kv": args.kv},
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(B / (ms_per_step * 1e-3), 2),
         "kv_bytes_per_step": step_kv,

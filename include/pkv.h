@@ -210,6 +210,53 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
                            int32_t block_size, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
                            void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
 
+/*
+ * FP8 KV cache. The pages name low-precision KV storage (INT8/FP8) with
+ * higher-precision arithmetic ("KV Cache and Inference Optimization", section
+ * "KV quantization") without fixing a format; these calls use:
+ *   - codes: OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias 7, 3
+ *     mantissa bits; no infinities; S.1111.111 is NaN; largest value 448),
+ *     caches [num_blocks, num_kv_heads, block_size, head_dim] of uint8;
+ *   - scales: one fp32 per token row of one KV head, arrays
+ *     [num_blocks, num_kv_heads, block_size];
+ *   - value attended over = code * scale;
+ *   - quantization of a new row x (head_dim values, computed in fp32):
+ *     amax = max |x|, scale = amax / 448, inv = 448 / amax (1 and 1 when
+ *     amax == 0), code = E4M3 nearest to x * inv (ties to even, clamped to
+ *     +-448, sign kept).
+ * Queries and outputs stay bf16 or fp16 (dtype); codes are converted exactly
+ * to that type in registers, scores and weights are scaled in fp32.
+ *
+ * pkv_kv_append_fp8 -- quantize each new token's K and V rows (k, v of type
+ *   `dtype`: f32, f16 or bf16) and write codes and scales into slot
+ *   slot_mapping[i]; slot < 0 skipped; otherwise as pkv_kv_append.
+ * pkv_paged_decode_attention_fp8 -- as pkv_paged_decode_attention over FP8
+ *   caches (dtype = q/out type: f16 or bf16; f32 is EUNSUPPORTED); the
+ *   workspace is sized by pkv_decode_workspace_bytes.
+ * pkv_decode_step_fp8 -- as pkv_decode_step over FP8 caches: the new rows
+ *   are quantized in the kernel with the rule above (bit-identical to
+ *   pkv_kv_append_fp8) and attended over as code * scale; workspace sized by
+ *   pkv_decode_step_workspace_bytes, zero-filled before first use.
+ */
+pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                             void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                             void* stream);
+pkv_status pkv_paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scales, const float* v_scales,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                          void* workspace, size_t workspace_bytes, int32_t partition_blocks,
+                                          void* stream);
+pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               float* k_scales, float* v_scales, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, int32_t partition_blocks, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block pool, block tables and slot mapping                            */
 /* ------------------------------------------------------------------------ */

@@ -27,4 +27,14 @@ from .paged_decode import (  # noqa: F401
     decode_attention,
     decode_attention_seq,
     kv_append,
+    gather_sequence_fp8,
+    decode_attention_fp8,
+    kv_append_fp8,
+)
+from .quant import (  # noqa: F401
+    e4m3_value,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_rows,
+    dequantize_rows,
 )

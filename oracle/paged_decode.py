@@ -88,6 +88,22 @@ def attention_weights(q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
     return e / e.sum()
 
 
+def _attend_heads(qf: np.ndarray, gather_k, gather_v, num_kv_heads: int, n: int, scale: float) -> np.ndarray:
+    """Query heads h of KV head h // g against that head's gathered K/V."""
+    num_heads, head_dim = qf.shape
+    if num_heads % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    group = num_heads // num_kv_heads
+    out = np.zeros((num_heads, head_dim), dtype=np.float64)
+    if n == 0:
+        return out
+    for j in range(num_kv_heads):
+        K, V = gather_k(j), gather_v(j)
+        for h in range(j * group, (j + 1) * group):
+            out[h] = attention_weights(qf[h], K, scale) @ V
+    return out
+
+
 def decode_attention_seq(q_b: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                          table_row: Sequence[int], n: int, scale: float, num_kv_heads: int,
                          block_size: int, dtype: str) -> np.ndarray:
@@ -99,21 +115,10 @@ def decode_attention_seq(q_b: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarr
     row n-1 of causal attention: the mask lets it see positions 0..n-1 (§1.2
     and §2.2 of the page "Understanding KV Cache"). n = 0 yields zeros.
     """
-    num_heads, head_dim = q_b.shape
-    if num_heads % num_kv_heads:
-        raise ValueError("num_heads must be a multiple of num_kv_heads")
-    group = num_heads // num_kv_heads
-    out = np.zeros((num_heads, head_dim), dtype=np.float64)
-    if n == 0:
-        return out
-    qf = upcast(q_b, dtype)
-    for j in range(num_kv_heads):
-        K = gather_sequence(k_cache, dtype, table_row, n, j, block_size)
-        V = gather_sequence(v_cache, dtype, table_row, n, j, block_size)
-        for h in range(j * group, (j + 1) * group):
-            alpha = attention_weights(qf[h], K, scale)
-            out[h] = alpha @ V
-    return out
+    return _attend_heads(upcast(q_b, dtype),
+                         lambda j: gather_sequence(k_cache, dtype, table_row, n, j, block_size),
+                         lambda j: gather_sequence(v_cache, dtype, table_row, n, j, block_size),
+                         num_kv_heads, n, scale)
 
 
 def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
@@ -146,3 +151,53 @@ def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new
         pb, off = s // block_size, s % block_size
         k_cache[pb, :, off, :] = k_new[i]
         v_cache[pb, :, off, :] = v_new[i]
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) caches: codes uint8 [NB, Hkv, bs, D], scales float32 [NB, Hkv, bs]
+# ---------------------------------------------------------------------------
+def gather_sequence_fp8(codes: np.ndarray, scales: np.ndarray, table_row: Sequence[int], n: int, kv_head: int,
+                        block_size: int) -> np.ndarray:
+    """Contiguous float64 [n, D] of decode(code) * scale for one KV head."""
+    from .quant import e4m3_decode
+    out = np.empty((n, codes.shape[-1]), dtype=np.float64)
+    for i in range(n):
+        _, off, pb, _ = slot_address(i, table_row, block_size)
+        out[i] = e4m3_decode(codes[pb, kv_head, off]) * np.float64(scales[pb, kv_head, off])
+    return out
+
+
+def decode_attention_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray,
+                         v_scales: np.ndarray, block_tables: np.ndarray, context_lens: Sequence[int], scale: float,
+                         num_kv_heads: int, block_size: int, q_dtype: str,
+                         seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Decode attention over FP8 caches: the same softmax attention, over the
+    dequantized cached values."""
+    B, Hq, D = q.shape
+    out = np.full((B, Hq, D), np.nan, dtype=np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        n = int(context_lens[b])
+        row = block_tables[b]
+        out[b] = _attend_heads(upcast(q[b], q_dtype),
+                               lambda j: gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size),
+                               lambda j: gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size),
+                               num_kv_heads, n, scale)
+    return out
+
+
+def kv_append_fp8(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray, v_scales: np.ndarray,
+                  k_new: np.ndarray, v_new: np.ndarray, slots: Sequence[int], block_size: int, in_dtype: str) -> None:
+    """Quantize each new token's K and V rows (one scale per KV head row, see
+    ``oracle.quant``) and write codes and scales into the slot, in place."""
+    from .quant import quantize_rows
+    kq, ks = quantize_rows(upcast(k_new, in_dtype).astype(np.float32))
+    vq, vs = quantize_rows(upcast(v_new, in_dtype).astype(np.float32))
+    for i, s in enumerate(slots):
+        s = int(s)
+        if s < 0:
+            continue
+        pb, off = s // block_size, s % block_size
+        k_codes[pb, :, off, :] = kq[i]
+        v_codes[pb, :, off, :] = vq[i]
+        k_scales[pb, :, off] = ks[i]
+        v_scales[pb, :, off] = vs[i]

@@ -1,0 +1,87 @@
+"""FP8 (OCP E4M3) KV-cache quantization, as plain NumPy.
+
+Test infrastructure only (see the package docstring).
+
+The pages name the idea -- store K/V in INT8/FP8 and keep higher-precision
+arithmetic -- without a format or a scaling rule (page "KV Cache and Inference
+Optimization", section "KV quantization"). This reference fixes the plainest
+reading, stated in full so that both sides take every rounding decision in the
+same precision:
+
+  * format: OCP 8-bit floating point E4M3 -- 1 sign bit, 4 exponent bits (bias
+    7), 3 mantissa bits; exponent field 0 encodes subnormals 2^-6 * m/8; no
+    infinities; S.1111.111 is NaN; the largest finite magnitude is 448;
+  * one scale per token row of one KV head (D values): scale = amax / 448 in
+    float32, inv = 448 / amax in float32 (amax = 0 gives scale 1 and inv 1);
+  * code = nearest E4M3 value to float32(x * inv), ties to the even code,
+    magnitudes above 448 saturate to 448, the sign bit is kept (a negative
+    value that rounds to zero gives -0);
+  * the cached value a kernel attends over is decode(code) * scale (exact in
+    float64).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Real value of one E4M3 code (NaN for S.1111.111)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * 2.0 ** -6 * (m / 8.0)
+    return sign * 2.0 ** (e - 7) * (1.0 + m / 8.0)
+
+
+# every non-negative finite code and its value, in increasing order (codes 0..126)
+_POS_CODES = np.arange(0, 0x7F, dtype=np.int64)
+_POS_VALUES = np.array([e4m3_value(c) for c in _POS_CODES], dtype=np.float64)
+assert np.all(np.diff(_POS_VALUES) > 0)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """float64 values of uint8 codes."""
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code (ties to the even code), saturating at 448; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_POS_VALUES, a, side="left"), 0, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = np.abs(_POS_VALUES[hi] - a)
+    d_lo = np.abs(a - _POS_VALUES[lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (_POS_CODES[lo] % 2 == 0))
+    code = np.where(pick_lo, _POS_CODES[lo], _POS_CODES[hi]).astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)  # the sign is kept, zero included
+    code = np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+    return code
+
+
+def quantize_rows(x: np.ndarray):
+    """Quantize the last axis of float32 ``x`` row by row.
+
+    Returns (codes uint8 with x's shape, scales float32 with x's shape minus the
+    last axis), following the module docstring step by step in float32.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1).astype(np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    y = (x * inv[..., None]).astype(np.float32)
+    return e4m3_encode(y), scale
+
+
+def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 values decode(code) * scale."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]

@@ -49,6 +49,11 @@ SIGNATURES = [
     ("pkv_decode_step_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     ("pkv_decode_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_kv_append_fp8", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    ("pkv_paged_decode_attention_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_decode_step_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                   _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
     ("pkv_seq_grow", _i32, [_vp, _i32, _i32]),
@@ -333,4 +338,73 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
                                 a["t"], a["mb"], a["lens"], B, a["Hq"], Hkv, D, a["bs"], a["NB"], float(scale),
                                 a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
     _check(st, "pkv_decode_step")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) caches: uint8 codes [NB, Hkv, bs, D] + fp32 scales [NB, Hkv, bs]
+# ---------------------------------------------------------------------------
+def _fp8_cache(codes, scales, name):
+    import torch
+    if codes.dtype != torch.uint8 or codes.dim() != 4:
+        raise TypeError(f"{name} codes must be a uint8 [NB, Hkv, bs, D] tensor")
+    if tuple(scales.shape) != tuple(codes.shape[:3]) or scales.dtype != torch.float32:
+        raise ValueError(f"{name} scales must be float32 [NB, Hkv, bs]")
+    return _dev(codes, name), _dev(scales, name + " scales")
+
+
+def kv_append_fp8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, stream=None):
+    """Quantize new K/V rows ([T, Hkv, D], f32/f16/bf16) into the FP8 caches."""
+    import torch
+    T, Hkv, D = k.shape
+    NB, Hkv2, bs, D2 = k_codes.shape
+    if (Hkv, D) != (Hkv2, D2) or tuple(v.shape) != tuple(k.shape) or tuple(v_codes.shape) != tuple(k_codes.shape):
+        raise ValueError("shape mismatch between k/v and the caches")
+    kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
+    vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
+    st = load().pkv_kv_append_fp8(_dev(k, "k"), _dev(v, "v", k.dtype), _dev(slot_mapping, "slot_mapping", torch.int64),
+                                  T, kc, vc, ks, vs, NB, Hkv, D, bs, _torch_dtype_code(k), _stream_ptr(stream))
+    _check(st, "pkv_kv_append_fp8")
+
+
+def _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace):
+    import torch
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_codes.shape
+    if D2 != D or tuple(v_codes.shape) != tuple(k_codes.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, maxNB] and context_lens [B]")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, t=_dev(block_tables, "block_tables", torch.int32),
+                mb=block_tables.shape[1], lens=_dev(context_lens, "context_lens", torch.int32),
+                out=_dev(out, "out", q.dtype), code=_torch_dtype_code(q), ws=ws_ptr, wsb=ws_bytes)
+
+
+def paged_decode_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, scale: float,
+                               out, workspace=None, partition_blocks: int = 0, stream=None):
+    a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace)
+    kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
+    vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
+    st = load().pkv_paged_decode_attention_fp8(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"],
+                                               a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], float(scale), a["out"],
+                                               a["code"], a["ws"], a["wsb"], int(partition_blocks),
+                                               _stream_ptr(stream))
+    _check(st, "pkv_paged_decode_attention_fp8")
+    return out
+
+
+def decode_step_fp8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                    scale: float, out, workspace=None, partition_blocks: int = 0, stream=None):
+    a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace)
+    if tuple(k_new.shape) != (a["B"], a["Hkv"], a["D"]) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, Hkv, D]")
+    kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
+    vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
+    st = load().pkv_decode_step_fp8(_dev(q, "q"), _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype), kc,
+                                    vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                    a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
+                                    int(partition_blocks), _stream_ptr(stream))
+    _check(st, "pkv_decode_step_fp8")
     return out

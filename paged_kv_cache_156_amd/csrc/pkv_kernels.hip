@@ -209,6 +209,127 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const char* kt, c
 }
 
 // ---------------------------------------------------------------------------
+// FP8 (OCP E4M3) caches: one code byte per element plus one fp32 scale per
+// token row of one KV head; the value attended over is code * scale.
+// ---------------------------------------------------------------------------
+// Raw registers of one FP8 block. K: lane (q4, r) holds token r's bytes
+// [q4*D/4, q4*D/4 + D/4) (MFMA chunk c = bytes 8c..8c+7 of that slice, the
+// queries use the same d order). V: rows 4*q4 + i, bytes [r*D/16, r*D/16 + D/16).
+// ks / vs: the scales of rows 4*q4 + i.
+template <int D>
+struct Fp8Regs {
+  u32x4 k[D / 64];
+  unsigned v[4][D / 64];
+  f32x4 ks, vs;
+};
+
+template <int D>
+__device__ __forceinline__ void load_block_fp8(Fp8Regs<D>& r, const char* kt, const char* vt, const char* kst,
+                                               const char* vst, int rows, int q4, int ln) {
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows * D);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows * D);
+  const __amdgpu_buffer_rsrc_t rks = tile_rsrc(kst, rows * 4);
+  const __amdgpu_buffer_rsrc_t rvs = tile_rsrc(vst, rows * 4);
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * D + q4 * (D / 4) + 16 * c, 0, kCacheNT);
+    r.k[c] = u32x4{v[0], v[1], v[2], v[3]};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int off = (4 * q4 + i) * D + ln * (D / 16);
+    if constexpr (D / 64 == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, kCacheNT);
+      r.v[i][0] = v[0];
+      r.v[i][1] = v[1];
+    } else {
+      r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, kCacheNT);
+    }
+  }
+  const auto ks = __builtin_amdgcn_raw_buffer_load_b128(rks, 16 * q4, 0, kCacheNT);
+  const auto vs = __builtin_amdgcn_raw_buffer_load_b128(rvs, 16 * q4, 0, kCacheNT);
+  r.ks = f32x4{__uint_as_float(ks[0]), __uint_as_float(ks[1]), __uint_as_float(ks[2]), __uint_as_float(ks[3])};
+  r.vs = f32x4{__uint_as_float(vs[0]), __uint_as_float(vs[1]), __uint_as_float(vs[2]), __uint_as_float(vs[3])};
+}
+
+// four E4M3 codes (one dword, lowest byte first) -> two dwords of 16-bit
+// values, exactly (every E4M3 value is representable in bf16 and fp16)
+template <typename T>
+__device__ __forceinline__ u32x2 fp8x4_to_16(unsigned w);
+template <>
+__device__ __forceinline__ u32x2 fp8x4_to_16<__bf16>(unsigned w) {
+  return u32x2{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+template <>
+__device__ __forceinline__ u32x2 fp8x4_to_16<_Float16>(unsigned w) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2{to_bits16<_Float16>(lo[0]) | (to_bits16<_Float16>(lo[1]) << 16),
+               to_bits16<_Float16>(hi[0]) | (to_bits16<_Float16>(hi[1]) << 16)};
+}
+
+// FP8 raw block -> the 16-bit operand registers of the MFMA pipeline
+template <typename T, int D>
+__device__ __forceinline__ void fp8_to_16(const Fp8Regs<D>& r, BlockRegs<T, D>& o) {
+#pragma unroll
+  for (int c = 0; c < Shape<T, D>::kNK; ++c) {  // chunk c = fp8 bytes 8c..8c+7 of the lane's slice
+    const u32x2 a = fp8x4_to_16<T>(r.k[c >> 1][(c & 1) * 2]);
+    const u32x2 b = fp8x4_to_16<T>(r.k[c >> 1][(c & 1) * 2 + 1]);
+    o.k[c] = u32x4{a[0], a[1], b[0], b[1]};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) {
+      const u32x2 a = fp8x4_to_16<T>(r.v[i][w]);
+      o.v[i][2 * w] = a[0];
+      o.v[i][2 * w + 1] = a[1];
+    }
+}
+
+// Quantize values of one token row to E4M3 given the row's absolute maximum:
+// scale = amax / 448, inv = 448 / amax (both fp32; amax == 0 -> 1, 1), and each
+// code is the nearest E4M3 value of x * inv (ties to even, clamped to +-448).
+struct RowQuant {
+  float scale, inv;
+};
+__device__ __forceinline__ RowQuant row_quant(float amax) {
+  if (amax == 0.f) return {1.f, 1.f};
+  return {amax / 448.0f, 448.0f / amax};
+}
+__device__ __forceinline__ unsigned quant4(float x0, float x1, float x2, float x3, float inv) {
+  auto c = [inv](float x) { return fminf(fmaxf(x * inv, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x0), c(x1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x2), c(x3), w, true);
+  return static_cast<unsigned>(w);
+}
+
+template <typename T>
+__device__ __forceinline__ float elt_to_float(const char* p);
+template <>
+__device__ __forceinline__ float elt_to_float<float>(const char* p) {
+  return *reinterpret_cast<const float*>(p);
+}
+template <>
+__device__ __forceinline__ float elt_to_float<__bf16>(const char* p) {
+  return from_bits16<__bf16>(*reinterpret_cast<const unsigned short*>(p));
+}
+template <>
+__device__ __forceinline__ float elt_to_float<_Float16>(const char* p) {
+  return from_bits16<_Float16>(*reinterpret_cast<const unsigned short*>(p));
+}
+
+template <typename T, int D, bool kFp8>
+struct RegsOf {
+  using type = BlockRegs<T, D>;
+};
+template <typename T, int D>
+struct RegsOf<T, D, true> {
+  using type = Fp8Regs<D>;
+};
+
+// ---------------------------------------------------------------------------
 // decode partition kernel
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
@@ -235,6 +356,9 @@ struct DecodeArgs {
   char* k_cache_w;      // the caches, writable
   char* v_cache_w;
   int32_t* counters;    // [B, Hkv, head_groups] arrival counters, zero between calls
+  // FP8 caches only: fp32 scale per (block, KV head, token row)
+  const char* k_scales;
+  const char* v_scales;
 };
 
 // kStep = false: one partition of attention (a split sequence leaves partials
@@ -242,10 +366,17 @@ struct DecodeArgs {
 // holds position n-1 also appends the newest token's K/V (written to its slot
 // and patched into its registers, never read back), and the last partition of
 // a split sequence to finish merges all partitions (arrival counter).
-template <typename T, int D, bool kStep>
+//
+// kFp8 = true: the caches hold E4M3 codes with per-row scales (T, the query
+// and output type, is bf16 or fp16); each block is converted exactly to T in
+// registers, the K scales multiply the scores and the V scales the weights.
+template <typename T, int D, bool kStep, bool kFp8>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
+  using R = typename RegsOf<T, D, kFp8>::type;
   constexpr bool k16 = sizeof(T) == 2;
+  static_assert(!kFp8 || k16, "FP8 caches are read with 16-bit queries");
+  constexpr int kCacheTile = kFp8 ? kBlockSize * D : S::kTileBytes;  // one KV head's block, bytes
   const int lane = threadIdx.x;
   const int q4 = lane >> 4;
   const int ln = lane & 15;
@@ -278,12 +409,17 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   {
     const char* qrow = a.q + (static_cast<size_t>(b) * a.num_heads + hq) * S::kRowBytes;
 #pragma unroll
-    for (int c = 0; c < S::kNK; ++c)
-      qv[c] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + q4) * 16) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < S::kNK; ++c) {
+      // byte offset of 16-byte chunk c: same-type caches (4c + q4) * 16 (the K
+      // tile's chunk order); FP8 caches (T is 16-bit) elements q4 * D/4 + 8c
+      const int off = kFp8 ? (q4 * (D / 4) + 8 * c) * 2 : (4 * c + q4) * 16;
+      static_assert(kFp8 ? (D / 4) * 2 <= S::kRowBytes : true, "query slice must lie inside the row");
+      qv[c] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0, 0, 0, 0};
+    }
   }
 
-  const size_t head_off = static_cast<size_t>(j) * S::kTileBytes;
-  const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * S::kTileBytes;
+  const size_t head_off = static_cast<size_t>(j) * kCacheTile;
+  const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * kCacheTile;
 
   // fused append: the partition holding position n-1 takes the new token's
   // K/V from k_new/v_new (row layout), in the same per-lane chunks the tiles use
@@ -292,7 +428,67 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const int new_row = (n - 1) % kBlockSize;
   u32x4 kn[S::kNK];
   unsigned vn[S::kVDW];
-  if constexpr (kStep) {
+  u32x4 kn8[D / 64];  // FP8: quantized new K slice (this lane's q4 slice)
+  unsigned vn8[D / 64];
+  float ks_new = 1.f, vs_new = 1.f;
+  if constexpr (kStep && kFp8) {
+    if (has_new) {  // wave-uniform
+      const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + j) * S::kRowBytes;
+      // K: this lane's D/4 values [q4*D/4, ...); the row maximum spans the 4 quarters
+      float kx[D / 4];
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) kx[e] = elt_to_float<T>(a.k_new + src + (q4 * (D / 4) + e) * S::kElt);
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) am = fmaxf(am, fabsf(kx[e]));
+      am = fmaxf(am, xor_shuffle(am, 16));
+      am = fmaxf(am, xor_shuffle(am, 32));
+      const RowQuant kq = row_quant(am);
+      ks_new = kq.scale;
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) {
+        unsigned w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          w[d] = quant4(kx[16 * c + 4 * d], kx[16 * c + 4 * d + 1], kx[16 * c + 4 * d + 2], kx[16 * c + 4 * d + 3],
+                        kq.inv);
+        kn8[c] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      // V: this lane's D/16 values [ln*D/16, ...); the maximum spans the 16 lanes of a quarter
+      float vx[D / 16];
+#pragma unroll
+      for (int e = 0; e < D / 16; ++e) vx[e] = elt_to_float<T>(a.v_new + src + (ln * (D / 16) + e) * S::kElt);
+      float vm = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 16; ++e) vm = fmaxf(vm, fabsf(vx[e]));
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) vm = fmaxf(vm, xor_shuffle(vm, m));
+      const RowQuant vq = row_quant(vm);
+      vs_new = vq.scale;
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w) vn8[w] = quant4(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq.inv);
+      // write codes and scales into the slot (head group 0 only)
+      const int id = __builtin_amdgcn_readlane(my_id, new_t);
+      if (hg == 0 && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) {
+        const size_t row = (static_cast<size_t>(id) * a.num_kv_heads + j) * kBlockSize + new_row;
+        if (ln == 0) {
+#pragma unroll
+          for (int c = 0; c < D / 64; ++c)
+            *reinterpret_cast<u32x4*>(a.k_cache_w + row * D + q4 * (D / 4) + 16 * c) = kn8[c];
+        }
+        if (q4 == 0) {
+          char* vd = a.v_cache_w + row * D + ln * (D / 16);
+          if constexpr (D / 64 == 2) *reinterpret_cast<u32x2*>(vd) = u32x2{vn8[0], vn8[1]};
+          else *reinterpret_cast<unsigned*>(vd) = vn8[0];
+        }
+        if (lane == 0) {
+          reinterpret_cast<float*>(const_cast<char*>(a.k_scales))[row] = ks_new;
+          reinterpret_cast<float*>(const_cast<char*>(a.v_scales))[row] = vs_new;
+        }
+      }
+    }
+  }
+  if constexpr (kStep && !kFp8) {
     if (has_new) {
       const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + j) * S::kRowBytes;
 #pragma unroll
@@ -334,30 +530,62 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   // Tile offset of the partition's block t and how many of its token rows to
   // fetch: 0 past the partition end or for an out-of-range id (nothing is
   // read then), else the block's tokens below n.
-  auto block_src = [&](int t, int& rows) -> size_t {
+  auto block_src = [&](int t, int& rows) -> size_t {  // returns (block id) * Hkv + j
     const int id = __builtin_amdgcn_readlane(my_id, min(t, 63));
     const bool ok = t < nblk && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
     rows = ok ? min(kBlockSize, n - (blk0 + t) * kBlockSize) : 0;
     if (kStep && t == new_t) rows = new_row;  // the new row comes from registers
-    return (ok ? static_cast<size_t>(id) : 0) * block_stride + head_off;
+    return (ok ? static_cast<size_t>(id) : 0) * a.num_kv_heads + j;
+  };
+  auto load_ring = [&](R& r, size_t tile, int rows) {
+    if constexpr (kFp8) {
+      load_block_fp8<D>(r, a.k_cache + tile * kCacheTile, a.v_cache + tile * kCacheTile,
+                        a.k_scales + tile * (kBlockSize * 4), a.v_scales + tile * (kBlockSize * 4), rows, q4, ln);
+    } else {
+      load_block<T, D>(r, a.k_cache + tile * kCacheTile, a.v_cache + tile * kCacheTile, rows, q4, ln);
+    }
   };
 
-  auto process = [&](BlockRegs<T, D>& r, int valid, int t) {  // valid: token rows of this block in range
+  auto process = [&](R& rr, int valid, int t) {  // valid: token rows of this block in range
     if constexpr (kStep) {
       if (t == new_t) {  // wave-uniform: patch in the appended token
         valid = new_row + 1;
-        if (ln == new_row) {
+        if constexpr (kFp8) {
+          if (ln == new_row) {
 #pragma unroll
-          for (int c = 0; c < S::kNK; ++c) r.k[c] = kn[c];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * q4 + i == new_row) {
-#pragma unroll
-            for (int w = 0; w < S::kVDW; ++w) r.v[i][w] = vn[w];
+            for (int c = 0; c < D / 64; ++c) rr.k[c] = kn8[c];
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * q4 + i == new_row) {
+#pragma unroll
+              for (int w = 0; w < D / 64; ++w) rr.v[i][w] = vn8[w];
+              rr.ks[i] = ks_new;
+              rr.vs[i] = vs_new;
+            }
+        } else {
+          if (ln == new_row) {
+#pragma unroll
+            for (int c = 0; c < S::kNK; ++c) rr.k[c] = kn[c];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * q4 + i == new_row) {
+#pragma unroll
+              for (int w = 0; w < S::kVDW; ++w) rr.v[i][w] = vn[w];
+            }
+        }
       }
     }
+    BlockRegs<T, D> conv;
+    BlockRegs<T, D>* rp;
+    if constexpr (kFp8) {
+      fp8_to_16<T, D>(rr, conv);
+      rp = &conv;
+    } else {
+      rp = &rr;
+    }
+    BlockRegs<T, D>& r = *rp;
     // scores
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (k16) {
@@ -372,7 +600,10 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = s[i] * a.qk_scale;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kFp8) sc[i] = s[i] * rr.ks[i] * a.qk_scale;
+      else sc[i] = s[i] * a.qk_scale;
+    }
     if (valid < kBlockSize) {  // wave-uniform: the last block of a sequence, or a bad id
       // rows past `valid` were not fetched (K and V read as zero), so no NaN
       // padding enters the MFMAs; their scores are selected out here
@@ -406,8 +637,10 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       unsigned ph[4], pl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ph[i] = to_bits16<T>(pr[i]);
-        pl[i] = to_bits16<T>(pr[i] - from_bits16<T>(ph[i]));
+        float pv = pr[i];
+        if constexpr (kFp8) pv *= rr.vs[i];  // FP8: the V scale rides on the weight
+        ph[i] = to_bits16<T>(pv);
+        pl[i] = to_bits16<T>(pv - from_bits16<T>(ph[i]));
       }
       l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       const u32x2 pw_hi = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
@@ -437,13 +670,13 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   // can wait on a precise outstanding-load count.
   constexpr int kAhead = sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT;
   constexpr int kRing = kAhead + 1;
-  BlockRegs<T, D> ring[kRing];
+  R ring[kRing];
   int ring_rows[kRing];
   if (nblk > 0) {  // wave-uniform; nblk == 0 only for an empty sequence
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
-      const size_t off = block_src(u, ring_rows[u]);
-      load_block<T, D>(ring[u], a.k_cache + off, a.v_cache + off, ring_rows[u], q4, ln);
+      const size_t tile = block_src(u, ring_rows[u]);
+      load_ring(ring[u], tile, ring_rows[u]);
     }
     // several ring rotations per loop iteration: only the first block after
     // the back-edge may see a conservative wait
@@ -453,8 +686,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       for (int uu = 0; uu < kUnroll; ++uu) {
         const int u = uu % kRing;
         const int slot = (u + kAhead) % kRing;
-        const size_t off = block_src(t0 + uu + kAhead, ring_rows[slot]);
-        load_block<T, D>(ring[slot], a.k_cache + off, a.v_cache + off, ring_rows[slot], q4, ln);
+        const size_t tile = block_src(t0 + uu + kAhead, ring_rows[slot]);
+        load_ring(ring[slot], tile, ring_rows[slot]);
         __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
         if (t0 + uu < nblk) process(ring[u], ring_rows[u], t0 + uu);
       }
@@ -655,6 +888,42 @@ __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
+// FP8 append: one wave per (token, KV head, K or V) quantizes the row (scale =
+// row amax / 448) and writes codes and scale into the slot
+// ---------------------------------------------------------------------------
+template <typename Tin, int D>
+__global__ __launch_bounds__(64) void append_fp8_kernel(const char* __restrict__ k, const char* __restrict__ v,
+                                                        const int64_t* __restrict__ slots, char* k_cache,
+                                                        char* v_cache, float* k_scales, float* v_scales,
+                                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots) {
+  constexpr int kPer = D / 64;  // elements per lane
+  const int lane = threadIdx.x;
+  const int j = blockIdx.x;
+  const int64_t i = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const char* src = (is_v ? v : k) + (i * num_kv_heads + j) * D * static_cast<int64_t>(sizeof(Tin));
+  float x[kPer];
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    x[e] = elt_to_float<Tin>(src + (lane * kPer + e) * sizeof(Tin));
+    am = fmaxf(am, fabsf(x[e]));
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, xor_shuffle(am, m));
+  const RowQuant rq = row_quant(am);
+  const int64_t pb = slot / block_size;
+  const int64_t row = (pb * num_kv_heads + j) * block_size + (slot - pb * block_size);
+  char* dst = (is_v ? v_cache : k_cache) + row * D + lane * kPer;
+  const unsigned codes = quant4(x[0], kPer > 1 ? x[kPer - 1] : 0.f, 0.f, 0.f, rq.inv);
+  if constexpr (kPer == 2) *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(codes & 0xffffu);
+  else *reinterpret_cast<unsigned char*>(dst) = static_cast<unsigned char>(codes & 0xffu);
+  if (lane == 0) (is_v ? v_scales : k_scales)[row] = rq.scale;
+}
+
+// ---------------------------------------------------------------------------
 // host-side helpers
 // ---------------------------------------------------------------------------
 int elt_bytes(pkv_dtype dt) {
@@ -683,16 +952,16 @@ int32_t auto_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_k
 
 enum Phase : unsigned { kPartitions = 1u, kMerge = 2u, kFusedStep = 4u };
 
-template <typename T, int D>
+template <typename T, int D, bool kFp8 = false>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
   if (phases & kFusedStep) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, true>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, true, kFp8>), grid, dim3(64), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
   if (phases & kPartitions) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, false>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, false, kFp8>), grid, dim3(64), 0, stream, a);
   }
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
@@ -732,7 +1001,8 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                         void* out, pkv_dtype dtype, const void* workspace, size_t workspace_bytes,
                         int32_t partition_blocks, unsigned phases, void* stream, const void* k_new = nullptr,
-                        const void* v_new = nullptr) {
+                        const void* v_new = nullptr, const float* k_scales = nullptr,
+                        const float* v_scales = nullptr, bool fp8 = false) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
   if ((phases & kPartitions) && num_blocks <= 0) return PKV_EINVAL;
   if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
@@ -743,6 +1013,8 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   if (!context_lens || !out) return PKV_EINVAL;
   if ((phases & (kPartitions | kFusedStep)) && (!q || !k_cache || !v_cache || !block_tables)) return PKV_EINVAL;
   if ((phases & kFusedStep) && (!k_new || !v_new)) return PKV_EINVAL;
+  if (fp8 && (phases & (kPartitions | kFusedStep)) && (!k_scales || !v_scales)) return PKV_EINVAL;
+  if (fp8 && dtype == PKV_F32) return PKV_EUNSUPPORTED;
   if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;  // every length clamps to 0 -> zero rows
 
   DecodeArgs a{};
@@ -764,6 +1036,8 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, a.pb_per_part));
   a.qk_scale = scale * kLog2e;
   if (static_cast<int64_t>(num_kv_heads) * a.head_groups > 65535 || num_seqs > 65535) return PKV_EINVAL;
+  a.k_scales = reinterpret_cast<const char*>(k_scales);
+  a.v_scales = reinterpret_cast<const char*>(v_scales);
   a.k_new = static_cast<const char*>(k_new);
   a.v_new = static_cast<const char*>(v_new);
   a.k_cache_w = const_cast<char*>(static_cast<const char*>(k_cache));
@@ -785,6 +1059,13 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8) {
+    if (dtype == PKV_BF16)
+      return head_dim == 128 ? launch_decode<__bf16, 128, true>(a, num_seqs, phases, s)
+                             : launch_decode<__bf16, 64, true>(a, num_seqs, phases, s);
+    return head_dim == 128 ? launch_decode<_Float16, 128, true>(a, num_seqs, phases, s)
+                           : launch_decode<_Float16, 64, true>(a, num_seqs, phases, s);
+  }
   switch (dtype) {
     case PKV_BF16:
       return head_dim == 128 ? launch_decode<__bf16, 128>(a, num_seqs, phases, s)
@@ -891,6 +1172,56 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
                       partition_blocks, kFusedStep, stream, k_new, v_new);
+}
+
+pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                             void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                             void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0) return PKV_EINVAL;
+  if (elt_bytes(dtype) == 0) return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (num_kv_heads > 65535 || num_tokens > 65535) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales) return PKV_EINVAL;
+  dim3 grid(num_kv_heads, num_tokens, 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, static_cast<const char*>(k), static_cast<const char*>(v),
+                       slot_mapping, static_cast<char*>(k_cache), static_cast<char*>(v_cache), k_scales, v_scales,
+                       num_kv_heads, block_size, num_slots);
+  };
+  switch (dtype) {
+    case PKV_F32: head_dim == 128 ? go(append_fp8_kernel<float, 128>) : go(append_fp8_kernel<float, 64>); break;
+    case PKV_F16: head_dim == 128 ? go(append_fp8_kernel<_Float16, 128>) : go(append_fp8_kernel<_Float16, 64>); break;
+    case PKV_BF16: head_dim == 128 ? go(append_fp8_kernel<__bf16, 128>) : go(append_fp8_kernel<__bf16, 64>); break;
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+pkv_status pkv_paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scales, const float* v_scales,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                          void* workspace, size_t workspace_bytes, int32_t partition_blocks,
+                                          void* stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
+                      partition_blocks, kPartitions | kMerge, stream, nullptr, nullptr, k_scales, v_scales, true);
+}
+
+pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               float* k_scales, float* v_scales, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
+                      partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, true);
 }
 
 pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

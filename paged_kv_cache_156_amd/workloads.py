@@ -400,3 +400,164 @@ def make_device_workload(cfg: DecodeConfig, device, layers: int = 1, seed: Optio
     tables = torch.from_numpy(asg.table()).to(device)
     lens_dev = torch.from_numpy(lens.astype(np.int32)).to(device)
     return DeviceWorkload(cfg, lens, asg, qs, kns, vns, kcs, vcs, tables, lens_dev)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) caches: the cached codes and per-row scales are drawn directly as
+# input data (any finite code, scales spread over an order of magnitude); the
+# new tokens' K/V are drawn like every other value and quantized by the path.
+# ---------------------------------------------------------------------------
+FP8_NAN = 0x7F
+
+
+def draw_fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ np.uint8(1), c).astype(np.uint8)  # no NaN codes
+
+
+def draw_fp8_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    return (rng.uniform(0.3, 3.0, size=shape) / 448.0).astype(np.float32)
+
+
+@dataclasses.dataclass
+class HostWorkloadFp8:
+    cfg: DecodeConfig  # cfg.dtype is the query / output / new-token type
+    context_lens: np.ndarray
+    assignment: BlockAssignment
+    q: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    k_codes: np.ndarray  # uint8 [NB, Hkv, bs, D]
+    v_codes: np.ndarray
+    k_scales: np.ndarray  # float32 [NB, Hkv, bs]
+    v_scales: np.ndarray
+
+    @property
+    def block_tables(self) -> np.ndarray:
+        return self.assignment.table()
+
+
+def make_host_workload_fp8(cfg: DecodeConfig, context_lens: Optional[Sequence[int]] = None,
+                           seed: Optional[int] = None, pool_blocks: Optional[int] = None) -> HostWorkloadFp8:
+    seed = cfg.seed if seed is None else seed
+    r_val, r_perm, r_len = streams(seed)
+    lens = draw_context_lens(cfg, r_len) if context_lens is None else np.asarray(context_lens, dtype=np.int32)
+    B, Hq, Hkv, D, bs = len(lens), cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    pool = cfg.pool_blocks if pool_blocks is None else pool_blocks
+    asg = assign_blocks(lens, bs, r_perm, cfg.shared_prefix_tokens, pool)
+    q = draw_values(r_val, (B, Hq, D), cfg.dtype)
+    k_new = draw_values(r_val, (B, Hkv, D), cfg.dtype)
+    v_new = draw_values(r_val, (B, Hkv, D), cfg.dtype)
+    kc = np.full((asg.num_blocks, Hkv, bs, D), FP8_NAN, np.uint8)
+    vc = np.full((asg.num_blocks, Hkv, bs, D), FP8_NAN, np.uint8)
+    ks = np.full((asg.num_blocks, Hkv, bs), np.nan, np.float32)
+    vs = np.full((asg.num_blocks, Hkv, bs), np.nan, np.float32)
+    n_pref = len(asg.shared_ids)
+    pref = [(draw_fp8_codes(r_val, (Hkv, bs, D)), draw_fp8_codes(r_val, (Hkv, bs, D)),
+             draw_fp8_scales(r_val, (Hkv, bs)), draw_fp8_scales(r_val, (Hkv, bs))) for _ in range(n_pref)]
+    for lb, pb in enumerate(asg.shared_ids):
+        kc[pb], vc[pb], ks[pb], vs[pb] = pref[lb]
+    shared = set(int(x) for x in asg.shared_ids)
+    for b, n in enumerate(lens):
+        n = int(n)
+        for lb, pb in enumerate(asg.blocks[b]):
+            pb = int(pb)
+            if pb in shared:
+                continue
+            cnt = min(bs, max(0, n - 1 - lb * bs))
+            if cnt <= 0:
+                continue
+            if lb < n_pref:
+                src = pref[lb]
+                kc[pb, :, :cnt], vc[pb, :, :cnt] = src[0][:, :cnt], src[1][:, :cnt]
+                ks[pb, :, :cnt], vs[pb, :, :cnt] = src[2][:, :cnt], src[3][:, :cnt]
+            else:
+                kc[pb, :, :cnt] = draw_fp8_codes(r_val, (Hkv, cnt, D))
+                vc[pb, :, :cnt] = draw_fp8_codes(r_val, (Hkv, cnt, D))
+                ks[pb, :, :cnt] = draw_fp8_scales(r_val, (Hkv, cnt))
+                vs[pb, :, :cnt] = draw_fp8_scales(r_val, (Hkv, cnt))
+    return HostWorkloadFp8(cfg, lens, asg, q, k_new, v_new, kc, vc, ks, vs)
+
+
+@dataclasses.dataclass
+class DeviceWorkloadFp8:
+    cfg: DecodeConfig
+    context_lens: np.ndarray
+    assignment: BlockAssignment
+    q: list
+    k_new: list
+    v_new: list
+    k_codes: list  # per layer uint8 [NB, Hkv, bs, D]
+    v_codes: list
+    k_scales: list  # per layer float32 [NB, Hkv, bs]
+    v_scales: list
+    block_tables: object
+    context_lens_dev: object
+
+    @property
+    def layers(self) -> int:
+        return len(self.k_codes)
+
+
+def fill_codes_device(t, generator):
+    import torch
+    flat = t.view(-1)
+    chunk = 1 << 28
+    for s in range(0, flat.numel(), chunk):
+        e = min(flat.numel(), s + chunk)
+        c = torch.randint(0, 256, (e - s,), generator=generator, device=t.device, dtype=torch.int32)
+        c = torch.where((c & 0x7F) == 0x7F, c ^ 1, c)
+        flat[s:e].copy_(c)
+    return t
+
+
+def make_device_workload_fp8(cfg: DecodeConfig, device, layers: int = 1, seed: Optional[int] = None,
+                             context_lens: Optional[np.ndarray] = None,
+                             assignment: Optional[BlockAssignment] = None) -> DeviceWorkloadFp8:
+    import torch
+    seed = cfg.seed if seed is None else seed
+    if assignment is None:
+        lens, asg = make_structure(cfg, seed)
+    else:
+        lens, asg = np.asarray(context_lens, np.int32), assignment
+    gen = value_generator(seed, device)
+    tdt = torch_dtype(cfg.dtype)
+    B, Hq, Hkv, D, bs = len(lens), cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    out = dict(q=[], k_new=[], v_new=[], k_codes=[], v_codes=[], k_scales=[], v_scales=[])
+    for _ in range(layers):
+        for name in ("k_codes", "v_codes"):
+            out[name].append(fill_codes_device(torch.empty((asg.num_blocks, Hkv, bs, D), dtype=torch.uint8,
+                                                           device=device), gen))
+        for name in ("k_scales", "v_scales"):
+            sc = torch.rand((asg.num_blocks, Hkv, bs), generator=gen, device=device, dtype=torch.float32)
+            out[name].append(sc.mul_(2.7).add_(0.3).div_(448.0))
+        # copy-on-write set-up and poison, as for 16-bit caches
+        n_pref = len(asg.shared_ids)
+        shared = set(int(x) for x in asg.shared_ids)
+        for b, blocks in enumerate(asg.blocks):
+            for lb in range(min(n_pref, len(blocks))):
+                pb = int(blocks[lb])
+                if pb not in shared:
+                    src = int(asg.shared_ids[lb])
+                    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+                        out[name][-1][pb].copy_(out[name][-1][src])
+        for name in ("k_codes", "v_codes"):
+            out[name][-1][asg.poison_block].fill_(FP8_NAN)
+        for name in ("k_scales", "v_scales"):
+            out[name][-1][asg.poison_block].fill_(float("nan"))
+        for b, n in enumerate(lens):
+            n = int(n)
+            if n == 0:
+                continue
+            pb = int(asg.blocks[b][(n - 1) // bs])
+            off = (n - 1) % bs
+            for name in ("k_codes", "v_codes"):
+                out[name][-1][pb, :, off:].fill_(FP8_NAN)
+            for name in ("k_scales", "v_scales"):
+                out[name][-1][pb, :, off:].fill_(float("nan"))
+        for name, shape in (("q", (B, Hq, D)), ("k_new", (B, Hkv, D)), ("v_new", (B, Hkv, D))):
+            out[name].append(fill_pool_device(torch.empty(shape, dtype=tdt, device=device), gen))
+    tables = torch.from_numpy(asg.table()).to(device)
+    lens_dev = torch.from_numpy(lens.astype(np.int32)).to(device)
+    return DeviceWorkloadFp8(cfg, lens, asg, out["q"], out["k_new"], out["v_new"], out["k_codes"], out["v_codes"],
+                             out["k_scales"], out["v_scales"], tables, lens_dev)

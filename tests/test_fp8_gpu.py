@@ -1,0 +1,177 @@
+"""GPU parity of the FP8 (E4M3) KV cache path against the CPU reference.
+
+The quantizing append (separate kernel and fused into the decode step) must
+match the reference bit for bit: codes and fp32 scales. Attention over the
+FP8 cache is compared with the reference attention over the dequantized
+values (code * scale, exact in float64) at the 16-bit tolerance
+|gpu - ref| <= 2e-3 + 1e-2 |ref|: the kernel converts codes exactly, so only
+fp32 accumulation, the weight split and output rounding separate the two.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_156_amd import binding as pkv
+from paged_kv_cache_156_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load()
+    return torch, torch.device("cuda:0")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bound = 2e-3 + 1e-2 * np.abs(ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert (err <= bound).all(), f"{what}: max|err|={err.max():.3e} at {worst}: {got[worst]} vs {ref[worst]}"
+
+
+def to_dev(torch, dev, wk):
+    dt = wk.cfg.dtype
+    return dict(q=wl.raw_to_torch(wk.q, dt, dev), kn=wl.raw_to_torch(wk.k_new, dt, dev),
+                vn=wl.raw_to_torch(wk.v_new, dt, dev), kc=torch.from_numpy(wk.k_codes.copy()).to(dev),
+                vc=torch.from_numpy(wk.v_codes.copy()).to(dev), ks=torch.from_numpy(wk.k_scales.copy()).to(dev),
+                vs=torch.from_numpy(wk.v_scales.copy()).to(dev),
+                t=torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev),
+                lens=torch.from_numpy(wk.context_lens.astype(np.int32)).to(dev))
+
+
+def oracle_fp8(wk):
+    """Reference append (quantize) + attention over the dequantized cache."""
+    cfg = wk.cfg
+    kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
+    slots = oracle.slot_mapping(wk.block_tables, wk.context_lens - 1, cfg.block_size)
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, cfg.block_size, cfg.dtype)
+    ref = oracle.decode_attention_fp8(wk.q, kc, vc, ks, vs, wk.block_tables, wk.context_lens, cfg.scale,
+                                      cfg.num_kv_heads, cfg.block_size, cfg.dtype)
+    return ref, kc, vc, ks, vs
+
+
+def assert_caches_equal(torch, d, kc, vc, ks, vs, what):
+    assert d["kc"].cpu().numpy().tobytes() == kc.tobytes(), f"{what}: K codes differ"
+    assert d["vc"].cpu().numpy().tobytes() == vc.tobytes(), f"{what}: V codes differ"
+    assert d["ks"].cpu().numpy().tobytes() == ks.tobytes(), f"{what}: K scales differ"
+    assert d["vs"].cpu().numpy().tobytes() == vs.tobytes(), f"{what}: V scales differ"
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_append_bit_exact(torch_dev, in_dtype, D):
+    torch, dev = torch_dev
+    note(f"fp8 append: {in_dtype} rows, D={D}")
+    cfg = wl.DecodeConfig("fp8app", 0, 1, 6, 8, 4, D, 16, in_dtype, context_lens=(1, 16, 17, 40, 300, 33))
+    wk = wl.make_host_workload_fp8(cfg)
+    # scale some rows up and down so amax spans many binades
+    wk.k_new[:] = wl.draw_values(np.random.default_rng(9), wk.k_new.shape, in_dtype)
+    d = to_dev(torch, dev, wk)
+    slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
+    slots[2] = -1  # a padding token
+    pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"])
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, 16, in_dtype)
+    assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 append")
+
+
+def test_fp8_append_extreme_rows(torch_dev):
+    """Rows with a zero amax, a single huge value, and subnormal-range values."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("fp8ext", 0, 1, 4, 4, 2, 128, 16, "f32", context_lens=(3, 20, 33, 50))
+    wk = wl.make_host_workload_fp8(cfg)
+    wk.k_new[0] = 0.0
+    wk.k_new[1] = 1e-6
+    wk.k_new[1, :, 5] = 3e4
+    wk.v_new[2] = np.float32(2.0 ** -20) * np.arange(128, dtype=np.float32)
+    wk.v_new[3, 0] = -0.0
+    d = to_dev(torch, dev, wk)
+    slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
+    pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"])
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, 16, "f32")
+    assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 append, extreme rows")
+
+
+EDGE_LENS = (1, 2, 15, 16, 17, 33, 128, 129, 257, 600)
+SHAPES = [(4, 2, 64), (32, 8, 128), (8, 8, 64), (64, 8, 128), (28, 4, 128), (64, 2, 128)]
+
+
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_attention_and_fused_step(torch_dev, q_dtype, shape):
+    torch, dev = torch_dev
+    Hq, Hkv, D = shape
+    cfg = wl.DecodeConfig("fp8", 0, 1, len(EDGE_LENS), Hq, Hkv, D, 16, q_dtype, context_lens=EDGE_LENS)
+    wk = wl.make_host_workload_fp8(cfg, seed=3000 + Hq + Hkv + D)
+    ref, kc, vc, ks, vs = oracle_fp8(wk)
+    for pb in (0, 1, 3, 64):
+        note(f"fp8 {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: append + attention")
+        d = to_dev(torch, dev, wk)
+        slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
+        pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"])
+        out = torch.full_like(d["q"], float("nan"))
+        ws = pkv.alloc_workspace(d["q"], d["kc"], d["t"], pb)
+        pkv.paged_decode_attention_fp8(d["q"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"], cfg.scale,
+                                       out, ws, pb)
+        torch.cuda.synchronize()
+        assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 split path")
+        check_close(oracle.upcast(wl.torch_to_raw(out, q_dtype), q_dtype), ref, f"fp8 split {shape} pb={pb}")
+        note(f"fp8 {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: fused step x2")
+        d = to_dev(torch, dev, wk)
+        ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], pb)
+        outs = []
+        for _ in range(2):
+            out = torch.full_like(d["q"], float("nan"))
+            pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                                cfg.scale, out, ws, pb)
+            torch.cuda.synchronize()
+            outs.append(wl.torch_to_raw(out, q_dtype))
+        assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 fused step")
+        check_close(oracle.upcast(outs[0], q_dtype), ref, f"fp8 fused {shape} pb={pb}")
+        assert outs[0].tobytes() == outs[1].tobytes()
+
+
+def test_fp8_full_size_70b_sampled(torch_dev):
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME["llama3_70b"]
+    note("fp8 full-size Llama-3-70B layer: drawing on the device")
+    wkd = wl.make_device_workload_fp8(cfg, dev, layers=1)
+    seqs = [0, 13, 31]
+    refs = {}
+    for b in seqs:  # reference on the sampled sequences' blocks, copied back before the append
+        idx = torch.from_numpy(wkd.assignment.blocks[b].astype(np.int64)).to(dev)
+        kc = wkd.k_codes[0].index_select(0, idx).cpu().numpy()
+        vc = wkd.v_codes[0].index_select(0, idx).cpu().numpy()
+        ks = wkd.k_scales[0].index_select(0, idx).cpu().numpy()
+        vs = wkd.v_scales[0].index_select(0, idx).cpu().numpy()
+        table = np.arange(len(idx), dtype=np.int32)[None, :]
+        n = int(wkd.context_lens[b])
+        slots = oracle.slot_mapping(table, [n - 1], 16)
+        oracle.kv_append_fp8(kc, vc, ks, vs, wl.torch_to_raw(wkd.k_new[0][b:b + 1], "bf16"),
+                             wl.torch_to_raw(wkd.v_new[0][b:b + 1], "bf16"), slots, 16, "bf16")
+        refs[b] = oracle.decode_attention_fp8(wl.torch_to_raw(wkd.q[0][b:b + 1], "bf16"), kc, vc, ks, vs, table, [n],
+                                              cfg.scale, cfg.num_kv_heads, 16, "bf16")[0]
+    out = torch.full_like(wkd.q[0], float("nan"))
+    ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_codes[0], wkd.block_tables)
+    pkv.decode_step_fp8(wkd.q[0], wkd.k_new[0], wkd.v_new[0], wkd.k_codes[0], wkd.v_codes[0], wkd.k_scales[0],
+                        wkd.v_scales[0], wkd.block_tables, wkd.context_lens_dev, cfg.scale, out, ws)
+    torch.cuda.synchronize()
+    o = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
+    assert np.isfinite(o).all()
+    for b, r in refs.items():
+        check_close(o[b], r, f"fp8 70B seq {b}")
