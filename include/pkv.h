@@ -130,7 +130,7 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t n
  *                 rounded from fp32 to the output type to nearest-even
  *   workspace     device scratch of >= pkv_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0); contents on entry ignored
- *   partition_blocks  blocks per partition, 0 = the library's choice
+ *   partition_blocks  blocks per partition (1..128), 0 = the library's choice
  *
  * Accumulation is fp32. Preconditions the device does not check at full
  * cost: context_lens[b] <= max_blocks_per_seq * block_size and table entries

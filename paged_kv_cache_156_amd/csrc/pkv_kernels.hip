@@ -55,6 +55,7 @@ using s16x4 = short __attribute__((ext_vector_type(4)));
 using f16x4 = _Float16 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockSize = 16;
+constexpr int kMaxPartitionBlocks = 128;  // two block ids per lane
 
 // K/V blocks kept in flight per wave ahead of the one being consumed
 #ifndef PKV_AHEAD_16BIT
@@ -62,6 +63,9 @@ constexpr int kBlockSize = 16;
 #endif
 #ifndef PKV_AHEAD_32BIT
 #define PKV_AHEAD_32BIT 1
+#endif
+#ifndef PKV_AHEAD_FP8
+#define PKV_AHEAD_FP8 2
 #endif
 #ifndef PKV_RING_ROTATIONS
 #define PKV_RING_ROTATIONS 3
@@ -347,7 +351,7 @@ struct DecodeArgs {
   int32_t group;        // Hq / Hkv
   int32_t head_groups;  // ceil(group / 16)
   int32_t num_blocks;
-  int32_t pb_per_part;  // blocks per partition (<= 64)
+  int32_t pb_per_part;  // blocks per partition (<= 128)
   int32_t num_parts;    // P
   float qk_scale;       // scale * log2(e)
   // fused decode step only
@@ -386,23 +390,29 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
 
   const int cap = a.max_blocks * kBlockSize;
+  const int blk0 = p * a.pb_per_part;
+  // Physical ids of this partition's blocks (lane i: block blk0 + i, and
+  // blk0 + 64 + i for partitions longer than 64 blocks). They are loaded
+  // together with the sequence length, bounded by the table width rather than
+  // by the length, so the first K/V loads wait for one round trip, not two.
+  const size_t trow = static_cast<size_t>(b) * a.max_blocks;
+  int my_id = 0, my_id2 = 0;
+  if (lane < a.pb_per_part && blk0 + lane < a.max_blocks) my_id = a.block_tables[trow + blk0 + lane];
+  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < a.max_blocks) my_id2 = a.block_tables[trow + blk0 + 64 + lane];
   int n = a.context_lens[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
   const int nblk_seq = (n + kBlockSize - 1) / kBlockSize;
   const int nparts = nblk_seq == 0 ? 1 : (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
   if (p >= nparts) return;
-  const int blk0 = p * a.pb_per_part;
   const int nblk = min(a.pb_per_part, nblk_seq - blk0);  // may be 0 only when n == 0
+  auto block_id = [&](int t) -> int {  // t wave-uniform, < 128
+    return t < 64 ? __builtin_amdgcn_readlane(my_id, t & 63) : __builtin_amdgcn_readlane(my_id2, t & 63);
+  };
 
   // this lane's query head (column of the score tile)
   const int hin = hg * 16 + ln;                 // head index inside the GQA group
   const bool head_ok = hin < a.group;
   const int hq = j * a.group + (head_ok ? hin : 0);
-
-  // physical ids of this partition's blocks: lane i holds block blk0 + i
-  // (loaded first: the first K/V loads wait on it, the queries can arrive later)
-  int my_id = 0;
-  if (lane < nblk) my_id = a.block_tables[static_cast<size_t>(b) * a.max_blocks + blk0 + lane];
 
   // Q as the B operand, same chunk permutation as K
   u32x4 qv[S::kNK];
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < D / 64; ++w) vn8[w] = quant4(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq.inv);
       // write codes and scales into the slot (head group 0 only)
-      const int id = __builtin_amdgcn_readlane(my_id, new_t);
+      const int id = block_id(new_t);
       if (hg == 0 && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) {
         const size_t row = (static_cast<size_t>(id) * a.num_kv_heads + j) * kBlockSize + new_row;
         if (ln == 0) {
@@ -509,7 +519,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         }
       }
       // write it into its slot (one head group writes; the others only read)
-      const int id = __builtin_amdgcn_readlane(my_id, new_t);
+      const int id = block_id(new_t);
       if (hg == 0 && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) {
         const size_t dst = static_cast<size_t>(id) * block_stride + head_off + new_row * S::kRowBytes;
         if (ln == 0) {
@@ -531,7 +541,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   // fetch: 0 past the partition end or for an out-of-range id (nothing is
   // read then), else the block's tokens below n.
   auto block_src = [&](int t, int& rows) -> size_t {  // returns (block id) * Hkv + j
-    const int id = __builtin_amdgcn_readlane(my_id, min(t, 63));
+    const int id = block_id(min(t, 127));
     const bool ok = t < nblk && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
     rows = ok ? min(kBlockSize, n - (blk0 + t) * kBlockSize) : 0;
     if (kStep && t == new_t) rows = new_row;  // the new row comes from registers
@@ -668,7 +678,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   // are issued unconditionally (past the partition end they fetch nothing, see
   // load_block) so that every iteration issues the same loads and the compiler
   // can wait on a precise outstanding-load count.
-  constexpr int kAhead = sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT;
+  constexpr int kAhead = kFp8 ? PKV_AHEAD_FP8 : (sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT);
   constexpr int kRing = kAhead + 1;
   R ring[kRing];
   int ring_rows[kRing];
@@ -1008,7 +1018,7 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
   if (elt_bytes(dtype) == 0) return PKV_EINVAL;
   if (block_size != kBlockSize || (head_dim != 64 && head_dim != 128)) return PKV_EUNSUPPORTED;
-  if (partition_blocks < 0 || partition_blocks > 64) return PKV_EINVAL;
+  if (partition_blocks < 0 || partition_blocks > kMaxPartitionBlocks) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!context_lens || !out) return PKV_EINVAL;
   if ((phases & (kPartitions | kFusedStep)) && (!q || !k_cache || !v_cache || !block_tables)) return PKV_EINVAL;

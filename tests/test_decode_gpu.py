@@ -143,6 +143,22 @@ def test_shapes_and_edge_lengths(torch_dev, dtype, shape):
         full_parity(torch, dev, wk, pb, f"{dtype} {shape} pb={pb}")
 
 
+LONG_LENS = (1, 1023, 1024, 1025, 1040, 2047, 2048, 2049, 3001)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_partitions(torch_dev, dtype):
+    """Partitions of 65..128 blocks take their block ids from a second register."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("long", 0, 1, len(LONG_LENS), 16, 2, 128, 16, dtype, context_lens=LONG_LENS)
+    wk = wl.make_host_workload(cfg, seed=4242)
+    for pb in (65, 100, 128):
+        note(f"long partitions {dtype} partition_blocks={pb}: split path")
+        full_parity(torch, dev, wk, pb, f"long {dtype} pb={pb}")
+        note(f"long partitions {dtype} partition_blocks={pb}: fused step")
+        fused_parity(torch, dev, wk, pb, f"long fused {dtype} pb={pb}")
+
+
 def test_zero_length_rows_are_zero(torch_dev):
     torch, dev = torch_dev
     cfg = wl.DecodeConfig("zero", 0, 1, 3, 8, 2, 128, 16, "bf16", context_lens=(5, 40, 17))

@@ -107,7 +107,7 @@ def test_fp8_append_extreme_rows(torch_dev):
     assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 append, extreme rows")
 
 
-EDGE_LENS = (1, 2, 15, 16, 17, 33, 128, 129, 257, 600)
+EDGE_LENS = (1, 2, 15, 16, 17, 33, 128, 129, 257, 600, 1100, 2049)
 SHAPES = [(4, 2, 64), (32, 8, 128), (8, 8, 64), (64, 8, 128), (28, 4, 128), (64, 2, 128)]
 
 
@@ -119,7 +119,7 @@ def test_fp8_attention_and_fused_step(torch_dev, q_dtype, shape):
     cfg = wl.DecodeConfig("fp8", 0, 1, len(EDGE_LENS), Hq, Hkv, D, 16, q_dtype, context_lens=EDGE_LENS)
     wk = wl.make_host_workload_fp8(cfg, seed=3000 + Hq + Hkv + D)
     ref, kc, vc, ks, vs = oracle_fp8(wk)
-    for pb in (0, 1, 3, 64):
+    for pb in (0, 1, 3, 64, 128):
         note(f"fp8 {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: append + attention")
         d = to_dev(torch, dev, wk)
         slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)

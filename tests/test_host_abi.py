@@ -193,7 +193,7 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
     assert attn(bs=32) == pkv.PKV_EUNSUPPORTED
     assert attn(dt=3) == pkv.PKV_EINVAL
     assert attn(q=None) == pkv.PKV_EINVAL
-    assert attn(pb=65) == pkv.PKV_EINVAL
+    assert attn(pb=129) == pkv.PKV_EINVAL
     # a launch that needs a workspace but gets none (4 blocks in partitions of 1)
     assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4, 1) > 0
     assert attn(pb=1) == pkv.PKV_ESMALL
