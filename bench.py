@@ -111,6 +111,68 @@ def _run_cpu(samples, cfg, budget_s, oracle):
     return done, kv_bytes, t_total
 
 
+def run_copy_blocks(args):
+    """--op copy_blocks: copy-on-write block copies at the Llama-3-70B cache
+    shape (bf16, 8 KV heads, head_dim 128, 16-token blocks: 32 KiB per block
+    per tensor), K and V in one launch, `--copy-pairs` random (src, dst) pairs
+    per launch with distinct destinations."""
+    import torch
+    from paged_kv_cache_156_amd import binding as pkv
+
+    pkv.load()
+    dev = torch.device("cuda:0")
+    Hkv, D, bs, n = 8, 128, 16, args.copy_pairs
+    NB = 2 * n
+    g = torch.Generator(device=dev)
+    g.manual_seed(156)
+    kc = torch.randn((NB, Hkv, bs, D), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((NB, Hkv, bs, D), generator=g, device=dev).to(torch.bfloat16)
+    rng = np.random.default_rng(156)
+    pairs_h = np.stack([rng.permutation(n), n + rng.permutation(n)], 1).astype(np.int32)  # sources, then fresh blocks
+    pairs = torch.from_numpy(pairs_h).to(dev)
+    block_bytes = Hkv * bs * D * 2
+    bytes_launch = 2 * 2 * block_bytes * n  # K and V, read + write
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pkv.copy_blocks([kc, vc], pairs)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        pkv.copy_blocks([kc, vc], pairs)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    assert torch.equal(kc[pairs[:, 1].long()], kc[pairs[:, 0].long()])
+    gbs = bytes_launch / (ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        k_h = kc[: min(n, 4096)].view(torch.int16).cpu().numpy()  # 128 MiB: larger than the host caches
+        sample = [(i, i + len(k_h) // 2) for i in range(len(k_h) // 2)]
+        done, t_cpu = 0, 0.0
+        while t_cpu < min(args.cpu_budget, 5.0):
+            t = time.perf_counter()
+            oracle.copy_blocks(k_h, sample)
+            t_cpu += time.perf_counter() - t
+            done += len(sample)
+        cpu = {"value": round(2 * block_bytes * done / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} block copies of one 32 KiB tensor block (NumPy, one thread), {t_cpu:.1f}s"}
+    result = {
+        "metric": "copy-on-write block copy GB/s (bytes read + written)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (bit copy)", "data": "synthetic",
+        "config": {"workload": f"copy_blocks: {n} random block pairs, K and V caches of 8 KV heads x 16 tokens x "
+                               f"128 dims bf16 (32 KiB per block per tensor), one launch", "pairs": n},
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": bytes_launch, "avg_launch_us": round(ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +187,9 @@ def main():
                          "split: kv_append, decode_partitions, decode_merge")
     ap.add_argument("--kv", choices=("native", "fp8"), default="native",
                     help="native: K/V cached in the configuration's dtype; fp8: E4M3 codes + fp32 per-row scales")
+    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
+                    help="decode: the decode step (default); copy_blocks: copy-on-write block copies")
+    ap.add_argument("--copy-pairs", type=int, default=8192, help="block pairs per copy_blocks launch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -133,6 +198,10 @@ def main():
         print("bench.py: the decode path runs on one GPU; --gpus must be 1 (there is no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "copy_blocks":
+        run_copy_blocks(args)
+        return
 
     import torch
     from paged_kv_cache_156_amd import binding as pkv

@@ -257,6 +257,26 @@ pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_n
                                int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
                                size_t workspace_bytes, int32_t partition_blocks, void* stream);
 
+/*
+ * pkv_copy_blocks -- copy-on-write of whole physical blocks ("KV Cache and
+ * Inference Optimization", section "PagedAttention": shared blocks are copied
+ * when a sequence diverges). For each pair k (pairs[2k] = source id,
+ * pairs[2k+1] = destination id; DEVICE int32 array) and each of the n_caches
+ * tensors c, copies block_bytes[c] bytes from caches[c] + src * block_bytes[c]
+ * to caches[c] + dst * block_bytes[c]. `caches` and `block_bytes` are HOST
+ * arrays of n_caches (1..4) entries: e.g. K and V caches with
+ * Hkv * block_size * head_dim * elt bytes per block, plus for FP8 caches the
+ * two scale tensors with Hkv * block_size * 4 bytes per block. Pairs with an
+ * id outside [0, num_blocks) or src == dst are skipped. Precondition (what
+ * pkv_seq_append_slots produces): no destination appears twice or is also a
+ * source; otherwise the result depends on scheduling. Asynchronous on
+ * `stream`; run it before the append that writes the destinations.
+ * Errors: EINVAL (n_caches outside 1..4, a block_bytes not a positive
+ * multiple of 16, a null or unaligned pointer, n_pairs < 0), EHIP.
+ */
+pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int32_t n_caches, int32_t num_blocks,
+                           const int32_t* pairs, int32_t n_pairs, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block pool, block tables and slot mapping                            */
 /* ------------------------------------------------------------------------ */
@@ -271,7 +291,7 @@ typedef struct pkv_pool pkv_pool;
 
 typedef struct pkv_pool_stats {
   int64_t num_blocks;       /* pool size                                          */
-  int64_t free_blocks;      /* blocks on the free list                            */
+  int64_t free_blocks;      /* blocks no sequence holds (incl. evictable cached)  */
   int64_t used_blocks;      /* distinct blocks held by at least one sequence      */
   int64_t shared_blocks;    /* blocks held by more than one sequence              */
   int64_t live_seqs;        /* sequences with at least one token                  */
@@ -299,9 +319,80 @@ pkv_status pkv_seq_grow(pkv_pool* pool, int32_t seq, int32_t new_len);
  * exceeds src's length. */
 pkv_status pkv_seq_share_prefix(pkv_pool* pool, int32_t dst, int32_t src, int32_t n_tokens);
 
-/* Release all blocks of `seq` (a block returns to the free list when its
- * reference count reaches 0). EINVAL if `seq` holds nothing (double free). */
+/* Make empty sequence `dst` share ALL blocks of `src`, the partial last block
+ * included (reference counts + 1), and take src's length: parallel samples or
+ * beams that store their common prefix once and copy only where they branch
+ * ("KV Cache and Inference Optimization", the beam-search / multi-sample item
+ * of its list of pitfalls, and "PagedAttention": shared blocks, copied on
+ * divergence). The first append of either sequence into the shared
+ * partial block goes through pkv_seq_append_slots, which copies it.
+ * EINVAL if dst is not empty or dst == src. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int32_t dst, int32_t src);
+
+/* Release all blocks of `seq` (a block nobody holds any more returns to the
+ * free list, or, if it is in the prefix cache, becomes evictable).
+ * EINVAL if `seq` holds nothing (double free). */
 pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
+
+/* One decode step's append for sequences seqs[0..n) (distinct): each grows by
+ * one token at position = its current length, and slots[i] receives that
+ * token's slot. A position at a block boundary takes a fresh block; a
+ * position inside a block that other sequences also hold makes the block
+ * private first (copy-on-write, "KV Cache and Inference Optimization",
+ * "PagedAttention"): a fresh block replaces it in this sequence and the pair
+ * (shared id, fresh id) is written to copy_pairs[2k], copy_pairs[2k+1];
+ * *n_copies receives k. copy_pairs must hold 2n ints. The caller copies those
+ * blocks on the device (pkv_copy_blocks) before the append writes the slots.
+ * Errors (nothing is changed): EINVAL (bad or repeated sequence, null
+ * pointers), ENOMEM (fewer free blocks than needed), EBUSY (the target block
+ * is in the prefix cache: cannot happen through this API, since only full
+ * blocks are cached). */
+pkv_status pkv_seq_append_slots(pkv_pool* pool, const int32_t* seqs, int32_t n, int64_t* slots,
+                                int32_t* copy_pairs, int32_t* n_copies);
+
+/* ---- Prefix cache ("KV Cache and Inference Optimization", section "APC") ----
+ * Full blocks are cached under a key chained over the token prefix that ends
+ * with them (block i's key covers tokens [0, 16(i+1))) and the caller's
+ * namespace `ns` (e.g. a model / adapter identity: reused state must match the
+ * model and the exact token sequence and positions, "Why does a request use
+ * more memory the longer it generates?", section "Paging changes allocation,
+ * not a token's representation"). A lookup walks a request's full blocks from the first one
+ * and stops at the first miss; a hit is accepted only after comparing the
+ * block's tokens and its predecessor exactly, so a hash collision can only
+ * cause a miss. Partial blocks are never cached. */
+typedef struct pkv_prefix_stats {
+  int64_t cached_blocks;     /* blocks in the prefix cache                          */
+  int64_t evictable_blocks;  /* cached blocks no sequence holds                      */
+  int64_t lookups;           /* pkv_seq_adopt_prefix calls                           */
+  int64_t lookup_blocks;     /* full blocks those requests had                       */
+  int64_t hit_blocks;        /* of which reused from the cache                       */
+  int64_t evictions;         /* cached blocks reclaimed for new data                 */
+  int64_t cow_copies;        /* blocks copied by pkv_seq_append_slots                */
+} pkv_prefix_stats;
+
+/* Cache the full blocks of `seq` covering tokens[0..n_tokens) (the caller has
+ * written their K/V). Registration stops early where the same content is
+ * already cached in another block. *n_cached (may be NULL) receives how many
+ * leading blocks of `seq` are now in the cache. Errors: EINVAL (bad sequence,
+ * or a block of `seq` already cached with other tokens), ERANGE (n_tokens
+ * beyond the sequence's length), ENOMEM. */
+pkv_status pkv_prefix_register(pkv_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                               uint64_t ns, int32_t* n_cached);
+
+/* Leading cached blocks for tokens[0..n_tokens): *n_hit receives their count
+ * and block_ids (may be NULL) the first min(count, capacity) ids. Changes
+ * nothing. */
+pkv_status pkv_prefix_match(const pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                            int32_t* block_ids, int32_t capacity, int32_t* n_hit);
+
+/* Start empty sequence `seq` from the cache: it holds the leading hit blocks
+ * of tokens[0..n_tokens) (reference counts + 1) and its length becomes
+ * 16 x hits tokens, returned in *hit_tokens (may be NULL); the caller computes
+ * K/V only for the rest. EINVAL if `seq` is not empty. */
+pkv_status pkv_seq_adopt_prefix(pkv_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                                int32_t* hit_tokens);
+
+pkv_status pkv_pool_get_prefix_stats(const pkv_pool* pool, pkv_prefix_stats* out);
 
 /* Current length and block list of one sequence. `blocks` may be NULL to
  * query only the count; otherwise capacity must hold the count (ESMALL). */

@@ -5,9 +5,11 @@ path computes. Only the test suite, the smoke entry point and the benchmark's
 CPU-baseline leg may import this package; the library under
 ``paged_kv_cache_156_amd`` never does, and this package imports nothing from it.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against figures the
-pages print, closed forms, library routines (torch's fp64 SDPA on the CPU) or
-brute force. No function here is "parity unpinned".
+Every function is pinned (``tests/test_oracle_pins.py``,
+``tests/test_oracle_quant_pins.py``, ``tests/test_oracle_prefix_pins.py``)
+against figures the pages print, closed forms, library routines (torch's fp64
+SDPA and float8 type on the CPU) or brute force. No function here is "parity
+unpinned".
 """
 from .accounting import (  # noqa: F401
     kv_cache_bytes,
@@ -30,6 +32,12 @@ from .paged_decode import (  # noqa: F401
     gather_sequence_fp8,
     decode_attention_fp8,
     kv_append_fp8,
+)
+from .prefix import (  # noqa: F401
+    cached_full_blocks,
+    apc_hit_blocks,
+    copy_blocks,
+    LogicalSequences,
 )
 from .quant import (  # noqa: F401
     e4m3_value,

@@ -35,6 +35,14 @@ class PoolStats(ctypes.Structure):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
+class PrefixStats(ctypes.Structure):
+    _fields_ = [(n, _c.c_int64) for n in ("cached_blocks", "evictable_blocks", "lookups", "lookup_blocks",
+                                          "hit_blocks", "evictions", "cow_copies")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
 SIGNATURES = [
     ("pkv_status_string", _c.c_char_p, [_i32]),
     ("pkv_version", _i32, []),
@@ -54,11 +62,18 @@ SIGNATURES = [
                                               _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_decode_step_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_copy_blocks", _i32, [_c.POINTER(_vp), _pi64, _i32, _i32, _vp, _i32, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
     ("pkv_seq_grow", _i32, [_vp, _i32, _i32]),
     ("pkv_seq_share_prefix", _i32, [_vp, _i32, _i32, _i32]),
+    ("pkv_seq_fork", _i32, [_vp, _i32, _i32]),
     ("pkv_seq_free", _i32, [_vp, _i32]),
+    ("pkv_seq_append_slots", _i32, [_vp, _pi32, _i32, _pi64, _pi32, _pi32]),
+    ("pkv_prefix_register", _i32, [_vp, _i32, _pi32, _i32, _u64, _pi32]),
+    ("pkv_prefix_match", _i32, [_vp, _pi32, _i32, _u64, _pi32, _i32, _pi32]),
+    ("pkv_seq_adopt_prefix", _i32, [_vp, _i32, _pi32, _i32, _u64, _pi32]),
+    ("pkv_pool_get_prefix_stats", _i32, [_vp, _c.POINTER(PrefixStats)]),
     ("pkv_seq_info", _i32, [_vp, _i32, _pi32, _pi32, _pi32, _i32]),
     ("pkv_build_block_tables", _i32, [_vp, _pi32, _i32, _i32, _i32, _pi32]),
     ("pkv_build_slot_mapping", _i32, [_vp, _pi32, _pi32, _i32, _pi64]),
@@ -174,6 +189,46 @@ class BlockPool:
     def free(self, seq: int):
         _check(self._lib.pkv_seq_free(self._h, seq), "pkv_seq_free")
 
+    def fork(self, dst: int, src: int):
+        _check(self._lib.pkv_seq_fork(self._h, dst, src), "pkv_seq_fork")
+
+    def append_slots(self, seqs: Sequence[int]):
+        """Grow each sequence by one token; returns (slots int64 [n], copy pairs int32 [k, 2])."""
+        s = _np_i32(seqs)
+        slots = np.empty(len(s), np.int64)
+        pairs = np.empty(max(2 * len(s), 2), np.int32)
+        k = ctypes.c_int32()
+        _check(self._lib.pkv_seq_append_slots(self._h, _ptr32(s), len(s), slots.ctypes.data_as(_pi64), _ptr32(pairs),
+                                              ctypes.byref(k)), "pkv_seq_append_slots")
+        return slots, pairs[: 2 * k.value].reshape(k.value, 2).copy()
+
+    def prefix_register(self, seq: int, tokens: Sequence[int], ns: int = 0) -> int:
+        t = _np_i32(tokens)
+        k = ctypes.c_int32()
+        _check(self._lib.pkv_prefix_register(self._h, seq, _ptr32(t), len(t), ns, ctypes.byref(k)),
+               "pkv_prefix_register")
+        return k.value
+
+    def prefix_match(self, tokens: Sequence[int], ns: int = 0) -> np.ndarray:
+        t = _np_i32(tokens)
+        ids = np.zeros(max(len(t) // self.block_size, 1), np.int32)
+        k = ctypes.c_int32()
+        _check(self._lib.pkv_prefix_match(self._h, _ptr32(t), len(t), ns, _ptr32(ids), len(ids), ctypes.byref(k)),
+               "pkv_prefix_match")
+        return ids[: k.value].copy()
+
+    def adopt_prefix(self, seq: int, tokens: Sequence[int], ns: int = 0) -> int:
+        t = _np_i32(tokens)
+        k = ctypes.c_int32()
+        _check(self._lib.pkv_seq_adopt_prefix(self._h, seq, _ptr32(t), len(t), ns, ctypes.byref(k)),
+               "pkv_seq_adopt_prefix")
+        return k.value
+
+    def prefix_stats(self) -> dict:
+        st = PrefixStats()
+        _check(self._lib.pkv_pool_get_prefix_stats(self._h, ctypes.byref(st)), "pkv_pool_get_prefix_stats")
+        return st.as_dict()
+
     def seq_info(self, seq: int):
         length, nb = ctypes.c_int32(), ctypes.c_int32()
         _check(self._lib.pkv_seq_info(self._h, seq, ctypes.byref(length), ctypes.byref(nb), None, 0), "pkv_seq_info")
@@ -247,6 +302,29 @@ def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None):
                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
                               NB, Hkv, D, bs, code, _stream_ptr(stream))
     _check(st, "pkv_kv_append")
+
+
+def copy_blocks(caches, pairs, stream=None):
+    """Copy whole blocks ``pairs[k, 0] -> pairs[k, 1]`` in every tensor of
+    ``caches`` (1..4 device tensors whose first dim is the block id, e.g. the K
+    and V caches, plus the scale tensors of FP8 caches). ``pairs``: device int32
+    [n, 2] (or an empty tensor)."""
+    import torch
+    if not 1 <= len(caches) <= 4:
+        raise ValueError("copy_blocks takes 1..4 cache tensors")
+    nb = caches[0].shape[0]
+    ptrs = (ctypes.c_void_p * len(caches))()
+    sizes = (ctypes.c_int64 * len(caches))()
+    for i, c in enumerate(caches):
+        if c.shape[0] != nb:
+            raise ValueError("all caches must have the same number of blocks")
+        ptrs[i] = _dev(c, f"caches[{i}]")
+        sizes[i] = c[0].numel() * c.element_size()
+    n = pairs.shape[0]
+    if n and tuple(pairs.shape) != (n, 2):
+        raise ValueError("pairs must be [n, 2]")
+    pp = _dev(pairs, "pairs", torch.int32) if n else None
+    _check(load().pkv_copy_blocks(ptrs, sizes, len(caches), nb, pp, n, _stream_ptr(stream)), "pkv_copy_blocks")
 
 
 def decode_partition_blocks(num_seqs: int, num_heads: int, num_kv_heads: int, max_blocks: int) -> int:

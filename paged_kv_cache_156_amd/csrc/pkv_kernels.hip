@@ -873,6 +873,39 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int num_seqs) 
 }
 
 // ---------------------------------------------------------------------------
+// copy-on-write: whole blocks of up to four cache tensors, one workgroup per
+// (pair, tensor), 16 bytes per thread per step with four copies in flight
+// ---------------------------------------------------------------------------
+struct CopyArgs {
+  char* base[4];
+  int64_t bytes[4];  // per block, multiple of 16
+};
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, const int32_t* __restrict__ pairs,
+                                                          int32_t num_blocks) {
+  const int32_t src = pairs[2 * static_cast<int64_t>(blockIdx.x)];
+  const int32_t dst = pairs[2 * static_cast<int64_t>(blockIdx.x) + 1];
+  if (src == dst || static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks))
+    return;
+  const unsigned c = blockIdx.y;  // select, not index: keeps the arguments out of scratch
+  char* base = c == 0 ? a.base[0] : c == 1 ? a.base[1] : c == 2 ? a.base[2] : a.base[3];
+  const int64_t nb = c == 0 ? a.bytes[0] : c == 1 ? a.bytes[1] : c == 2 ? a.bytes[2] : a.bytes[3];
+  const u32x4* s = reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(src) * nb);
+  u32x4* d = reinterpret_cast<u32x4*>(base + static_cast<int64_t>(dst) * nb);
+  const int64_t chunks = nb / 16;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * 256 < chunks; i += 4 * 256) {
+    const u32x4 x0 = s[i], x1 = s[i + 256], x2 = s[i + 512], x3 = s[i + 768];
+    d[i] = x0;
+    d[i + 256] = x1;
+    d[i + 512] = x2;
+    d[i + 768] = x3;
+  }
+  for (; i < chunks; i += 256) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------
 // append: one thread per 16-byte chunk of a new token's head row
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k, const char* __restrict__ v,
@@ -1108,7 +1141,7 @@ const char* pkv_status_string(pkv_status s) {
   return "PKV_?: unknown status";
 }
 
-int32_t pkv_version(void) { return 100; }
+int32_t pkv_version(void) { return 110; }
 
 pkv_status pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                          void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
@@ -1182,6 +1215,24 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
                       partition_blocks, kFusedStep, stream, k_new, v_new);
+}
+
+pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int32_t n_caches, int32_t num_blocks,
+                           const int32_t* pairs, int32_t n_pairs, void* stream) {
+  if (n_caches < 1 || n_caches > 4 || num_blocks <= 0 || n_pairs < 0 || !caches || !block_bytes) return PKV_EINVAL;
+  CopyArgs a{};
+  for (int c = 0; c < n_caches; ++c) {
+    if (!caches[c] || reinterpret_cast<uintptr_t>(caches[c]) % 16 != 0) return PKV_EINVAL;
+    if (block_bytes[c] <= 0 || block_bytes[c] % 16 != 0) return PKV_EINVAL;
+    if (block_bytes[c] > INT64_MAX / num_blocks) return PKV_EINVAL;
+    a.base[c] = static_cast<char*>(caches[c]);
+    a.bytes[c] = block_bytes[c];
+  }
+  if (n_pairs == 0) return PKV_OK;
+  if (!pairs) return PKV_EINVAL;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs, n_caches), dim3(256), 0, static_cast<hipStream_t>(stream), a,
+                     pairs, num_blocks);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
 pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,

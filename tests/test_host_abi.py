@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     lib = pkv.load()
     for code in range(8):
         assert lib.pkv_status_string(code).decode().startswith(pkv.STATUS_NAMES[code])
-    assert lib.pkv_version() == 100
+    assert lib.pkv_version() == 110
 
 
 def test_block_accounting_matches_oracle():
