@@ -15,6 +15,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--config NAME] [--layers L]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -187,6 +188,9 @@ def main():
                          "split: kv_append, decode_partitions, decode_merge")
     ap.add_argument("--kv", choices=("native", "fp8"), default="native",
                     help="native: K/V cached in the configuration's dtype; fp8: E4M3 codes + fp32 per-row scales")
+    ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
+                    help="cache block layout: HND [NB, Hkv, bs, D] (default) or NHD [NB, bs, Hkv, D]")
+    ap.add_argument("--block-size", type=int, default=0, help="tokens per cache block (0 = the configuration's, 16)")
     ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
                     help="decode: the decode step (default); copy_blocks: copy-on-write block copies")
     ap.add_argument("--copy-pairs", type=int, default=8192, help="block pairs per copy_blocks launch")
@@ -210,6 +214,9 @@ def main():
     pkv.load()
     dev = torch.device("cuda:0")
     cfg = wl.CONFIG_BY_NAME[args.config]
+    if args.block_size:
+        cfg = dataclasses.replace(cfg, block_size=args.block_size)
+    lay = args.layout
     L = args.layers or cfg.num_layers
     _, _, r_len = wl.streams(cfg.seed)
     lens = wl.draw_context_lens(cfg, r_len)
@@ -226,6 +233,16 @@ def main():
     else:
         wkd = wl.make_device_workload(cfg, dev, layers=L, context_lens=lens, assignment=asg,
                                       progress=lambda l: (l % 20 == 0) and log(f"  drew layer {l}/{L}"))
+    if lay == "NHD":  # token-major copies of the same caches, one layer at a time
+        for l in range(L):
+            if fp8:
+                wkd.k_codes[l] = wkd.k_codes[l].transpose(1, 2).contiguous()
+                wkd.v_codes[l] = wkd.v_codes[l].transpose(1, 2).contiguous()
+                wkd.k_scales[l] = wkd.k_scales[l].transpose(1, 2).contiguous()
+                wkd.v_scales[l] = wkd.v_scales[l].transpose(1, 2).contiguous()
+            else:
+                wkd.k_cache[l] = wkd.k_cache[l].transpose(1, 2).contiguous()
+                wkd.v_cache[l] = wkd.v_cache[l].transpose(1, 2).contiguous()
     torch.cuda.synchronize()
     log(f"device workload ready in {time.time() - t0:.1f}s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
@@ -233,13 +250,13 @@ def main():
     samples = cpu_samples(wkd) if (args.cpu_budget > 0 and not fp8) else []
 
     max_blocks = wkd.block_tables.shape[1]
-    pb = args.partition_blocks or pkv.decode_partition_blocks(B, Hq, Hkv, max_blocks)
+    pb = args.partition_blocks or pkv.decode_partition_blocks(B, Hq, Hkv, max_blocks, bs)
     fused = args.mode == "fused"
     kcache0 = wkd.k_codes[0] if fp8 else wkd.k_cache[0]
     if fused:
-        ws = pkv.alloc_step_workspace(wkd.q[0], kcache0, wkd.block_tables, pb)
+        ws = pkv.alloc_step_workspace(wkd.q[0], kcache0, wkd.block_tables, pb, layout=lay)
     else:
-        ws = pkv.alloc_workspace(wkd.q[0], kcache0, wkd.block_tables, pb)
+        ws = pkv.alloc_workspace(wkd.q[0], kcache0, wkd.block_tables, pb, layout=lay)
     slots_d = torch.from_numpy(slots).to(dev)
     outs = [torch.empty_like(wkd.q[l]) for l in range(L)]
     stream = torch.cuda.current_stream()
@@ -252,13 +269,13 @@ def main():
                 if fused:
                     pkv.decode_step_fp8(wkd.q[l], wkd.k_new[l], wkd.v_new[l], wkd.k_codes[l], wkd.v_codes[l],
                                         wkd.k_scales[l], wkd.v_scales[l], wkd.block_tables, wkd.context_lens_dev,
-                                        cfg.scale, outs[l], ws, pb)
+                                        cfg.scale, outs[l], ws, pb, layout=lay)
                 else:
                     pkv.kv_append_fp8(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_codes[l], wkd.v_codes[l],
-                                      wkd.k_scales[l], wkd.v_scales[l])
+                                      wkd.k_scales[l], wkd.v_scales[l], layout=lay)
                     pkv.paged_decode_attention_fp8(wkd.q[l], wkd.k_codes[l], wkd.v_codes[l], wkd.k_scales[l],
                                                    wkd.v_scales[l], wkd.block_tables, wkd.context_lens_dev,
-                                                   cfg.scale, outs[l], ws, pb)
+                                                   cfg.scale, outs[l], ws, pb, layout=lay)
                 if events is not None:
                     events[l][1].record(stream)
                 continue
@@ -266,19 +283,19 @@ def main():
                 if events is not None:
                     events[l][0].record(stream)
                 pkv.decode_step(wkd.q[l], wkd.k_new[l], wkd.v_new[l], wkd.k_cache[l], wkd.v_cache[l],
-                                wkd.block_tables, wkd.context_lens_dev, cfg.scale, outs[l], ws, pb)
+                                wkd.block_tables, wkd.context_lens_dev, cfg.scale, outs[l], ws, pb, layout=lay)
                 if events is not None:
                     events[l][1].record(stream)
                 continue
-            pkv.kv_append(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_cache[l], wkd.v_cache[l])
+            pkv.kv_append(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_cache[l], wkd.v_cache[l], layout=lay)
             if events is not None:
                 events[l][0].record(stream)
             pkv.decode_partitions(wkd.q[l], wkd.k_cache[l], wkd.v_cache[l], wkd.block_tables, wkd.context_lens_dev,
-                                  cfg.scale, outs[l], ws, pb)
+                                  cfg.scale, outs[l], ws, pb, layout=lay)
             if events is not None:
                 events[l][1].record(stream)
             pkv.decode_merge(wkd.q[l], wkd.k_cache[l], wkd.v_cache[l], wkd.block_tables, wkd.context_lens_dev,
-                             outs[l], ws, pb)
+                             outs[l], ws, pb, layout=lay)
 
     log(f"warmup {args.warmup} steps (partition_blocks={pb}, workspace {0 if ws is None else ws.numel()} B)")
     for _ in range(args.warmup):
@@ -324,7 +341,8 @@ def main():
     achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
 
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}{'_fp8' if fp8 else ''}_{cfg.name}_traffic.json")
+    geom = "" if (lay == "HND" and bs == 16) else f"_{lay.lower()}_bs{bs}"
+    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}{'_fp8' if fp8 else ''}{geom}_{cfg.name}_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
@@ -366,10 +384,10 @@ def main():
         "dtype": (f"e4m3 K/V + f32 row scales, {cfg.dtype} q/out" if fp8 else cfg.dtype),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: batch {B}, context {'ragged' if cfg.context_len_range else int(lens[0])}, "
-                               f"{Hq} query / {Hkv} KV heads, head_dim {D}, block 16, {L} layers, one decode step "
+                               f"{Hq} query / {Hkv} KV heads, head_dim {D}, {lay} blocks of {bs}, {L} layers, one decode step "
                                f"(append + attention) per layer",
                    "global_batch": B, "seq_len": int(lens.max()), "layers": L, "partition_blocks": pb,
-                   "mode": args.mode, "kv": args.kv},
+                   "mode": args.mode, "kv": args.kv, "layout": lay, "block_size": bs},
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(B / (ms_per_step * 1e-3), 2),
         "kv_bytes_per_step": step_kv,

@@ -60,10 +60,22 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
 
+/*
+ * Cache block layouts ("Understanding KV Cache" §3.2). One layer's K (and,
+ * separately, V) cache of num_blocks blocks of block_size tokens:
+ *   PKV_HND  [num_blocks, num_kv_heads, block_size, head_dim] (head-major:
+ *            one head's tokens of a block are contiguous)
+ *   PKV_NHD  [num_blocks, block_size, num_kv_heads, head_dim] (token-major)
+ * FP8 scale tensors follow the same order without the head_dim axis.
+ * Attention calls take block sizes that are multiples of 16 up to 2048
+ * (the kernels walk 16-token tiles); the append takes any block size.
+ */
+typedef enum pkv_layout { PKV_HND = 0, PKV_NHD = 1 } pkv_layout;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pkv_status_string(pkv_status s);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 200. */
 int32_t pkv_version(void);
 
 /* ------------------------------------------------------------------------ */
@@ -76,7 +88,8 @@ int32_t pkv_version(void);
  * The cache is an append-only log ("Understanding KV Cache" §1.3); token i's
  * slot s = slot_mapping[i] is offset s % block_size of physical block
  * s / block_size (§3.3). For every KV head j:
- *   k_cache[s / bs, j, s % bs, :] = k[i, j, :]   (likewise v)
+ *   k_cache[s / bs, j, s % bs, :] = k[i, j, :]   (HND; likewise v)
+ *   k_cache[s / bs, s % bs, j, :] = k[i, j, :]   (NHD)
  * The copy is bit-exact. slot_mapping[i] < 0 marks a padding token: skipped.
  *
  *   k, v          device, [num_tokens, num_kv_heads, head_dim]
@@ -92,16 +105,18 @@ int32_t pkv_version(void);
  */
 pkv_status pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                          void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t block_size, pkv_dtype dtype, void* stream);
+                         int32_t head_dim, int32_t block_size, pkv_layout layout, pkv_dtype dtype, void* stream);
 
 /*
- * pkv_decode_partition_blocks -- blocks per context partition the library
- * picks for a launch of this shape (the split-context work unit). Each
- * partition covers this many 16-token blocks of one sequence and one KV head;
- * partial results are merged exactly with a log-sum-exp combine.
+ * pkv_decode_partition_blocks -- cache blocks per context partition the
+ * library picks for a launch of this shape (the split-context work unit).
+ * Each partition covers this many blocks of one sequence and one KV head;
+ * partial results are merged exactly with a log-sum-exp combine. Returns 0
+ * for an unsupported block_size. A partition may span at most 2048 tokens
+ * (partition_blocks * block_size <= 2048) in every call below.
  */
 int32_t pkv_decode_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                    int32_t max_blocks_per_seq);
+                                    int32_t max_blocks_per_seq, int32_t block_size);
 
 /*
  * pkv_decode_workspace_bytes -- device scratch that pkv_paged_decode_attention
@@ -111,14 +126,15 @@ int32_t pkv_decode_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t
  * sequence fits one partition (no merge needed).
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_blocks);
+                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                  int32_t partition_blocks);
 
 /*
  * pkv_paged_decode_attention -- one decode step of attention over the paged
  * cache, for all sequences and query heads.
  *
  *   q             device [num_seqs, num_heads, head_dim]
- *   k_cache, v_cache  device [num_blocks, num_kv_heads, block_size, head_dim]
+ *   k_cache, v_cache  device, in `layout` (see pkv_layout)
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]: entry [b][i]
  *                 is the physical block of logical block i of sequence b;
  *                 entries past ceil(context_lens[b] / block_size) are never
@@ -130,7 +146,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t n
  *                 rounded from fp32 to the output type to nearest-even
  *   workspace     device scratch of >= pkv_decode_workspace_bytes(...) bytes
  *                 (may be NULL when that is 0); contents on entry ignored
- *   partition_blocks  blocks per partition (1..128), 0 = the library's choice
+ *   partition_blocks  blocks per partition (partition_blocks * block_size
+ *                 <= 2048), 0 = the library's choice
  *
  * Accumulation is fp32. Preconditions the device does not check at full
  * cost: context_lens[b] <= max_blocks_per_seq * block_size and table entries
@@ -138,16 +155,18 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t n
  * skips out-of-range block ids instead of reading outside the pool, so a bad
  * table gives a wrong result, never a fault (pkv_validate_tables checks them
  * on the host).
- * Errors: EINVAL (null/shape/dtype/Hq % Hkv), EUNSUPPORTED (head_dim,
- * block_size), ESMALL (workspace), EHIP. num_seqs == 0 is a no-op.
+ * Errors: EINVAL (null/shape/dtype/Hq % Hkv, layout, partition size),
+ * EUNSUPPORTED (head_dim not 64/128, block_size not a multiple of 16 up to
+ * 2048, num_blocks * num_kv_heads * block_size >= 2^31), ESMALL (workspace),
+ * EHIP. num_seqs == 0 is a no-op.
  */
 pkv_status pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                      int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
-                                      void* workspace, size_t workspace_bytes, int32_t partition_blocks,
-                                      void* stream);
+                                      pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                                      pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      int32_t partition_blocks, void* stream);
 
 /*
  * The two phases of pkv_paged_decode_attention, for callers that schedule or
@@ -171,9 +190,9 @@ pkv_status pkv_paged_decode_attention(const void* q, const void* k_cache, const 
 pkv_status pkv_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                 float scale, void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
-                                 int32_t partition_blocks, void* stream);
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                                 int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t partition_blocks, void* stream);
 pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_blocks, void* out,
@@ -203,12 +222,14 @@ pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const
  * this; here it is a precondition).
  */
 size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_blocks);
+                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_blocks);
 pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t block_size, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
-                           void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
+                           int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                           pkv_dtype dtype, void* workspace, size_t workspace_bytes, int32_t partition_blocks,
+                           void* stream);
 
 /*
  * FP8 KV cache. The pages name low-precision KV storage (INT8/FP8) with
@@ -216,9 +237,11 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
  * "KV quantization") without fixing a format; these calls use:
  *   - codes: OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias 7, 3
  *     mantissa bits; no infinities; S.1111.111 is NaN; largest value 448),
- *     caches [num_blocks, num_kv_heads, block_size, head_dim] of uint8;
+ *     caches [num_blocks, num_kv_heads, block_size, head_dim] of uint8 (HND;
+ *     [num_blocks, block_size, num_kv_heads, head_dim] for NHD);
  *   - scales: one fp32 per token row of one KV head, arrays
- *     [num_blocks, num_kv_heads, block_size];
+ *     [num_blocks, num_kv_heads, block_size] (NHD: [num_blocks, block_size,
+ *     num_kv_heads]);
  *   - value attended over = code * scale;
  *   - quantization of a new row x (head_dim values, computed in fp32):
  *     amax = max |x|, scale = amax / 448, inv = 448 / amax (1 and 1 when
@@ -240,22 +263,22 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
  */
 pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                              void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
-                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_dtype dtype,
-                             void* stream);
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                             pkv_dtype dtype, void* stream);
 pkv_status pkv_paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
                                           const float* k_scales, const float* v_scales,
                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                          int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
-                                          void* workspace, size_t workspace_bytes, int32_t partition_blocks,
-                                          void* stream);
+                                          pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                                          pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          int32_t partition_blocks, void* stream);
 pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                float* k_scales, float* v_scales, const int32_t* block_tables,
                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
-                               size_t workspace_bytes, int32_t partition_blocks, void* stream);
+                               pkv_layout layout, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                               void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
 
 /*
  * pkv_copy_blocks -- copy-on-write of whole physical blocks ("KV Cache and

@@ -6,8 +6,10 @@ contiguous arrays, then run dense softmax attention for the single new query.
 
 Storage conventions shared with the inputs (not with the GPU code):
   * caches are raw arrays of shape [num_blocks, num_kv_heads, block_size,
-    head_dim] (HND), element type float32 ("f32"), float16 ("f16") or uint16
-    holding bfloat16 bits ("bf16");
+    head_dim] (layout "HND") or [num_blocks, block_size, num_kv_heads,
+    head_dim] (layout "NHD"), the two block layouts of §3.2 of the page
+    "Understanding KV Cache"; element type float32 ("f32"), float16 ("f16") or
+    uint16 holding bfloat16 bits ("bf16");
   * q is [num_seqs, num_heads, head_dim], k/v of the new token are
     [num_seqs, num_kv_heads, head_dim], in the same raw storage;
   * context_lens[b] counts the tokens attended by sequence b, the newest one
@@ -57,8 +59,17 @@ def slot_mapping(block_tables: np.ndarray, positions: Sequence[int], block_size:
     return out
 
 
+def _at(cache: np.ndarray, pb: int, off: int, kv_head: int, layout: str):
+    """Index of token `off` of block `pb`, KV head `kv_head` (the trailing axes stay)."""
+    if layout == "HND":
+        return cache[pb, kv_head, off]
+    if layout == "NHD":
+        return cache[pb, off, kv_head]
+    raise ValueError(f"unknown layout {layout!r}")
+
+
 def gather_sequence(cache: np.ndarray, dtype: str, table_row: Sequence[int], n: int,
-                    kv_head: int, block_size: int) -> np.ndarray:
+                    kv_head: int, block_size: int, layout: str = "HND") -> np.ndarray:
     """Contiguous float64 [n, head_dim] copy of one KV head of one sequence.
 
     The attention kernel collects K/V from the physical blocks the block table
@@ -70,7 +81,7 @@ def gather_sequence(cache: np.ndarray, dtype: str, table_row: Sequence[int], n: 
     out = np.empty((n, head_dim), dtype=np.float64)
     for i in range(n):
         _, off, pb, _ = slot_address(i, table_row, block_size)
-        out[i] = upcast(cache[pb, kv_head, off], dtype)
+        out[i] = upcast(_at(cache, pb, off, kv_head, layout), dtype)
     return out
 
 
@@ -106,7 +117,7 @@ def _attend_heads(qf: np.ndarray, gather_k, gather_v, num_kv_heads: int, n: int,
 
 def decode_attention_seq(q_b: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                          table_row: Sequence[int], n: int, scale: float, num_kv_heads: int,
-                         block_size: int, dtype: str) -> np.ndarray:
+                         block_size: int, dtype: str, layout: str = "HND") -> np.ndarray:
     """Output [num_heads, head_dim] (float64) of one sequence's decode step.
 
     Query head h reads KV head h // (num_heads / num_kv_heads): consecutive
@@ -116,27 +127,27 @@ def decode_attention_seq(q_b: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarr
     and §2.2 of the page "Understanding KV Cache"). n = 0 yields zeros.
     """
     return _attend_heads(upcast(q_b, dtype),
-                         lambda j: gather_sequence(k_cache, dtype, table_row, n, j, block_size),
-                         lambda j: gather_sequence(v_cache, dtype, table_row, n, j, block_size),
+                         lambda j: gather_sequence(k_cache, dtype, table_row, n, j, block_size, layout),
+                         lambda j: gather_sequence(v_cache, dtype, table_row, n, j, block_size, layout),
                          num_kv_heads, n, scale)
 
 
 def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                      block_tables: np.ndarray, context_lens: Sequence[int], scale: float,
                      num_kv_heads: int, block_size: int, dtype: str,
-                     seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+                     seqs: Optional[Sequence[int]] = None, layout: str = "HND") -> np.ndarray:
     """Output [num_seqs, num_heads, head_dim] float64. With ``seqs`` only
     those sequences are computed and the other rows are NaN."""
     B, Hq, D = q.shape
     out = np.full((B, Hq, D), np.nan, dtype=np.float64)
     for b in (range(B) if seqs is None else seqs):
         out[b] = decode_attention_seq(q[b], k_cache, v_cache, block_tables[b], int(context_lens[b]),
-                                      scale, num_kv_heads, block_size, dtype)
+                                      scale, num_kv_heads, block_size, dtype, layout)
     return out
 
 
 def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
-              slots: Sequence[int], block_size: int) -> None:
+              slots: Sequence[int], block_size: int, layout: str = "HND") -> None:
     """Write each new token's K and V (all KV heads) into its slot, in place.
 
     The cache is an append-only log: each generated token adds one K/V record
@@ -149,28 +160,30 @@ def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new
         if s < 0:
             continue
         pb, off = s // block_size, s % block_size
-        k_cache[pb, :, off, :] = k_new[i]
-        v_cache[pb, :, off, :] = v_new[i]
+        for j in range(k_new.shape[1]):
+            _at(k_cache, pb, off, j, layout)[...] = k_new[i, j]
+            _at(v_cache, pb, off, j, layout)[...] = v_new[i, j]
 
 
 # ---------------------------------------------------------------------------
 # FP8 (E4M3) caches: codes uint8 [NB, Hkv, bs, D], scales float32 [NB, Hkv, bs]
+# (NHD: [NB, bs, Hkv, D] and [NB, bs, Hkv])
 # ---------------------------------------------------------------------------
 def gather_sequence_fp8(codes: np.ndarray, scales: np.ndarray, table_row: Sequence[int], n: int, kv_head: int,
-                        block_size: int) -> np.ndarray:
+                        block_size: int, layout: str = "HND") -> np.ndarray:
     """Contiguous float64 [n, D] of decode(code) * scale for one KV head."""
     from .quant import e4m3_decode
     out = np.empty((n, codes.shape[-1]), dtype=np.float64)
     for i in range(n):
         _, off, pb, _ = slot_address(i, table_row, block_size)
-        out[i] = e4m3_decode(codes[pb, kv_head, off]) * np.float64(scales[pb, kv_head, off])
+        out[i] = e4m3_decode(_at(codes, pb, off, kv_head, layout)) * np.float64(_at(scales, pb, off, kv_head, layout))
     return out
 
 
 def decode_attention_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray,
                          v_scales: np.ndarray, block_tables: np.ndarray, context_lens: Sequence[int], scale: float,
                          num_kv_heads: int, block_size: int, q_dtype: str,
-                         seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+                         seqs: Optional[Sequence[int]] = None, layout: str = "HND") -> np.ndarray:
     """Decode attention over FP8 caches: the same softmax attention, over the
     dequantized cached values."""
     B, Hq, D = q.shape
@@ -179,14 +192,15 @@ def decode_attention_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray
         n = int(context_lens[b])
         row = block_tables[b]
         out[b] = _attend_heads(upcast(q[b], q_dtype),
-                               lambda j: gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size),
-                               lambda j: gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size),
+                               lambda j: gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size, layout),
+                               lambda j: gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size, layout),
                                num_kv_heads, n, scale)
     return out
 
 
 def kv_append_fp8(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray, v_scales: np.ndarray,
-                  k_new: np.ndarray, v_new: np.ndarray, slots: Sequence[int], block_size: int, in_dtype: str) -> None:
+                  k_new: np.ndarray, v_new: np.ndarray, slots: Sequence[int], block_size: int, in_dtype: str,
+                  layout: str = "HND") -> None:
     """Quantize each new token's K and V rows (one scale per KV head row, see
     ``oracle.quant``) and write codes and scales into the slot, in place."""
     from .quant import quantize_rows
@@ -197,7 +211,12 @@ def kv_append_fp8(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray
         if s < 0:
             continue
         pb, off = s // block_size, s % block_size
-        k_codes[pb, :, off, :] = kq[i]
-        v_codes[pb, :, off, :] = vq[i]
-        k_scales[pb, :, off] = ks[i]
-        v_scales[pb, :, off] = vs[i]
+        for j in range(k_new.shape[1]):
+            _at(k_codes, pb, off, j, layout)[...] = kq[i, j]
+            _at(v_codes, pb, off, j, layout)[...] = vq[i, j]
+            if layout == "HND":
+                k_scales[pb, j, off] = ks[i, j]
+                v_scales[pb, j, off] = vs[i, j]
+            else:
+                k_scales[pb, off, j] = ks[i, j]
+                v_scales[pb, off, j] = vs[i, j]

@@ -46,22 +46,22 @@ class PrefixStats(ctypes.Structure):
 SIGNATURES = [
     ("pkv_status_string", _c.c_char_p, [_i32]),
     ("pkv_version", _i32, []),
-    ("pkv_kv_append", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
-    ("pkv_decode_partition_blocks", _i32, [_i32, _i32, _i32, _i32]),
-    ("pkv_decode_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    ("pkv_paged_decode_attention", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+    ("pkv_kv_append", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    ("pkv_decode_partition_blocks", _i32, [_i32, _i32, _i32, _i32, _i32]),
+    ("pkv_decode_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    ("pkv_paged_decode_attention", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
-    ("pkv_decode_partitions", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+    ("pkv_decode_partitions", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_decode_merge", _i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
-    ("pkv_decode_step_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    ("pkv_decode_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+    ("pkv_decode_step_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    ("pkv_decode_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
-    ("pkv_kv_append_fp8", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    ("pkv_kv_append_fp8", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     ("pkv_paged_decode_attention_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
-                                              _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+                                              _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_decode_step_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
-                                   _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+                                   _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_copy_blocks", _i32, [_c.POINTER(_vp), _pi64, _i32, _i32, _vp, _i32, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
@@ -287,12 +287,26 @@ def _stream_ptr(stream):
     return s.cuda_stream
 
 
-def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None):
-    """k, v: [T, Hkv, D]; slot_mapping int64 [T]; caches [NB, Hkv, bs, D]."""
+LAYOUT_CODES = {"HND": 0, "NHD": 1}
+
+
+def _geom(cache, layout: str):
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a 4-D cache tensor in
+    ``layout``: "HND" = [NB, Hkv, bs, D], "NHD" = [NB, bs, Hkv, D]."""
+    if layout not in LAYOUT_CODES:
+        raise ValueError(f"layout must be 'HND' or 'NHD', got {layout!r}")
+    if cache.dim() != 4:
+        raise ValueError("caches are 4-D")
+    NB, a, b, D = cache.shape
+    return (NB, a, b, D) if layout == "HND" else (NB, b, a, D)
+
+
+def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None, layout: str = "HND"):
+    """k, v: [T, Hkv, D]; slot_mapping int64 [T]; caches in ``layout``."""
     import torch
     code = _torch_dtype_code(k_cache)
     T, Hkv, D = k.shape
-    NB, Hkv2, bs, D2 = k_cache.shape
+    NB, Hkv2, bs, D2 = _geom(k_cache, layout)
     if (Hkv, D) != (Hkv2, D2) or tuple(v.shape) != tuple(k.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("shape mismatch between k/v and the caches")
     if tuple(slot_mapping.shape) != (T,):
@@ -300,7 +314,7 @@ def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None):
     st = load().pkv_kv_append(_dev(k, "k", k_cache.dtype), _dev(v, "v", k_cache.dtype),
                               _dev(slot_mapping, "slot_mapping", torch.int64), T,
                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
-                              NB, Hkv, D, bs, code, _stream_ptr(stream))
+                              NB, Hkv, D, bs, LAYOUT_CODES[layout], code, _stream_ptr(stream))
     _check(st, "pkv_kv_append")
 
 
@@ -327,27 +341,30 @@ def copy_blocks(caches, pairs, stream=None):
     _check(load().pkv_copy_blocks(ptrs, sizes, len(caches), nb, pp, n, _stream_ptr(stream)), "pkv_copy_blocks")
 
 
-def decode_partition_blocks(num_seqs: int, num_heads: int, num_kv_heads: int, max_blocks: int) -> int:
-    return int(load().pkv_decode_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks))
+def decode_partition_blocks(num_seqs: int, num_heads: int, num_kv_heads: int, max_blocks: int,
+                            block_size: int = 16) -> int:
+    return int(load().pkv_decode_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks, block_size))
 
 
-def decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, partition_blocks=0) -> int:
-    return int(load().pkv_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks,
+def decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, partition_blocks=0,
+                           block_size=16) -> int:
+    return int(load().pkv_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, block_size,
                                                  partition_blocks))
 
 
-def alloc_workspace(q, k_cache, block_tables, partition_blocks=0):
+def alloc_workspace(q, k_cache, block_tables, partition_blocks=0, layout: str = "HND"):
     """Device scratch for ``paged_decode_attention`` (a torch uint8 tensor, or None)."""
     import torch
     B, Hq, D = q.shape
-    nbytes = decode_workspace_bytes(B, Hq, k_cache.shape[1], D, block_tables.shape[1], partition_blocks)
+    _, Hkv, bs, _ = _geom(k_cache, layout)
+    nbytes = decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], partition_blocks, bs)
     return torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
 
 
-def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace):
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, layout):
     import torch
     B, Hq, D = q.shape
-    NB, Hkv, bs, D2 = k_cache.shape
+    NB, Hkv, bs, D2 = _geom(k_cache, layout)
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
         raise ValueError("shape mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
@@ -357,132 +374,138 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace
     return dict(q=_dev(q, "q"), k=_dev(k_cache, "k_cache", q.dtype), v=_dev(v_cache, "v_cache", q.dtype),
                 t=_dev(block_tables, "block_tables", torch.int32), mb=block_tables.shape[1],
                 lens=_dev(context_lens, "context_lens", torch.int32), B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB,
-                out=_dev(out, "out", q.dtype), code=_torch_dtype_code(q), ws=ws_ptr, wsb=ws_bytes)
+                lay=LAYOUT_CODES[layout], out=_dev(out, "out", q.dtype), code=_torch_dtype_code(q), ws=ws_ptr,
+                wsb=ws_bytes)
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
-                           workspace=None, partition_blocks: int = 0, stream=None):
-    """q, out: [B, Hq, D]; caches [NB, Hkv, bs, D]; block_tables int32 [B, maxNB];
+                           workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
+    """q, out: [B, Hq, D]; caches in ``layout``; block_tables int32 [B, maxNB];
     context_lens int32 [B]; workspace: uint8 device tensor or None."""
-    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, layout)
     st = load().pkv_paged_decode_attention(a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"], a["B"], a["Hq"],
-                                           a["Hkv"], a["D"], a["bs"], a["NB"], float(scale), a["out"], a["code"],
-                                           a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+                                           a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale), a["out"],
+                                           a["code"], a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
     _check(st, "pkv_paged_decode_attention")
     return out
 
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
-                      workspace=None, partition_blocks: int = 0, stream=None):
+                      workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
     """First phase of ``paged_decode_attention`` (see pkv_decode_partitions)."""
-    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, layout)
     st = load().pkv_decode_partitions(a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"], a["B"], a["Hq"],
-                                      a["Hkv"], a["D"], a["bs"], a["NB"], float(scale), a["out"], a["code"],
-                                      a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+                                      a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale), a["out"],
+                                      a["code"], a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
     _check(st, "pkv_decode_partitions")
 
 
 def decode_merge(q, k_cache, v_cache, block_tables, context_lens, out, workspace=None, partition_blocks: int = 0,
-                 stream=None):
+                 stream=None, layout: str = "HND"):
     """Second phase: log-sum-exp merge of the partition results into ``out``."""
-    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, layout)
     st = load().pkv_decode_merge(a["ws"], a["wsb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["mb"], a["bs"],
                                  int(partition_blocks), a["out"], a["code"], _stream_ptr(stream))
     _check(st, "pkv_decode_merge")
 
 
-def decode_step_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, partition_blocks=0) -> int:
+def decode_step_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, partition_blocks=0,
+                                block_size=16) -> int:
     return int(load().pkv_decode_step_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks,
-                                                      partition_blocks))
+                                                      block_size, partition_blocks))
 
 
-def alloc_step_workspace(q, k_cache, block_tables, partition_blocks=0):
+def alloc_step_workspace(q, k_cache, block_tables, partition_blocks=0, layout: str = "HND"):
     """Zero-filled device workspace for ``decode_step`` (or None if not needed)."""
     import torch
     B, Hq, D = q.shape
-    nbytes = decode_step_workspace_bytes(B, Hq, k_cache.shape[1], D, block_tables.shape[1], partition_blocks)
+    _, Hkv, bs, _ = _geom(k_cache, layout)
+    nbytes = decode_step_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], partition_blocks, bs)
     return torch.zeros(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
 
 
 def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float, out,
-                workspace=None, partition_blocks: int = 0, stream=None):
+                workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
     """Fused append of each sequence's newest token (position context_lens-1)
     and paged decode attention, one launch (see pkv_decode_step)."""
-    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, layout)
     B, Hkv, D = a["B"], a["Hkv"], a["D"]
     if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
         raise ValueError("k_new / v_new must be [B, Hkv, D]")
     st = load().pkv_decode_step(a["q"], _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype), a["k"], a["v"],
-                                a["t"], a["mb"], a["lens"], B, a["Hq"], Hkv, D, a["bs"], a["NB"], float(scale),
-                                a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+                                a["t"], a["mb"], a["lens"], B, a["Hq"], Hkv, D, a["bs"], a["lay"], a["NB"],
+                                float(scale), a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
+                                _stream_ptr(stream))
     _check(st, "pkv_decode_step")
     return out
 
 
 # ---------------------------------------------------------------------------
-# FP8 (E4M3) caches: uint8 codes [NB, Hkv, bs, D] + fp32 scales [NB, Hkv, bs]
+# FP8 (E4M3) caches: uint8 codes in ``layout`` + fp32 scales without the D axis
 # ---------------------------------------------------------------------------
 def _fp8_cache(codes, scales, name):
     import torch
     if codes.dtype != torch.uint8 or codes.dim() != 4:
-        raise TypeError(f"{name} codes must be a uint8 [NB, Hkv, bs, D] tensor")
+        raise TypeError(f"{name} codes must be a uint8 4-D tensor")
     if tuple(scales.shape) != tuple(codes.shape[:3]) or scales.dtype != torch.float32:
-        raise ValueError(f"{name} scales must be float32 [NB, Hkv, bs]")
+        raise ValueError(f"{name} scales must be float32 with the codes' shape minus head_dim")
     return _dev(codes, name), _dev(scales, name + " scales")
 
 
-def kv_append_fp8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, stream=None):
+def kv_append_fp8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, stream=None, layout: str = "HND"):
     """Quantize new K/V rows ([T, Hkv, D], f32/f16/bf16) into the FP8 caches."""
     import torch
     T, Hkv, D = k.shape
-    NB, Hkv2, bs, D2 = k_codes.shape
+    NB, Hkv2, bs, D2 = _geom(k_codes, layout)
     if (Hkv, D) != (Hkv2, D2) or tuple(v.shape) != tuple(k.shape) or tuple(v_codes.shape) != tuple(k_codes.shape):
         raise ValueError("shape mismatch between k/v and the caches")
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
     st = load().pkv_kv_append_fp8(_dev(k, "k"), _dev(v, "v", k.dtype), _dev(slot_mapping, "slot_mapping", torch.int64),
-                                  T, kc, vc, ks, vs, NB, Hkv, D, bs, _torch_dtype_code(k), _stream_ptr(stream))
+                                  T, kc, vc, ks, vs, NB, Hkv, D, bs, LAYOUT_CODES[layout], _torch_dtype_code(k),
+                                  _stream_ptr(stream))
     _check(st, "pkv_kv_append_fp8")
 
 
-def _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace):
+def _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace, layout):
     import torch
     B, Hq, D = q.shape
-    NB, Hkv, bs, D2 = k_codes.shape
+    NB, Hkv, bs, D2 = _geom(k_codes, layout)
     if D2 != D or tuple(v_codes.shape) != tuple(k_codes.shape) or tuple(out.shape) != tuple(q.shape):
         raise ValueError("shape mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
         raise ValueError("block_tables must be [B, maxNB] and context_lens [B]")
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
                                                          workspace.numel() * workspace.element_size())
-    return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, t=_dev(block_tables, "block_tables", torch.int32),
-                mb=block_tables.shape[1], lens=_dev(context_lens, "context_lens", torch.int32),
-                out=_dev(out, "out", q.dtype), code=_torch_dtype_code(q), ws=ws_ptr, wsb=ws_bytes)
+    return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, lay=LAYOUT_CODES[layout],
+                t=_dev(block_tables, "block_tables", torch.int32), mb=block_tables.shape[1],
+                lens=_dev(context_lens, "context_lens", torch.int32), out=_dev(out, "out", q.dtype),
+                code=_torch_dtype_code(q), ws=ws_ptr, wsb=ws_bytes)
 
 
 def paged_decode_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, scale: float,
-                               out, workspace=None, partition_blocks: int = 0, stream=None):
-    a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace)
+                               out, workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
+    a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace, layout)
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
     st = load().pkv_paged_decode_attention_fp8(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"],
-                                               a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], float(scale), a["out"],
-                                               a["code"], a["ws"], a["wsb"], int(partition_blocks),
+                                               a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale),
+                                               a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
                                                _stream_ptr(stream))
     _check(st, "pkv_paged_decode_attention_fp8")
     return out
 
 
 def decode_step_fp8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
-                    scale: float, out, workspace=None, partition_blocks: int = 0, stream=None):
-    a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace)
+                    scale: float, out, workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
+    a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace, layout)
     if tuple(k_new.shape) != (a["B"], a["Hkv"], a["D"]) or tuple(v_new.shape) != tuple(k_new.shape):
         raise ValueError("k_new / v_new must be [B, Hkv, D]")
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
     st = load().pkv_decode_step_fp8(_dev(q, "q"), _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype), kc,
                                     vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
-                                    a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
+                                    a["lay"], a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
                                     int(partition_blocks), _stream_ptr(stream))
     _check(st, "pkv_decode_step_fp8")
     return out

@@ -54,8 +54,8 @@ using f16x8 = _Float16 __attribute__((ext_vector_type(8)));
 using s16x4 = short __attribute__((ext_vector_type(4)));
 using f16x4 = _Float16 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlockSize = 16;
-constexpr int kMaxPartitionBlocks = 128;  // two block ids per lane
+constexpr int kTile = 16;  // token rows per MFMA tile; a cache block holds block_size / 16 tiles
+constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two tile addresses per lane
 
 // K/V blocks kept in flight per wave ahead of the one being consumed
 #ifndef PKV_AHEAD_16BIT
@@ -185,7 +185,6 @@ struct Shape {
   static constexpr int kNK = kRowBytes / 64;     // 16-byte K chunks per lane
   static constexpr int kE = D / 16;              // V elements per lane per row
   static constexpr int kVDW = kE * kElt / 4;     // V dwords per lane per row
-  static constexpr int kTileBytes = kBlockSize * kRowBytes;
   static_assert(kRowBytes % 64 == 0, "head row must split into 4 x 16-byte chunk groups");
 };
 
@@ -195,21 +194,23 @@ struct BlockRegs {
   unsigned v[4][Shape<T, D>::kVDW];
 };
 
-// Load one block's K tile (MFMA A-operand layout) and V tile (row layout);
-// only the first `rows` token rows are fetched, the rest read as zero.
+// Load one 16-row tile of K (MFMA A-operand layout) and V (row layout); token
+// row r of the tile starts r * rs bytes after kt / vt (rs = the row bytes for
+// HND caches, num_kv_heads times that for NHD). Only the first `rows` rows are
+// fetched (the buffer bound is rows * rs), the rest read as zero.
 template <typename T, int D>
 __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const char* kt, const char* vt, int rows, int q4,
-                                           int ln) {
+                                           int ln, int rs) {
   using S = Shape<T, D>;
-  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows * S::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows * S::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows * rs);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows * rs);
 #pragma unroll
   for (int c = 0; c < S::kNK; ++c) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * S::kRowBytes + (4 * c + q4) * 16, 0, kCacheNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * rs + (4 * c + q4) * 16, 0, kCacheNT);
     r.k[c] = u32x4{v[0], v[1], v[2], v[3]};
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_dwords<S::kVDW>(r.v[i], rv, (4 * q4 + i) * S::kRowBytes + ln * S::kE * S::kElt);
+  for (int i = 0; i < 4; ++i) load_dwords<S::kVDW>(r.v[i], rv, (4 * q4 + i) * rs + ln * S::kE * S::kElt);
 }
 
 // ---------------------------------------------------------------------------
@@ -227,21 +228,24 @@ struct Fp8Regs {
   f32x4 ks, vs;
 };
 
-template <int D>
+// rs: code row stride in bytes (D for HND, num_kv_heads * D for NHD); the
+// scales of consecutive rows are adjacent for HND and num_kv_heads apart for NHD.
+template <int D, bool kNHD>
 __device__ __forceinline__ void load_block_fp8(Fp8Regs<D>& r, const char* kt, const char* vt, const char* kst,
-                                               const char* vst, int rows, int q4, int ln) {
-  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows * D);
-  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows * D);
-  const __amdgpu_buffer_rsrc_t rks = tile_rsrc(kst, rows * 4);
-  const __amdgpu_buffer_rsrc_t rvs = tile_rsrc(vst, rows * 4);
+                                               const char* vst, int rows, int q4, int ln, int rs) {
+  const int ss = kNHD ? rs / D * 4 : 4;  // scale row stride, bytes
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows * rs);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows * rs);
+  const __amdgpu_buffer_rsrc_t rks = tile_rsrc(kst, rows * ss);
+  const __amdgpu_buffer_rsrc_t rvs = tile_rsrc(vst, rows * ss);
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * D + q4 * (D / 4) + 16 * c, 0, kCacheNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * rs + q4 * (D / 4) + 16 * c, 0, kCacheNT);
     r.k[c] = u32x4{v[0], v[1], v[2], v[3]};
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int off = (4 * q4 + i) * D + ln * (D / 16);
+    const int off = (4 * q4 + i) * rs + ln * (D / 16);
     if constexpr (D / 64 == 2) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, kCacheNT);
       r.v[i][0] = v[0];
@@ -250,10 +254,18 @@ __device__ __forceinline__ void load_block_fp8(Fp8Regs<D>& r, const char* kt, co
       r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, kCacheNT);
     }
   }
-  const auto ks = __builtin_amdgcn_raw_buffer_load_b128(rks, 16 * q4, 0, kCacheNT);
-  const auto vs = __builtin_amdgcn_raw_buffer_load_b128(rvs, 16 * q4, 0, kCacheNT);
-  r.ks = f32x4{__uint_as_float(ks[0]), __uint_as_float(ks[1]), __uint_as_float(ks[2]), __uint_as_float(ks[3])};
-  r.vs = f32x4{__uint_as_float(vs[0]), __uint_as_float(vs[1]), __uint_as_float(vs[2]), __uint_as_float(vs[3])};
+  if constexpr (kNHD) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.ks[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (4 * q4 + i) * ss, 0, kCacheNT));
+      r.vs[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (4 * q4 + i) * ss, 0, kCacheNT));
+    }
+  } else {
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b128(rks, 16 * q4, 0, kCacheNT);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b128(rvs, 16 * q4, 0, kCacheNT);
+    r.ks = f32x4{__uint_as_float(ks[0]), __uint_as_float(ks[1]), __uint_as_float(ks[2]), __uint_as_float(ks[3])};
+    r.vs = f32x4{__uint_as_float(vs[0]), __uint_as_float(vs[1]), __uint_as_float(vs[2]), __uint_as_float(vs[3])};
+  }
 }
 
 // four E4M3 codes (one dword, lowest byte first) -> two dwords of 16-bit
@@ -351,8 +363,10 @@ struct DecodeArgs {
   int32_t group;        // Hq / Hkv
   int32_t head_groups;  // ceil(group / 16)
   int32_t num_blocks;
-  int32_t pb_per_part;  // blocks per partition (<= 128)
+  int32_t pb_per_part;  // 16-row tiles per partition (<= 128)
   int32_t num_parts;    // P
+  int32_t tiles_per_block;  // block_size / 16
+  int32_t cap_tokens;       // max_blocks * block_size
   float qk_scale;       // scale * log2(e)
   // fused decode step only
   const char* k_new;    // [B, Hkv, D]: newest token's K (written at position n-1)
@@ -374,13 +388,18 @@ struct DecodeArgs {
 // kFp8 = true: the caches hold E4M3 codes with per-row scales (T, the query
 // and output type, is bf16 or fp16); each block is converted exactly to T in
 // registers, the K scales multiply the scores and the V scales the weights.
-template <typename T, int D, bool kStep, bool kFp8>
+//
+// kNHD: caches [num_blocks, block_size, Hkv, D] instead of [num_blocks, Hkv,
+// block_size, D]. Either way the kernel walks 16-row tiles: a block of
+// block_size tokens is block_size / 16 tiles, and a tile is addressed by the
+// cache row index (in units of one head's row) of its first token.
+template <typename T, int D, bool kStep, bool kFp8, bool kNHD>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
   using R = typename RegsOf<T, D, kFp8>::type;
   constexpr bool k16 = sizeof(T) == 2;
   static_assert(!kFp8 || k16, "FP8 caches are read with 16-bit queries");
-  constexpr int kCacheTile = kFp8 ? kBlockSize * D : S::kTileBytes;  // one KV head's block, bytes
+  constexpr int kRowB = kFp8 ? D : S::kRowBytes;  // one head's cached row, bytes
   const int lane = threadIdx.x;
   const int q4 = lane >> 4;
   const int ln = lane & 15;
@@ -389,24 +408,35 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const int hg = blockIdx.y - j * a.head_groups;
   const int b = blockIdx.z;
 
-  const int cap = a.max_blocks * kBlockSize;
-  const int blk0 = p * a.pb_per_part;
-  // Physical ids of this partition's blocks (lane i: block blk0 + i, and
-  // blk0 + 64 + i for partitions longer than 64 blocks). They are loaded
-  // together with the sequence length, bounded by the table width rather than
-  // by the length, so the first K/V loads wait for one round trip, not two.
+  const int cap = a.cap_tokens;
+  const int blk0 = p * a.pb_per_part;  // first tile of the partition
+  const int row_step = kNHD ? a.num_kv_heads : 1;  // cache rows between consecutive tokens of one head
+  // First cache row of each of this partition's tiles (lane i: tile blk0 + i,
+  // and blk0 + 64 + i for partitions longer than 64 tiles), -1 where the
+  // table names a block outside the pool. The table is read together with
+  // the sequence length, bounded by the table width rather than by the
+  // length, so the first K/V loads wait for one round trip, not two.
   const size_t trow = static_cast<size_t>(b) * a.max_blocks;
-  int my_id = 0, my_id2 = 0;
-  if (lane < a.pb_per_part && blk0 + lane < a.max_blocks) my_id = a.block_tables[trow + blk0 + lane];
-  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < a.max_blocks) my_id2 = a.block_tables[trow + blk0 + 64 + lane];
+  const int m = a.tiles_per_block;
+  const int max_tiles = a.max_blocks * m;
+  auto tile_row0 = [&](int lt) -> int {
+    const int lb = lt / m;
+    const int id = a.block_tables[trow + lb];
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) return -1;
+    const int sub = lt - lb * m;
+    return kNHD ? (id * m + sub) * kTile * a.num_kv_heads + j : ((id * a.num_kv_heads + j) * m + sub) * kTile;
+  };
+  int my_r0 = -1, my_r02 = -1;
+  if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
+  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
   int n = a.context_lens[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nblk_seq = (n + kBlockSize - 1) / kBlockSize;
+  const int nblk_seq = (n + kTile - 1) / kTile;  // tiles of the sequence
   const int nparts = nblk_seq == 0 ? 1 : (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
   if (p >= nparts) return;
   const int nblk = min(a.pb_per_part, nblk_seq - blk0);  // may be 0 only when n == 0
-  auto block_id = [&](int t) -> int {  // t wave-uniform, < 128
-    return t < 64 ? __builtin_amdgcn_readlane(my_id, t & 63) : __builtin_amdgcn_readlane(my_id2, t & 63);
+  auto tile_r0 = [&](int t) -> int {  // t wave-uniform, < 128
+    return t < 64 ? __builtin_amdgcn_readlane(my_r0, t & 63) : __builtin_amdgcn_readlane(my_r02, t & 63);
   };
 
   // this lane's query head (column of the score tile)
@@ -428,14 +458,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  const size_t head_off = static_cast<size_t>(j) * kCacheTile;
-  const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * kCacheTile;
-
   // fused append: the partition holding position n-1 takes the new token's
   // K/V from k_new/v_new (row layout), in the same per-lane chunks the tiles use
   const bool has_new = kStep && n > 0 && p == nparts - 1;
-  const int new_t = has_new ? (n - 1) / kBlockSize - blk0 : -1;  // block index inside the partition
-  const int new_row = (n - 1) % kBlockSize;
+  const int new_t = has_new ? (n - 1) / kTile - blk0 : -1;  // tile index inside the partition
+  const int new_row = (n - 1) % kTile;
   u32x4 kn[S::kNK];
   unsigned vn[S::kVDW];
   u32x4 kn8[D / 64];  // FP8: quantized new K slice (this lane's q4 slice)
@@ -478,9 +505,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < D / 64; ++w) vn8[w] = quant4(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq.inv);
       // write codes and scales into the slot (head group 0 only)
-      const int id = block_id(new_t);
-      if (hg == 0 && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) {
-        const size_t row = (static_cast<size_t>(id) * a.num_kv_heads + j) * kBlockSize + new_row;
+      const int r0 = tile_r0(new_t);
+      if (hg == 0 && r0 >= 0) {
+        const size_t row = static_cast<size_t>(r0) + static_cast<size_t>(new_row) * row_step;
         if (ln == 0) {
 #pragma unroll
           for (int c = 0; c < D / 64; ++c)
@@ -519,9 +546,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         }
       }
       // write it into its slot (one head group writes; the others only read)
-      const int id = block_id(new_t);
-      if (hg == 0 && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) {
-        const size_t dst = static_cast<size_t>(id) * block_stride + head_off + new_row * S::kRowBytes;
+      const int r0 = tile_r0(new_t);
+      if (hg == 0 && r0 >= 0) {
+        const size_t dst = (static_cast<size_t>(r0) + static_cast<size_t>(new_row) * row_step) * S::kRowBytes;
         if (ln == 0) {
 #pragma unroll
           for (int c = 0; c < S::kNK; ++c) *reinterpret_cast<u32x4*>(a.k_cache_w + dst + (4 * c + q4) * 16) = kn[c];
@@ -537,22 +564,23 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   float m_run = kNegInf;  // running max of scaled scores (log2 units)
   float l_run = 0.f;      // this lane's share of the running denominator
 
-  // Tile offset of the partition's block t and how many of its token rows to
-  // fetch: 0 past the partition end or for an out-of-range id (nothing is
-  // read then), else the block's tokens below n.
-  auto block_src = [&](int t, int& rows) -> size_t {  // returns (block id) * Hkv + j
-    const int id = block_id(min(t, 127));
-    const bool ok = t < nblk && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
-    rows = ok ? min(kBlockSize, n - (blk0 + t) * kBlockSize) : 0;
+  // First cache row of the partition's tile t and how many of its token rows
+  // to fetch: 0 past the partition end or for an out-of-range id (nothing is
+  // read then), else the tile's tokens below n.
+  const int rs = kRowB * row_step;  // bytes between consecutive token rows of one head
+  auto block_src = [&](int t, int& rows) -> size_t {
+    const int r0 = tile_r0(min(t, 127));
+    const bool ok = t < nblk && r0 >= 0;
+    rows = ok ? min(kTile, n - (blk0 + t) * kTile) : 0;
     if (kStep && t == new_t) rows = new_row;  // the new row comes from registers
-    return (ok ? static_cast<size_t>(id) : 0) * a.num_kv_heads + j;
+    return ok ? static_cast<size_t>(r0) : 0;
   };
-  auto load_ring = [&](R& r, size_t tile, int rows) {
+  auto load_ring = [&](R& r, size_t row0, int rows) {
     if constexpr (kFp8) {
-      load_block_fp8<D>(r, a.k_cache + tile * kCacheTile, a.v_cache + tile * kCacheTile,
-                        a.k_scales + tile * (kBlockSize * 4), a.v_scales + tile * (kBlockSize * 4), rows, q4, ln);
+      load_block_fp8<D, kNHD>(r, a.k_cache + row0 * D, a.v_cache + row0 * D, a.k_scales + row0 * 4,
+                              a.v_scales + row0 * 4, rows, q4, ln, rs);
     } else {
-      load_block<T, D>(r, a.k_cache + tile * kCacheTile, a.v_cache + tile * kCacheTile, rows, q4, ln);
+      load_block<T, D>(r, a.k_cache + row0 * S::kRowBytes, a.v_cache + row0 * S::kRowBytes, rows, q4, ln, rs);
     }
   };
 
@@ -614,7 +642,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       if constexpr (kFp8) sc[i] = s[i] * rr.ks[i] * a.qk_scale;
       else sc[i] = s[i] * a.qk_scale;
     }
-    if (valid < kBlockSize) {  // wave-uniform: the last block of a sequence, or a bad id
+    if (valid < kTile) {  // wave-uniform: the last tile of a sequence, or a bad id
       // rows past `valid` were not fetched (K and V read as zero), so no NaN
       // padding enters the MFMAs; their scores are selected out here
 #pragma unroll
@@ -838,10 +866,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int num_seqs) 
   if (wave >= num_seqs * a.num_heads) return;
   const int b = wave / a.num_heads;
   const int hq = wave - b * a.num_heads;
-  const int cap = a.max_blocks * kBlockSize;
+  const int cap = a.cap_tokens;
   int n = a.context_lens[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nblk_seq = (n + kBlockSize - 1) / kBlockSize;
+  const int nblk_seq = (n + kTile - 1) / kTile;
   const int nparts = nblk_seq == 0 ? 1 : (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
   if (nparts == 1) return;  // the partition kernel wrote this row directly
   const size_t row0 = (static_cast<size_t>(b) * a.num_heads + hq) * a.num_parts;
@@ -911,7 +939,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, const int3
 __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k, const char* __restrict__ v,
                                                      const int64_t* __restrict__ slots, char* k_cache, char* v_cache,
                                                      int64_t total, int32_t chunks_per_row, int32_t num_kv_heads,
-                                                     int32_t row_bytes, int32_t block_size, int64_t num_slots) {
+                                                     int32_t row_bytes, int32_t block_size, int64_t num_slots,
+                                                     int32_t nhd) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int32_t c = static_cast<int32_t>(idx % chunks_per_row);
@@ -923,8 +952,9 @@ __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k,
   const int64_t pb = slot / block_size;
   const int64_t off = slot - pb * block_size;
   const size_t src = (static_cast<size_t>(i) * num_kv_heads + jh) * row_bytes + static_cast<size_t>(c) * 16;
-  const size_t dst = ((static_cast<size_t>(pb) * num_kv_heads + jh) * block_size + off) * row_bytes +
-                     static_cast<size_t>(c) * 16;
+  const size_t row = nhd ? (static_cast<size_t>(pb) * block_size + off) * num_kv_heads + jh
+                         : (static_cast<size_t>(pb) * num_kv_heads + jh) * block_size + off;
+  const size_t dst = row * row_bytes + static_cast<size_t>(c) * 16;
   const char* s = blockIdx.y ? v : k;
   char* d = blockIdx.y ? v_cache : k_cache;
   *reinterpret_cast<u32x4*>(d + dst) = *reinterpret_cast<const u32x4*>(s + src);
@@ -938,7 +968,8 @@ template <typename Tin, int D>
 __global__ __launch_bounds__(64) void append_fp8_kernel(const char* __restrict__ k, const char* __restrict__ v,
                                                         const int64_t* __restrict__ slots, char* k_cache,
                                                         char* v_cache, float* k_scales, float* v_scales,
-                                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots) {
+                                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
+                                                        int32_t nhd) {
   constexpr int kPer = D / 64;  // elements per lane
   const int lane = threadIdx.x;
   const int j = blockIdx.x;
@@ -958,7 +989,8 @@ __global__ __launch_bounds__(64) void append_fp8_kernel(const char* __restrict__
   for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, xor_shuffle(am, m));
   const RowQuant rq = row_quant(am);
   const int64_t pb = slot / block_size;
-  const int64_t row = (pb * num_kv_heads + j) * block_size + (slot - pb * block_size);
+  const int64_t off = slot - pb * block_size;
+  const int64_t row = nhd ? (pb * block_size + off) * num_kv_heads + j : (pb * num_kv_heads + j) * block_size + off;
   char* dst = (is_v ? v_cache : k_cache) + row * D + lane * kPer;
   const unsigned codes = quant4(x[0], kPer > 1 ? x[kPer - 1] : 0.f, 0.f, 0.f, rq.inv);
   if constexpr (kPer == 2) *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(codes & 0xffffu);
@@ -980,8 +1012,8 @@ int elt_bytes(pkv_dtype dt) {
 
 int64_t ceil_div64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-int32_t auto_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks) {
-  if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads <= 0 || max_blocks <= 0) return 16;
+int32_t auto_partition_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int64_t max_tiles) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads <= 0 || max_tiles <= 0) return 16;
   const int64_t group = num_heads / num_kv_heads;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * ceil_div64(group, 16);
   // Long partitions amortise each wave's start-up (table and Q loads, then the
@@ -989,22 +1021,37 @@ int32_t auto_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_k
   // workgroups per CU (256 CUs) keep enough loads in flight.
   const int64_t target = 1024;
   int32_t pb = 64;
-  while (pb > 8 && units * ceil_div64(max_blocks, pb) < target) pb /= 2;
+  while (pb > 8 && units * ceil_div64(max_tiles, pb) < target) pb /= 2;
   return pb;
+}
+
+bool valid_block_size(int32_t block_size) {
+  return block_size >= kTile && block_size % kTile == 0 && block_size / kTile <= kMaxPartitionBlocks;
+}
+
+// Partition size in cache blocks: `requested` if > 0, else the library's
+// choice (a tile count converted to whole blocks). Callers check the block size.
+int32_t partition_blocks_for(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks,
+                             int32_t block_size, int32_t requested) {
+  if (requested > 0) return requested;
+  const int32_t m = block_size / kTile;
+  const int32_t tiles =
+      auto_partition_tiles(num_seqs, num_heads, num_kv_heads, static_cast<int64_t>(max_blocks) * m);
+  return tiles / m > 0 ? tiles / m : 1;
 }
 
 enum Phase : unsigned { kPartitions = 1u, kMerge = 2u, kFusedStep = 4u };
 
-template <typename T, int D, bool kFp8 = false>
+template <typename T, int D, bool kFp8, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
   if (phases & kFusedStep) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, true, kFp8>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, true, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
   if (phases & kPartitions) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, false, kFp8>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, false, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
   }
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
@@ -1012,6 +1059,12 @@ pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases,
                        a, num_seqs);
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+template <typename T, int D, bool kFp8 = false>
+pkv_status launch_layout(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream, bool nhd) {
+  return nhd ? launch_decode<T, D, kFp8, true>(a, num_seqs, phases, stream)
+             : launch_decode<T, D, kFp8, false>(a, num_seqs, phases, stream);
 }
 
 size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int64_t parts) {
@@ -1041,17 +1094,25 @@ StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 // chosen phases never read may be null (the merge needs no q or caches).
 pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                        void* out, pkv_dtype dtype, const void* workspace, size_t workspace_bytes,
-                        int32_t partition_blocks, unsigned phases, void* stream, const void* k_new = nullptr,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                        int32_t num_blocks, float scale, void* out, pkv_dtype dtype, const void* workspace,
+                        size_t workspace_bytes, int32_t partition_blocks, unsigned phases, void* stream,
+                        const void* k_new = nullptr,
                         const void* v_new = nullptr, const float* k_scales = nullptr,
                         const float* v_scales = nullptr, bool fp8 = false) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
   if ((phases & kPartitions) && num_blocks <= 0) return PKV_EINVAL;
   if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
   if (elt_bytes(dtype) == 0) return PKV_EINVAL;
-  if (block_size != kBlockSize || (head_dim != 64 && head_dim != 128)) return PKV_EUNSUPPORTED;
-  if (partition_blocks < 0 || partition_blocks > kMaxPartitionBlocks) return PKV_EINVAL;
+  if (!valid_block_size(block_size) || (head_dim != 64 && head_dim != 128)) return PKV_EUNSUPPORTED;
+  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
+  if (partition_blocks < 0 || static_cast<int64_t>(partition_blocks) * (block_size / kTile) > kMaxPartitionBlocks)
+    return PKV_EINVAL;
+  // tile addresses are cache row indices and lengths are int32
+  if ((phases & (kPartitions | kFusedStep)) &&
+      static_cast<int64_t>(num_blocks) * num_kv_heads * block_size > INT32_MAX)
+    return PKV_EUNSUPPORTED;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!context_lens || !out) return PKV_EINVAL;
   if ((phases & (kPartitions | kFusedStep)) && (!q || !k_cache || !v_cache || !block_tables)) return PKV_EINVAL;
@@ -1073,10 +1134,12 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   a.group = num_heads / num_kv_heads;
   a.head_groups = (a.group + 15) / 16;
   a.num_blocks = num_blocks;
-  a.pb_per_part = partition_blocks > 0
-                      ? partition_blocks
-                      : auto_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
-  a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, a.pb_per_part));
+  const int32_t pb = partition_blocks_for(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                                          partition_blocks);
+  a.tiles_per_block = block_size / kTile;
+  a.pb_per_part = pb * a.tiles_per_block;
+  a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, pb));
+  a.cap_tokens = max_blocks_per_seq * block_size;
   a.qk_scale = scale * kLog2e;
   if (static_cast<int64_t>(num_kv_heads) * a.head_groups > 65535 || num_seqs > 65535) return PKV_EINVAL;
   a.k_scales = reinterpret_cast<const char*>(k_scales);
@@ -1102,23 +1165,24 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool nhd = layout == PKV_NHD;
   if (fp8) {
     if (dtype == PKV_BF16)
-      return head_dim == 128 ? launch_decode<__bf16, 128, true>(a, num_seqs, phases, s)
-                             : launch_decode<__bf16, 64, true>(a, num_seqs, phases, s);
-    return head_dim == 128 ? launch_decode<_Float16, 128, true>(a, num_seqs, phases, s)
-                           : launch_decode<_Float16, 64, true>(a, num_seqs, phases, s);
+      return head_dim == 128 ? launch_layout<__bf16, 128, true>(a, num_seqs, phases, s, nhd)
+                             : launch_layout<__bf16, 64, true>(a, num_seqs, phases, s, nhd);
+    return head_dim == 128 ? launch_layout<_Float16, 128, true>(a, num_seqs, phases, s, nhd)
+                           : launch_layout<_Float16, 64, true>(a, num_seqs, phases, s, nhd);
   }
   switch (dtype) {
     case PKV_BF16:
-      return head_dim == 128 ? launch_decode<__bf16, 128>(a, num_seqs, phases, s)
-                             : launch_decode<__bf16, 64>(a, num_seqs, phases, s);
+      return head_dim == 128 ? launch_layout<__bf16, 128>(a, num_seqs, phases, s, nhd)
+                             : launch_layout<__bf16, 64>(a, num_seqs, phases, s, nhd);
     case PKV_F16:
-      return head_dim == 128 ? launch_decode<_Float16, 128>(a, num_seqs, phases, s)
-                             : launch_decode<_Float16, 64>(a, num_seqs, phases, s);
+      return head_dim == 128 ? launch_layout<_Float16, 128>(a, num_seqs, phases, s, nhd)
+                             : launch_layout<_Float16, 64>(a, num_seqs, phases, s, nhd);
     case PKV_F32:
-      return head_dim == 128 ? launch_decode<float, 128>(a, num_seqs, phases, s)
-                             : launch_decode<float, 64>(a, num_seqs, phases, s);
+      return head_dim == 128 ? launch_layout<float, 128>(a, num_seqs, phases, s, nhd)
+                             : launch_layout<float, 64>(a, num_seqs, phases, s, nhd);
   }
   return PKV_EINVAL;
 }
@@ -1141,13 +1205,14 @@ const char* pkv_status_string(pkv_status s) {
   return "PKV_?: unknown status";
 }
 
-int32_t pkv_version(void) { return 110; }
+int32_t pkv_version(void) { return 200; }
 
 pkv_status pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                          void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t block_size, pkv_dtype dtype, void* stream) {
+                         int32_t block_size, pkv_layout layout, pkv_dtype dtype, void* stream) {
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
     return PKV_EINVAL;
+  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
   const int eb = elt_bytes(dtype);
   if (eb == 0) return PKV_EINVAL;
   if ((head_dim * eb) % 16 != 0) return PKV_EUNSUPPORTED;
@@ -1161,60 +1226,66 @@ pkv_status pkv_kv_append(const void* k, const void* v, const int64_t* slot_mappi
   hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(blocks), 2), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const char*>(k), static_cast<const char*>(v),
                      slot_mapping, static_cast<char*>(k_cache), static_cast<char*>(v_cache), total, chunks,
-                     num_kv_heads, row_bytes, block_size, static_cast<int64_t>(num_blocks) * block_size);
+                     num_kv_heads, row_bytes, block_size, static_cast<int64_t>(num_blocks) * block_size,
+                     static_cast<int32_t>(layout == PKV_NHD));
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
 int32_t pkv_decode_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                    int32_t max_blocks_per_seq) {
-  return auto_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+                                    int32_t max_blocks_per_seq, int32_t block_size) {
+  if (!valid_block_size(block_size)) return 0;
+  return partition_blocks_for(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, block_size, 0);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_blocks_per_seq, int32_t partition_blocks) {
+                                  int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_blocks) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
-  const int32_t pb = partition_blocks > 0 ? partition_blocks
-                                          : auto_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+  if (!valid_block_size(block_size)) return 0;
+  const int32_t pb = partition_blocks_for(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                                          partition_blocks);
   return workspace_bytes_for(num_seqs, num_heads, head_dim, ceil_div64(max_blocks_per_seq, pb));
 }
 
 pkv_status pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                      float scale, void* out, pkv_dtype dtype, void* workspace,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                                      int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
                                       size_t workspace_bytes, int32_t partition_blocks, void* stream) {
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
-                      partition_blocks, kPartitions | kMerge, stream);
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kPartitions | kMerge, stream);
 }
 
 pkv_status pkv_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
-                                 void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+                                 int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                                 pkv_dtype dtype, void* workspace, size_t workspace_bytes, int32_t partition_blocks,
+                                 void* stream) {
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
-                      partition_blocks, kPartitions, stream);
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kPartitions, stream);
 }
 
 size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                       int32_t max_blocks_per_seq, int32_t partition_blocks) {
+                                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_blocks) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
-  const int32_t pb = partition_blocks > 0 ? partition_blocks
-                                          : auto_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+  if (!valid_block_size(block_size)) return 0;
+  const int32_t pb = partition_blocks_for(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                                          partition_blocks);
   return step_layout(num_seqs, num_heads, num_kv_heads, head_dim, ceil_div64(max_blocks_per_seq, pb)).total();
 }
 
 pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t block_size, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
-                           void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+                           int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                           pkv_dtype dtype, void* workspace, size_t workspace_bytes, int32_t partition_blocks,
+                           void* stream) {
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
-                      partition_blocks, kFusedStep, stream, k_new, v_new);
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new);
 }
 
 pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int32_t n_caches, int32_t num_blocks,
@@ -1237,9 +1308,10 @@ pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int3
 
 pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                              void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
-                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_dtype dtype,
-                             void* stream) {
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                             pkv_dtype dtype, void* stream) {
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0) return PKV_EINVAL;
+  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
   if (elt_bytes(dtype) == 0) return PKV_EINVAL;
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
   if (num_kv_heads > 65535 || num_tokens > 65535) return PKV_EINVAL;
@@ -1251,7 +1323,7 @@ pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_m
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, static_cast<const char*>(k), static_cast<const char*>(v),
                        slot_mapping, static_cast<char*>(k_cache), static_cast<char*>(v_cache), k_scales, v_scales,
-                       num_kv_heads, block_size, num_slots);
+                       num_kv_heads, block_size, num_slots, static_cast<int32_t>(layout == PKV_NHD));
   };
   switch (dtype) {
     case PKV_F32: head_dim == 128 ? go(append_fp8_kernel<float, 128>) : go(append_fp8_kernel<float, 64>); break;
@@ -1266,23 +1338,24 @@ pkv_status pkv_paged_decode_attention_fp8(const void* q, const void* k_cache, co
                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                          int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
-                                          void* workspace, size_t workspace_bytes, int32_t partition_blocks,
-                                          void* stream) {
+                                          pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                                          pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          int32_t partition_blocks, void* stream) {
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
-                      partition_blocks, kPartitions | kMerge, stream, nullptr, nullptr, k_scales, v_scales, true);
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kPartitions | kMerge, stream, nullptr, nullptr, k_scales,
+                      v_scales, true);
 }
 
 pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                float* k_scales, float* v_scales, const int32_t* block_tables,
                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
-                               size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+                               pkv_layout layout, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                               void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream) {
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, scale, out, dtype, workspace, workspace_bytes,
-                      partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, true);
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, true);
 }
 
 pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
@@ -1290,7 +1363,7 @@ pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const
                             int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_blocks, void* out,
                             pkv_dtype dtype, void* stream) {
   return decode_entry(nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, 1, 0.f, out, dtype, workspace, workspace_bytes,
+                      num_kv_heads, head_dim, block_size, PKV_HND, 1, 0.f, out, dtype, workspace, workspace_bytes,
                       partition_blocks, kMerge, stream);
 }
 

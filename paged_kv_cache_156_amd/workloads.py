@@ -561,3 +561,13 @@ def make_device_workload_fp8(cfg: DecodeConfig, device, layers: int = 1, seed: O
     lens_dev = torch.from_numpy(lens.astype(np.int32)).to(device)
     return DeviceWorkloadFp8(cfg, lens, asg, out["q"], out["k_new"], out["v_new"], out["k_codes"], out["v_codes"],
                              out["k_scales"], out["v_scales"], tables, lens_dev)
+
+
+def to_layout(cache: np.ndarray, layout: str) -> np.ndarray:
+    """A [NB, Hkv, bs, ...] host cache (HND) in ``layout``: unchanged for "HND",
+    axes 1 and 2 swapped (a contiguous copy) for "NHD" = [NB, bs, Hkv, ...]."""
+    if layout == "HND":
+        return cache
+    if layout == "NHD":
+        return np.ascontiguousarray(np.swapaxes(cache, 1, 2))
+    raise ValueError(f"unknown layout {layout!r}")

@@ -282,7 +282,7 @@ def test_full_size_config_sampled(torch_dev, cfg_name):
     pkv.kv_append(wkd.k_new[0], wkd.v_new[0], torch.from_numpy(slots).to(dev), wkd.k_cache[0], wkd.v_cache[0])
     out = torch.full_like(wkd.q[0], float("nan"))
     ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables)
-    note(f"  launch: partition_blocks={pkv.decode_partition_blocks(B, cfg.num_heads, cfg.num_kv_heads, wkd.block_tables.shape[1])}")
+    note(f"  launch: partition_blocks={pkv.decode_partition_blocks(B, cfg.num_heads, cfg.num_kv_heads, wkd.block_tables.shape[1], cfg.block_size)}")
     pkv.paged_decode_attention(wkd.q[0], wkd.k_cache[0], wkd.v_cache[0], wkd.block_tables, wkd.context_lens_dev,
                                cfg.scale, out, ws)
     torch.cuda.synchronize()

@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     lib = pkv.load()
     for code in range(8):
         assert lib.pkv_status_string(code).decode().startswith(pkv.STATUS_NAMES[code])
-    assert lib.pkv_version() == 110
+    assert lib.pkv_version() == 200
 
 
 def test_block_accounting_matches_oracle():
@@ -173,27 +173,33 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
     lib = pkv.load()
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call fails validation
     # append
-    assert lib.pkv_kv_append(None, None, None, 0, None, None, 4, 2, 64, 16, 2, None) == pkv.PKV_OK  # no-op
-    assert lib.pkv_kv_append(None, fake, fake, 1, fake, fake, 4, 2, 64, 16, 2, None) == pkv.PKV_EINVAL
-    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 64, 16, 7, None) == pkv.PKV_EINVAL
-    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 4, 16, 2, None) == pkv.PKV_EUNSUPPORTED
-    assert lib.pkv_kv_append(fake, fake, fake, -1, fake, fake, 4, 2, 64, 16, 2, None) == pkv.PKV_EINVAL
+    assert lib.pkv_kv_append(None, None, None, 0, None, None, 4, 2, 64, 16, 0, 2, None) == pkv.PKV_OK  # no-op
+    assert lib.pkv_kv_append(None, fake, fake, 1, fake, fake, 4, 2, 64, 16, 0, 2, None) == pkv.PKV_EINVAL
+    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 64, 16, 0, 7, None) == pkv.PKV_EINVAL
+    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 4, 16, 0, 2, None) == pkv.PKV_EUNSUPPORTED
+    assert lib.pkv_kv_append(fake, fake, fake, -1, fake, fake, 4, 2, 64, 16, 0, 2, None) == pkv.PKV_EINVAL
+    assert lib.pkv_kv_append(fake, fake, fake, 1, fake, fake, 4, 2, 64, 16, 2, 2, None) == pkv.PKV_EINVAL  # layout
 
     def attn(**kw):
-        a = dict(q=fake, k=fake, v=fake, t=fake, mb=4, lens=fake, B=2, Hq=4, Hkv=2, D=64, bs=16, NB=8, scale=0.125,
-                 out=fake, dt=2, ws=None, wsb=0, pb=0)
+        a = dict(q=fake, k=fake, v=fake, t=fake, mb=4, lens=fake, B=2, Hq=4, Hkv=2, D=64, bs=16, lay=0, NB=8,
+                 scale=0.125, out=fake, dt=2, ws=None, wsb=0, pb=0)
         a.update(kw)
         return lib.pkv_paged_decode_attention(a["q"], a["k"], a["v"], a["t"], a["mb"], a["lens"], a["B"], a["Hq"],
-                                              a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"], a["out"], a["dt"],
-                                              a["ws"], a["wsb"], a["pb"], None)
+                                              a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], a["scale"], a["out"],
+                                              a["dt"], a["ws"], a["wsb"], a["pb"], None)
 
     assert attn(B=0) == pkv.PKV_OK  # empty batch: no launch
     assert attn(Hq=6, Hkv=4) == pkv.PKV_EINVAL
     assert attn(D=96) == pkv.PKV_EUNSUPPORTED
-    assert attn(bs=32) == pkv.PKV_EUNSUPPORTED
+    assert attn(bs=8) == pkv.PKV_EUNSUPPORTED   # block sizes: multiples of 16 up to 2048
+    assert attn(bs=24) == pkv.PKV_EUNSUPPORTED
+    assert attn(bs=4096) == pkv.PKV_EUNSUPPORTED
+    assert attn(lay=2) == pkv.PKV_EINVAL
     assert attn(dt=3) == pkv.PKV_EINVAL
     assert attn(q=None) == pkv.PKV_EINVAL
     assert attn(pb=129) == pkv.PKV_EINVAL
+    assert attn(bs=64, pb=33) == pkv.PKV_EINVAL  # a partition spans at most 2048 tokens
+    assert attn(NB=2 ** 27, Hkv=2, bs=16, Hq=4) == pkv.PKV_EUNSUPPORTED  # cache rows must fit int32
     # a launch that needs a workspace but gets none (4 blocks in partitions of 1)
     assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4, 1) > 0
     assert attn(pb=1) == pkv.PKV_ESMALL
@@ -205,6 +211,11 @@ def test_workspace_and_partition_choice():
     assert pkv.decode_workspace_bytes(2, 4, 2, 64, 3, 16) == 0
     pb = pkv.decode_partition_blocks(32, 64, 8, 256)
     assert 8 <= pb <= 64 and (pb & (pb - 1)) == 0
+    # larger blocks: the same tile count in whole blocks, at most 2048 tokens
+    for bs in (32, 64, 256, 2048):
+        pbb = pkv.decode_partition_blocks(32, 64, 8, 256 * 16 // bs, bs)
+        assert pbb >= 1 and pbb * bs <= 2048
+    assert pkv.decode_partition_blocks(32, 64, 8, 256, 24) == 0
     parts = -(-256 // pb)
     rows = 32 * 64 * parts
     assert pkv.decode_workspace_bytes(32, 64, 8, 128, 256, 0) >= rows * 129 * 4

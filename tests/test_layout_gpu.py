@@ -1,0 +1,132 @@
+"""GPU parity for the other cache geometries: the token-major NHD block
+layout and block sizes above 16 ("Understanding KV Cache" §3.2), for the
+append, the split attention and the fused step, in 16-bit, fp32 and FP8
+caches, against the CPU reference run in the same layout."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_156_amd import binding as pkv
+from paged_kv_cache_156_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+LENS = (1, 2, 15, 16, 17, 33, 64, 65, 255, 256, 257, 700, 1100)
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load()
+    return torch, torch.device("cuda:0")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_close(got, ref, dtype, what):
+    atol, rtol = TOL[dtype]
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    assert (err <= atol + rtol * np.abs(ref)).all(), f"{what}: max|err|={err.max():.3e}"
+
+
+def reference(wk, layout):
+    cfg = wk.cfg
+    kc, vc = wl.to_layout(wk.k_cache, layout).copy(), wl.to_layout(wk.v_cache, layout).copy()
+    slots = oracle.slot_mapping(wk.block_tables, wk.context_lens - 1, cfg.block_size)
+    oracle.kv_append(kc, vc, wk.k_new, wk.v_new, slots, cfg.block_size, layout)
+    ref = oracle.decode_attention(wk.q, kc, vc, wk.block_tables, wk.context_lens, cfg.scale, cfg.num_kv_heads,
+                                  cfg.block_size, cfg.dtype, layout=layout)
+    return ref, kc, vc, slots
+
+
+def partition_choices(bs):
+    return sorted({0, 1, max(1, 2048 // bs), max(1, 64 // bs)})
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+@pytest.mark.parametrize("dtype,shape", [("bf16", (32, 8, 128)), ("f16", (8, 8, 64)), ("f32", (28, 4, 128)),
+                                         ("bf16", (16, 1, 64))], ids=lambda x: str(x))
+def test_layout_and_block_size_parity(torch_dev, layout, bs, dtype, shape):
+    torch, dev = torch_dev
+    Hq, Hkv, D = shape
+    cfg = wl.DecodeConfig("geom", 0, 1, len(LENS), Hq, Hkv, D, bs, dtype, context_lens=LENS)
+    wk = wl.make_host_workload(cfg, seed=5000 + bs + Hq + D)
+    ref, kc_o, vc_o, slots = reference(wk, layout)
+    t = torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev)
+    lens = torch.from_numpy(wk.context_lens.astype(np.int32)).to(dev)
+    q = wl.raw_to_torch(wk.q, dtype, dev)
+    kn, vn = wl.raw_to_torch(wk.k_new, dtype, dev), wl.raw_to_torch(wk.v_new, dtype, dev)
+    for pb in partition_choices(bs):
+        note(f"{layout} bs={bs} {dtype} {shape} pb={pb}: append + split attention")
+        kc = wl.raw_to_torch(wl.to_layout(wk.k_cache, layout), dtype, dev)
+        vc = wl.raw_to_torch(wl.to_layout(wk.v_cache, layout), dtype, dev)
+        pkv.kv_append(kn, vn, torch.from_numpy(slots).to(dev), kc, vc, layout=layout)
+        out = torch.full_like(q, float("nan"))
+        ws = pkv.alloc_workspace(q, kc, t, pb, layout=layout)
+        pkv.paged_decode_attention(q, kc, vc, t, lens, cfg.scale, out, ws, pb, layout=layout)
+        torch.cuda.synchronize()
+        assert wl.torch_to_raw(kc, dtype).tobytes() == kc_o.tobytes(), "K pool after append"
+        assert wl.torch_to_raw(vc, dtype).tobytes() == vc_o.tobytes(), "V pool after append"
+        check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype, f"split {layout} bs={bs} pb={pb}")
+        note(f"{layout} bs={bs} {dtype} {shape} pb={pb}: fused step x2")
+        kc = wl.raw_to_torch(wl.to_layout(wk.k_cache, layout), dtype, dev)
+        vc = wl.raw_to_torch(wl.to_layout(wk.v_cache, layout), dtype, dev)
+        ws = pkv.alloc_step_workspace(q, kc, t, pb, layout=layout)
+        outs = []
+        for _ in range(2):
+            out = torch.full_like(q, float("nan"))
+            pkv.decode_step(q, kn, vn, kc, vc, t, lens, cfg.scale, out, ws, pb, layout=layout)
+            torch.cuda.synchronize()
+            outs.append(wl.torch_to_raw(out, dtype))
+        assert wl.torch_to_raw(kc, dtype).tobytes() == kc_o.tobytes(), "K pool after the fused append"
+        assert wl.torch_to_raw(vc, dtype).tobytes() == vc_o.tobytes(), "V pool after the fused append"
+        check_close(oracle.upcast(outs[0], dtype), ref, dtype, f"fused {layout} bs={bs} pb={pb}")
+        assert outs[0].tobytes() == outs[1].tobytes()
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("bs", [16, 32, 128])
+def test_fp8_layout_and_block_size_parity(torch_dev, layout, bs):
+    torch, dev = torch_dev
+    Hq, Hkv, D, dtype = 32, 8, 128, "bf16"
+    cfg = wl.DecodeConfig("geom8", 0, 1, len(LENS), Hq, Hkv, D, bs, dtype, context_lens=LENS)
+    wk = wl.make_host_workload_fp8(cfg, seed=6000 + bs)
+    to = lambda x: wl.to_layout(x, layout)
+    # scales are [NB, Hkv, bs]: give them a trailing axis for the swap
+    to_s = lambda x: to(x[..., None])[..., 0].copy()
+    kc_o, vc_o, ks_o, vs_o = to(wk.k_codes).copy(), to(wk.v_codes).copy(), to_s(wk.k_scales), to_s(wk.v_scales)
+    slots = oracle.slot_mapping(wk.block_tables, wk.context_lens - 1, bs)
+    oracle.kv_append_fp8(kc_o, vc_o, ks_o, vs_o, wk.k_new, wk.v_new, slots, bs, dtype, layout)
+    ref = oracle.decode_attention_fp8(wk.q, kc_o, vc_o, ks_o, vs_o, wk.block_tables, wk.context_lens, cfg.scale, Hkv,
+                                      bs, dtype, layout=layout)
+    t = torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev)
+    lens = torch.from_numpy(wk.context_lens.astype(np.int32)).to(dev)
+    q = wl.raw_to_torch(wk.q, dtype, dev)
+    kn, vn = wl.raw_to_torch(wk.k_new, dtype, dev), wl.raw_to_torch(wk.v_new, dtype, dev)
+    for pb in partition_choices(bs):
+        for fused in (False, True):
+            note(f"fp8 {layout} bs={bs} pb={pb} fused={fused}")
+            kc, vc = torch.from_numpy(to(wk.k_codes).copy()).to(dev), torch.from_numpy(to(wk.v_codes).copy()).to(dev)
+            ks, vs = torch.from_numpy(to_s(wk.k_scales)).to(dev), torch.from_numpy(to_s(wk.v_scales)).to(dev)
+            out = torch.full_like(q, float("nan"))
+            if fused:
+                ws = pkv.alloc_step_workspace(q, kc, t, pb, layout=layout)
+                pkv.decode_step_fp8(q, kn, vn, kc, vc, ks, vs, t, lens, cfg.scale, out, ws, pb, layout=layout)
+            else:
+                pkv.kv_append_fp8(kn, vn, torch.from_numpy(slots).to(dev), kc, vc, ks, vs, layout=layout)
+                ws = pkv.alloc_workspace(q, kc, t, pb, layout=layout)
+                pkv.paged_decode_attention_fp8(q, kc, vc, ks, vs, t, lens, cfg.scale, out, ws, pb, layout=layout)
+            torch.cuda.synchronize()
+            assert kc.cpu().numpy().tobytes() == kc_o.tobytes() and vc.cpu().numpy().tobytes() == vc_o.tobytes()
+            assert ks.cpu().numpy().tobytes() == ks_o.tobytes() and vs.cpu().numpy().tobytes() == vs_o.tobytes()
+            check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype,
+                        f"fp8 {layout} bs={bs} pb={pb} fused={fused}")

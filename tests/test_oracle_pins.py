@@ -424,3 +424,75 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         return lb, off, pb, pb * block_size + off
 
     assert bad_slot(6, [7, 3, 12], 4)[3] != 14
+
+
+# ---------------------------------------------------------------------------
+# block layouts and block sizes ("Understanding KV Cache" §3.2)
+# ---------------------------------------------------------------------------
+def test_layouts_and_block_sizes_reach_the_same_attention():
+    """One set of logical K/V rows, paged with block sizes 16, 32, 64 and 256
+    in HND and in NHD order (built here by direct indexing and a transpose,
+    not by the reference's own append), gives bit-identical reference
+    attention, equal to dense softmax attention over the rows."""
+    rng = np.random.default_rng(42)
+    Hq, Hkv, D = 8, 2, 64
+    lens = [1, 17, 70, 300]
+    B = len(lens)
+    rows_k = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    rows_v = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    scale = D ** -0.5
+    dense = np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            j = h // (Hq // Hkv)
+            s = rows_k[b][:, j].astype(np.float64) @ q[b, h].astype(np.float64) * scale
+            w = np.exp(s - s.max())
+            dense[b, h] = (w / w.sum()) @ rows_v[b][:, j].astype(np.float64)
+    results = {}
+    for bs in (16, 32, 64, 256):
+        nb = [-(-n // bs) for n in lens]
+        perm = rng.permutation(sum(nb))
+        kc = np.full((sum(nb), Hkv, bs, D), np.nan, np.float32)
+        vc = np.full_like(kc, np.nan)
+        table = np.zeros((B, max(nb)), np.int32)
+        c = 0
+        for b, n in enumerate(lens):
+            for lb in range(nb[b]):
+                pb = perm[c]
+                c += 1
+                table[b, lb] = pb
+                cnt = min(bs, n - lb * bs)
+                kc[pb, :, :cnt] = np.swapaxes(rows_k[b][lb * bs:lb * bs + cnt], 0, 1)
+                vc[pb, :, :cnt] = np.swapaxes(rows_v[b][lb * bs:lb * bs + cnt], 0, 1)
+        for layout in ("HND", "NHD"):
+            k_l = kc if layout == "HND" else np.ascontiguousarray(np.swapaxes(kc, 1, 2))
+            v_l = vc if layout == "HND" else np.ascontiguousarray(np.swapaxes(vc, 1, 2))
+            results[(bs, layout)] = oracle.decode_attention(q, k_l, v_l, table, lens, scale, Hkv, bs, "f32",
+                                                            layout=layout)
+        # planted mistake: token-major data read as head-major
+        wrong = oracle.decode_attention(q, np.ascontiguousarray(np.swapaxes(kc, 1, 2)).reshape(kc.shape),
+                                        np.ascontiguousarray(np.swapaxes(vc, 1, 2)).reshape(vc.shape), table, lens,
+                                        scale, Hkv, bs, "f32", layout="HND")
+        assert not np.allclose(np.nan_to_num(wrong), dense, atol=1e-3)
+    first = results[(16, "HND")]
+    for key, r in results.items():
+        assert np.array_equal(r, first), key
+    assert np.max(np.abs(first - dense)) < 1e-12
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_nhd_append_is_the_transposed_hnd_append(bs):
+    rng = np.random.default_rng(bs)
+    NB, Hkv, D, T = 6, 3, 64, 5
+    kc = rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32)
+    kn = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    vn = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    slots = [3, bs + 1, -1, 4 * bs + bs - 1, 2 * bs]
+    k_n, v_n = np.ascontiguousarray(np.swapaxes(kc, 1, 2)), np.ascontiguousarray(np.swapaxes(vc, 1, 2))
+    oracle.kv_append(kc, vc, kn, vn, slots, bs)
+    oracle.kv_append(k_n, v_n, kn, vn, slots, bs, "NHD")
+    assert np.array_equal(np.swapaxes(k_n, 1, 2), kc) and np.array_equal(np.swapaxes(v_n, 1, 2), vc)
+    # the written rows are where the slot formula says, token-major
+    assert np.array_equal(k_n[1, 1], kn[1]) and np.array_equal(k_n[0, 3], kn[0])
