@@ -174,6 +174,97 @@ def run_copy_blocks(args):
     print(json.dumps(result), flush=True)
 
 
+def run_prefill(args):
+    """--op prefill: chunked-prefill attention at the Llama-3-70B attention
+    shape (64 query / 8 KV heads, head_dim 128, bf16, 16-token blocks):
+    `--prefill-seqs` sequences, each with `--prefill-context` cached tokens
+    followed by a chunk of `--prefill-chunk` new query tokens (their K/V
+    already appended). FLOPs counted: 4 * Hq * D per (query token, visible
+    key) pair -- QK^T and PV -- over the causal triangle."""
+    import torch
+    from paged_kv_cache_156_amd import binding as pkv
+    from paged_kv_cache_156_amd import workloads as wl
+
+    pkv.load()
+    dev = torch.device("cuda:0")
+    B, C, P = args.prefill_seqs, args.prefill_chunk, args.prefill_context
+    base = wl.CONFIG_BY_NAME["llama3_70b"]
+    cfg = dataclasses.replace(base, name="prefill_70b", num_seqs=B, context_lens=(P + C,) * B,
+                              block_size=args.block_size or 16)
+    Hq, Hkv, D, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    lens = np.full(B, P + C, np.int32)
+    asg, slots, _ = pool_assignment(cfg, lens, pkv, wl)
+    wkd = wl.make_device_workload(cfg, dev, layers=1, context_lens=lens, assignment=asg)
+    kc, vc = wkd.k_cache[0], wkd.v_cache[0]
+    if args.layout == "NHD":
+        kc, vc = kc.transpose(1, 2).contiguous(), vc.transpose(1, 2).contiguous()
+    # the last position too: every chunk token's K/V is in the cache
+    pkv.kv_append(wkd.k_new[0], wkd.v_new[0], torch.from_numpy(slots).to(dev), kc, vc, layout=args.layout)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    q = torch.randn((B * C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    q_start = torch.arange(0, B * C + 1, C, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    pb = args.partition_blocks
+    ws = pkv.alloc_prefill_workspace(q_start, Hq, kc, wkd.block_tables, C, pb, layout=args.layout)
+
+    def launch():
+        pkv.prefill_attention(q, kc, vc, wkd.block_tables, q_start, C, wkd.context_lens_dev, cfg.scale, out, ws, pb,
+                              layout=args.layout)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "non-finite prefill output"
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        launch()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    pairs = B * sum(P + i + 1 for i in range(C))  # (query token, visible key) pairs
+    flops = 4 * Hq * D * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        import time as _t
+        # one sequence's chunk, the first rows only, on the host
+        blocks = asg.blocks[0]
+        idx = torch.from_numpy(blocks.astype(np.int64)).to(dev)
+        kh = wl.torch_to_raw(kc.index_select(0, idx), "bf16")
+        vh = wl.torch_to_raw(vc.index_select(0, idx), "bf16")
+        qh = wl.torch_to_raw(q[:C], "bf16")
+        table = np.arange(len(blocks), dtype=np.int32)[None, :]
+        rows, spent, pairs_cpu = 1, 0.0, 0
+        while spent < min(args.cpu_budget, 10.0) and rows <= C:
+            t = _t.perf_counter()
+            oracle.prefill_attention(qh[:rows], kh, vh, table, [0, rows], [P + rows], cfg.scale, Hkv, bs, "bf16",
+                                     args.layout)
+            spent = _t.perf_counter() - t
+            pairs_cpu = sum(P + i + 1 for i in range(rows))
+            rows *= 2
+        cpu = {"value": round(4 * Hq * D * pairs_cpu / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+               "kind": "oracle", "sample": f"{rows // 2} query tokens of one sequence's chunk, fp64 NumPy, one thread, "
+                                           f"{spent:.1f}s"}
+    result = {
+        "metric": "chunked-prefill paged attention TFLOP/s (QK^T + PV over the causal triangle)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefill: {B} sequences x {C}-token chunks after {P} cached tokens, 64 query / 8 KV "
+                               f"heads, head_dim 128, {args.layout} blocks of {bs}", "seqs": B, "chunk": C,
+                   "context": P, "partition_blocks": pb},
+        "roofline": {"bound": "mfma", "kernel": "decode_partition_kernel<prefill>", "achieved": round(tflops, 2),
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "alg_flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,8 +282,12 @@ def main():
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="cache block layout: HND [NB, Hkv, bs, D] (default) or NHD [NB, bs, Hkv, D]")
     ap.add_argument("--block-size", type=int, default=0, help="tokens per cache block (0 = the configuration's, 16)")
-    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
-                    help="decode: the decode step (default); copy_blocks: copy-on-write block copies")
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
+                    help="decode: the decode step (default); copy_blocks: copy-on-write block copies; "
+                         "prefill: chunked-prefill attention")
+    ap.add_argument("--prefill-seqs", type=int, default=4)
+    ap.add_argument("--prefill-chunk", type=int, default=512)
+    ap.add_argument("--prefill-context", type=int, default=4096)
     ap.add_argument("--copy-pairs", type=int, default=8192, help="block pairs per copy_blocks launch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
@@ -205,6 +300,9 @@ def main():
 
     if args.op == "copy_blocks":
         run_copy_blocks(args)
+        return
+    if args.op == "prefill":
+        run_prefill(args)
         return
 
     import torch

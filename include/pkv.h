@@ -281,6 +281,55 @@ pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_n
                                void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
 
 /*
+ * pkv_prefill_attention -- chunked prefill: causal attention of a chunk of
+ * new query tokens per sequence over the paged cache. Prefill processes many
+ * query positions at once as matrix products ("KV Cache and Inference
+ * Optimization", the prefill / decode comparison; "Understanding KV Cache"
+ * §2.1); split into chunks, each chunk's K/V is appended first
+ * (pkv_kv_append) and the chunk then attends to everything cached before it
+ * plus itself, causally (§1.2: position i sees positions <= i).
+ *
+ *   q             device [total_q, num_heads, head_dim]: the chunks of all
+ *                 sequences, packed; sequence b owns rows q_start[b] ..
+ *                 q_start[b+1]-1 (q_len_b = q_start[b+1] - q_start[b])
+ *   q_start       device int32 [num_seqs + 1], non-decreasing
+ *   max_q_len     host bound on every q_len_b (sizes the launch); longer
+ *                 chunks are truncated to it
+ *   context_lens  device int32 [num_seqs]: the sequence's cached tokens, the
+ *                 chunk's own included; chunk token i is at position
+ *                 context_lens[b] - q_len_b + i and attends to positions
+ *                 0 .. context_lens[b] - q_len_b + i (q_len_b is clamped to
+ *                 context_lens[b])
+ *   out           device [total_q, num_heads, head_dim], dtype of q; rows
+ *                 beyond a truncated chunk are not written
+ *   workspace     >= pkv_prefill_workspace_bytes(...) bytes, zero-filled before
+ *                 its first use; each completed call leaves its counters at
+ *                 zero (calls sharing a workspace must not overlap)
+ * Every other argument as pkv_paged_decode_attention. Work unit: 16 (query
+ * token, query head) rows of one KV head, one context partition; split
+ * contexts are merged in the kernel by the partition that finishes last.
+ * Errors as pkv_paged_decode_attention.
+ */
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
+                                   int32_t partition_blocks);
+pkv_status pkv_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* q_start,
+                                 int32_t max_q_len, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                                 int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t partition_blocks, void* stream);
+/* As pkv_prefill_attention over FP8 caches (codes + per-row scales, see the
+ * FP8 section above; dtype = q/out type, f16 or bf16). */
+pkv_status pkv_prefill_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                                     const float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* q_start, int32_t max_q_len, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale,
+                                     void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     int32_t partition_blocks, void* stream);
+
+/*
  * pkv_copy_blocks -- copy-on-write of whole physical blocks ("KV Cache and
  * Inference Optimization", section "PagedAttention": shared blocks are copied
  * when a sequence diverges). For each pair k (pairs[2k] = source id,

@@ -33,6 +33,10 @@ from .paged_decode import (  # noqa: F401
     decode_attention_fp8,
     kv_append_fp8,
 )
+from .prefill import (  # noqa: F401
+    prefill_attention,
+    prefill_attention_fp8,
+)
 from .prefix import (  # noqa: F401
     cached_full_blocks,
     apc_hit_blocks,

@@ -62,6 +62,11 @@ SIGNATURES = [
                                               _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_decode_step_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_prefill_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    ("pkv_prefill_attention", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_prefill_attention_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_copy_blocks", _i32, [_c.POINTER(_vp), _pi64, _i32, _i32, _vp, _i32, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
@@ -508,4 +513,71 @@ def decode_step_fp8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, block
                                     a["lay"], a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
                                     int(partition_blocks), _stream_ptr(stream))
     _check(st, "pkv_decode_step_fp8")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill
+# ---------------------------------------------------------------------------
+def prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_q_len, max_blocks, block_size=16,
+                            partition_blocks=0) -> int:
+    return int(load().pkv_prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_q_len, max_blocks,
+                                                  block_size, partition_blocks))
+
+
+def alloc_prefill_workspace(q_start, num_heads, k_cache, block_tables, max_q_len, partition_blocks=0,
+                            layout: str = "HND", head_dim=None):
+    """Zero-filled device workspace for ``prefill_attention`` (or None)."""
+    import torch
+    _, Hkv, bs, D = _geom(k_cache, layout)
+    nbytes = prefill_workspace_bytes(q_start.shape[0] - 1, num_heads, Hkv, D if head_dim is None else head_dim,
+                                     max_q_len, block_tables.shape[1], bs, partition_blocks)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=q_start.device) if nbytes else None
+
+
+def _prefill_args(q, q_start, max_q_len, k_cache, block_tables, context_lens, out, workspace, layout):
+    import torch
+    T, Hq, D = q.shape
+    NB, Hkv, bs, D2 = _geom(k_cache, layout)
+    B = context_lens.shape[0]
+    if D2 != D or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if tuple(q_start.shape) != (B + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("q_start must be [B+1], block_tables [B, maxNB], context_lens [B]")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size())
+    return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, lay=LAYOUT_CODES[layout], mq=int(max_q_len),
+                qs=_dev(q_start, "q_start", torch.int32), t=_dev(block_tables, "block_tables", torch.int32),
+                mb=block_tables.shape[1], lens=_dev(context_lens, "context_lens", torch.int32),
+                out=_dev(out, "out", q.dtype), code=_torch_dtype_code(q), ws=ws_ptr, wsb=ws_bytes)
+
+
+def prefill_attention(q, k_cache, v_cache, block_tables, q_start, max_q_len, context_lens, scale: float, out,
+                      workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
+    """Causal attention of each sequence's chunk (rows q_start[b]..q_start[b+1]-1
+    of q, the last tokens of its context_lens[b] cached tokens) over the cache."""
+    a = _prefill_args(q, q_start, max_q_len, k_cache, block_tables, context_lens, out, workspace, layout)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch")
+    st = load().pkv_prefill_attention(_dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+                                      a["t"], a["mb"], a["qs"], a["mq"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                      a["bs"], a["lay"], a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
+                                      int(partition_blocks), _stream_ptr(stream))
+    _check(st, "pkv_prefill_attention")
+    return out
+
+
+def prefill_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, q_start, max_q_len, context_lens,
+                          scale: float, out, workspace=None, partition_blocks: int = 0, stream=None,
+                          layout: str = "HND"):
+    a = _prefill_args(q, q_start, max_q_len, k_codes, block_tables, context_lens, out, workspace, layout)
+    if tuple(v_codes.shape) != tuple(k_codes.shape):
+        raise ValueError("shape mismatch")
+    kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
+    vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
+    st = load().pkv_prefill_attention_fp8(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["qs"], a["mq"], a["lens"],
+                                          a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale),
+                                          a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
+                                          _stream_ptr(stream))
+    _check(st, "pkv_prefill_attention_fp8")
     return out

@@ -377,10 +377,21 @@ struct DecodeArgs {
   // FP8 caches only: fp32 scale per (block, KV head, token row)
   const char* k_scales;
   const char* v_scales;
+  // chunked prefill only
+  const int32_t* q_start;  // [B + 1]: sequence b's query tokens are rows q_start[b] .. q_start[b+1]-1
+  int32_t max_q_len;       // bound on q_start[b+1] - q_start[b]
+  int32_t q_tiles;         // 16-row query tiles per (sequence, KV head): ceil(max_q_len * group / 16)
 };
 
-// kStep = false: one partition of attention (a split sequence leaves partials
-// for merge_kernel). kStep = true: the fused decode step -- the partition that
+// What one launch of the tile kernel computes.
+enum Mode : int {
+  kModeSplit = 0,    // one partition of decode attention; partials go to merge_kernel
+  kModeStep = 1,     // fused decode step: append + attention + in-kernel merge
+  kModePrefill = 2,  // chunked prefill: causal attention of a chunk's query tokens, in-kernel merge
+};
+
+// kMode = kModeSplit: one partition of attention (a split sequence leaves
+// partials for merge_kernel). kModeStep: the fused decode step -- the partition that
 // holds position n-1 also appends the newest token's K/V (written to its slot
 // and patched into its registers, never read back), and the last partition of
 // a split sequence to finish merges all partitions (arrival counter).
@@ -393,8 +404,18 @@ struct DecodeArgs {
 // block_size, D]. Either way the kernel walks 16-row tiles: a block of
 // block_size tokens is block_size / 16 tiles, and a tile is addressed by the
 // cache row index (in units of one head's row) of its first token.
-template <typename T, int D, bool kStep, bool kFp8, bool kNHD>
+//
+// kModePrefill: the 16 columns of a wave's score tile are 16 (query token,
+// query head) rows of one KV head's group, token-major (row r = token r / g,
+// head r % g), and each row sees the keys up to its own position: the chunk's
+// query tokens are the last q_len of the sequence's n cached tokens, so token
+// i sits at position n - q_len + i and attends to positions 0..n - q_len + i
+// (causal attention, "Understanding KV Cache" §1.2; prefill as a matrix
+// product over many query positions, "KV Cache and Inference Optimization").
+template <typename T, int D, int kMode, bool kFp8, bool kNHD>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+  constexpr bool kStep = kMode == kModeStep;
+  constexpr bool kPrefill = kMode == kModePrefill;
   using S = Shape<T, D>;
   using R = typename RegsOf<T, D, kFp8>::type;
   constexpr bool k16 = sizeof(T) == 2;
@@ -404,8 +425,10 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const int q4 = lane >> 4;
   const int ln = lane & 15;
   const int p = blockIdx.x;
-  const int j = blockIdx.y / a.head_groups;
-  const int hg = blockIdx.y - j * a.head_groups;
+  const int units_per_head = kPrefill ? a.q_tiles : a.head_groups;  // work units per (sequence, KV head)
+  const int j = blockIdx.y / units_per_head;
+  const int ui = blockIdx.y - j * units_per_head;  // head group (decode) or query tile (prefill)
+  const int hg = kPrefill ? 0 : ui;
   const int b = blockIdx.z;
 
   const int cap = a.cap_tokens;
@@ -431,7 +454,27 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
   int n = a.context_lens[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nblk_seq = (n + kTile - 1) / kTile;  // tiles of the sequence
+  // prefill: this wave's 16 query rows, their key limits, and the wave's span
+  int q_tok0 = 0, my_limit = 0, min_limit = 0;
+  bool row_ok = true;
+  int row_tok = 0, row_hin = 0;
+  if constexpr (kPrefill) {
+    q_tok0 = a.q_start[b];
+    int q_len = a.q_start[b + 1] - q_tok0;
+    q_len = q_len < 0 ? 0 : min(q_len, min(a.max_q_len, n));
+    const int rows = q_len * a.group;
+    const int r = ui * kTile + ln;
+    row_ok = r < rows;
+    row_tok = r / a.group;
+    row_hin = r - row_tok * a.group;
+    const int first = n - q_len;  // position of the chunk's first token
+    my_limit = row_ok ? first + row_tok + 1 : 0;
+    min_limit = first + (ui * kTile) / a.group + 1;
+    // the wave reads keys up to its last row's position (none if it has no rows)
+    n = ui * kTile < rows ? first + min(ui * kTile + kTile - 1, rows - 1) / a.group + 1 : 0;
+    if (n == 0) return;  // no rows: the unit does nothing (its merge counter stays untouched)
+  }
+  const int nblk_seq = (n + kTile - 1) / kTile;  // tiles the wave reads
   const int nparts = nblk_seq == 0 ? 1 : (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
   if (p >= nparts) return;
   const int nblk = min(a.pb_per_part, nblk_seq - blk0);  // may be 0 only when n == 0
@@ -439,15 +482,19 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     return t < 64 ? __builtin_amdgcn_readlane(my_r0, t & 63) : __builtin_amdgcn_readlane(my_r02, t & 63);
   };
 
-  // this lane's query head (column of the score tile)
-  const int hin = hg * 16 + ln;                 // head index inside the GQA group
-  const bool head_ok = hin < a.group;
+  // this lane's query row (column of the score tile): a head of the GQA group
+  // (decode) or a (token, head) pair of the chunk (prefill); qidx indexes the
+  // [*, Hq] rows of q and out
+  const int hin = kPrefill ? row_hin : hg * 16 + ln;  // head index inside the GQA group
+  const bool head_ok = kPrefill ? row_ok : hin < a.group;
   const int hq = j * a.group + (head_ok ? hin : 0);
+  const size_t qidx = kPrefill ? (static_cast<size_t>(q_tok0) + (head_ok ? row_tok : 0)) * a.num_heads + hq
+                               : static_cast<size_t>(b) * a.num_heads + hq;
 
   // Q as the B operand, same chunk permutation as K
   u32x4 qv[S::kNK];
   {
-    const char* qrow = a.q + (static_cast<size_t>(b) * a.num_heads + hq) * S::kRowBytes;
+    const char* qrow = a.q + qidx * S::kRowBytes;
 #pragma unroll
     for (int c = 0; c < S::kNK; ++c) {
       // byte offset of 16-byte chunk c: same-type caches (4c + q4) * 16 (the K
@@ -648,6 +695,13 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = 4 * q4 + i < valid ? sc[i] : kNegInf;
     }
+    if constexpr (kPrefill) {
+      const int key0 = (blk0 + t) * kTile;
+      if (key0 + kTile > min_limit) {  // wave-uniform: some row's causal limit falls inside this tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = key0 + 4 * q4 + i < my_limit ? sc[i] : kNegInf;
+      }
+    }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, xor_shuffle(mx, 16));
     mx = fmaxf(mx, xor_shuffle(mx, 32));
@@ -740,7 +794,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
 
   // this lane's 4 x E output values (d = (4*q4 + i) * E + mt), scaled, to `out`
   auto write_out = [&](float scale_by) {
-    char* orow = a.out + (static_cast<size_t>(b) * a.num_heads + hq) * S::kRowBytes;
+    char* orow = a.out + qidx * S::kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = (4 * q4 + i) * S::kE;
@@ -761,7 +815,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     write_out(inv);
     return;
   }
-  if constexpr (!kStep) {
+  if constexpr (kMode == kModeSplit) {
     // partials for merge_kernel: [B, Hq, P, D] and [B, Hq, P]
     const size_t row0 = (static_cast<size_t>(b) * a.num_heads + hq) * a.num_parts;
     float* o = a.ws_o + (row0 + p) * D;
@@ -784,7 +838,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     // whose loads are issued together) and resets the counter for the next
     // call. No L2 write-back or invalidate is needed.
     constexpr int kChunks = S::kE;  // 16-byte chunks per lane: 4*E floats
-    const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * a.head_groups + hg;
+    const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * units_per_head + ui;
     const size_t part_stride = static_cast<size_t>(kChunks) * 64 * 16;
     char* ob = reinterpret_cast<char*>(a.ws_o) + unit * a.num_parts * part_stride;
     char* lb = reinterpret_cast<char*>(a.ws_lse) + unit * a.num_parts * 64;
@@ -1012,10 +1066,8 @@ int elt_bytes(pkv_dtype dt) {
 
 int64_t ceil_div64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-int32_t auto_partition_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int64_t max_tiles) {
-  if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads <= 0 || max_tiles <= 0) return 16;
-  const int64_t group = num_heads / num_kv_heads;
-  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * ceil_div64(group, 16);
+int32_t auto_partition_tiles_for_units(int64_t units, int64_t max_tiles) {
+  if (units <= 0 || max_tiles <= 0) return 16;
   // Long partitions amortise each wave's start-up (table and Q loads, then the
   // first dependent K/V loads) and the merge; about four single-wave
   // workgroups per CU (256 CUs) keep enough loads in flight.
@@ -1023,6 +1075,13 @@ int32_t auto_partition_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv
   int32_t pb = 64;
   while (pb > 8 && units * ceil_div64(max_tiles, pb) < target) pb /= 2;
   return pb;
+}
+
+int32_t auto_partition_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int64_t max_tiles) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads <= 0) return 16;
+  const int64_t group = num_heads / num_kv_heads;
+  return auto_partition_tiles_for_units(static_cast<int64_t>(num_seqs) * num_kv_heads * ceil_div64(group, 16),
+                                        max_tiles);
 }
 
 bool valid_block_size(int32_t block_size) {
@@ -1046,12 +1105,12 @@ template <typename T, int D, bool kFp8, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
   if (phases & kFusedStep) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, true, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
   if (phases & kPartitions) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, false, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
   }
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
@@ -1065,6 +1124,14 @@ template <typename T, int D, bool kFp8 = false>
 pkv_status launch_layout(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream, bool nhd) {
   return nhd ? launch_decode<T, D, kFp8, true>(a, num_seqs, phases, stream)
              : launch_decode<T, D, kFp8, false>(a, num_seqs, phases, stream);
+}
+
+template <typename T, int D, bool kFp8 = false>
+pkv_status launch_prefill(const DecodeArgs& a, int32_t num_seqs, hipStream_t stream, bool nhd) {
+  dim3 grid(a.num_parts, a.num_kv_heads * a.q_tiles, num_seqs);
+  if (nhd) hipLaunchKernelGGL((decode_partition_kernel<T, D, kModePrefill, kFp8, true>), grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL((decode_partition_kernel<T, D, kModePrefill, kFp8, false>), grid, dim3(64), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
 size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int64_t parts) {
@@ -1081,13 +1148,19 @@ struct StepLayout {
   size_t o_bytes, lse_bytes, ctr_bytes;
   size_t total() const { return o_bytes + lse_bytes + ctr_bytes; }
 };
-StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int64_t parts) {
+StepLayout merge_layout(int64_t units, int32_t head_dim, int64_t parts) {
   if (parts <= 1) return {0, 0, 0};
-  const int64_t groups = ceil_div64(num_heads / num_kv_heads, 16);
-  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * groups;
   return {static_cast<size_t>(ceil_div64(units * parts * 64 * (head_dim / 4) * 4, 256) * 256),
           static_cast<size_t>(ceil_div64(units * parts * 16 * 4, 256) * 256),
           static_cast<size_t>(ceil_div64(units * 4, 256) * 256)};
+}
+StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int64_t parts) {
+  const int64_t groups = ceil_div64(num_heads / num_kv_heads, 16);
+  return merge_layout(static_cast<int64_t>(num_seqs) * num_kv_heads * groups, head_dim, parts);
+}
+// query tiles per (sequence, KV head) for a chunk of up to max_q_len tokens
+int64_t prefill_q_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len) {
+  return ceil_div64(static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads), kTile);
 }
 
 // Validate, fill DecodeArgs and launch the requested phases. Pointers the
@@ -1183,6 +1256,91 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
     case PKV_F32:
       return head_dim == 128 ? launch_layout<float, 128>(a, num_seqs, phases, s, nhd)
                              : launch_layout<float, 64>(a, num_seqs, phases, s, nhd);
+  }
+  return PKV_EINVAL;
+}
+
+// Chunked prefill: validate, fill DecodeArgs for kModePrefill and launch.
+pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* q_start, int32_t max_q_len,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale,
+                         void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                         int32_t partition_blocks, void* stream, const float* k_scales, const float* v_scales,
+                         bool fp8) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || max_q_len < 0)
+    return PKV_EINVAL;
+  if (num_blocks <= 0 || num_heads % num_kv_heads != 0 || elt_bytes(dtype) == 0) return PKV_EINVAL;
+  if (!valid_block_size(block_size) || (head_dim != 64 && head_dim != 128)) return PKV_EUNSUPPORTED;
+  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
+  if (partition_blocks < 0 || static_cast<int64_t>(partition_blocks) * (block_size / kTile) > kMaxPartitionBlocks)
+    return PKV_EINVAL;
+  if (static_cast<int64_t>(num_blocks) * num_kv_heads * block_size > INT32_MAX) return PKV_EUNSUPPORTED;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX) return PKV_EINVAL;
+  if (fp8 && dtype == PKV_F32) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !q_start || !context_lens || !out) return PKV_EINVAL;
+  if (fp8 && (!k_scales || !v_scales)) return PKV_EINVAL;
+  if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;
+  const int64_t qt = prefill_q_tiles(num_heads, num_kv_heads, max_q_len);
+  if (qt * num_kv_heads > 65535 || num_seqs > 65535) return PKV_EINVAL;
+  DecodeArgs a{};
+  a.q = static_cast<const char*>(q);
+  a.k_cache = static_cast<const char*>(k_cache);
+  a.v_cache = static_cast<const char*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = static_cast<char*>(out);
+  a.max_blocks = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.head_groups = 1;
+  a.num_blocks = num_blocks;
+  a.q_start = q_start;
+  a.max_q_len = max_q_len;
+  a.q_tiles = static_cast<int32_t>(qt);
+  const int32_t m = block_size / kTile;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * qt;
+  int32_t pb = partition_blocks;
+  if (pb == 0) {
+    const int32_t tiles = auto_partition_tiles_for_units(units, static_cast<int64_t>(max_blocks_per_seq) * m);
+    pb = tiles / m > 0 ? tiles / m : 1;
+  }
+  a.tiles_per_block = m;
+  a.pb_per_part = pb * m;
+  a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, pb));
+  a.cap_tokens = max_blocks_per_seq * block_size;
+  a.qk_scale = scale * kLog2e;
+  a.k_scales = reinterpret_cast<const char*>(k_scales);
+  a.v_scales = reinterpret_cast<const char*>(v_scales);
+  if (a.num_parts > 1) {
+    const StepLayout L = merge_layout(units, head_dim, a.num_parts);
+    if (!workspace || workspace_bytes < L.total()) return PKV_ESMALL;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws);
+    a.ws_lse = reinterpret_cast<float*>(ws + L.o_bytes);
+    a.counters = reinterpret_cast<int32_t*>(ws + L.o_bytes + L.lse_bytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool nhd = layout == PKV_NHD;
+  if (fp8) {
+    if (dtype == PKV_BF16)
+      return head_dim == 128 ? launch_prefill<__bf16, 128, true>(a, num_seqs, s, nhd)
+                             : launch_prefill<__bf16, 64, true>(a, num_seqs, s, nhd);
+    return head_dim == 128 ? launch_prefill<_Float16, 128, true>(a, num_seqs, s, nhd)
+                           : launch_prefill<_Float16, 64, true>(a, num_seqs, s, nhd);
+  }
+  switch (dtype) {
+    case PKV_BF16:
+      return head_dim == 128 ? launch_prefill<__bf16, 128>(a, num_seqs, s, nhd)
+                             : launch_prefill<__bf16, 64>(a, num_seqs, s, nhd);
+    case PKV_F16:
+      return head_dim == 128 ? launch_prefill<_Float16, 128>(a, num_seqs, s, nhd)
+                             : launch_prefill<_Float16, 64>(a, num_seqs, s, nhd);
+    case PKV_F32:
+      return head_dim == 128 ? launch_prefill<float, 128>(a, num_seqs, s, nhd)
+                             : launch_prefill<float, 64>(a, num_seqs, s, nhd);
   }
   return PKV_EINVAL;
 }
@@ -1356,6 +1514,46 @@ pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_n
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
                       workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, true);
+}
+
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
+                                   int32_t partition_blocks) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_q_len <= 0 ||
+      max_blocks_per_seq <= 0 || num_heads % num_kv_heads != 0 || !valid_block_size(block_size))
+    return 0;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                        prefill_q_tiles(num_heads, num_kv_heads, max_q_len);
+  const int32_t m = block_size / kTile;
+  int32_t pb = partition_blocks;
+  if (pb <= 0) {
+    const int32_t tiles = auto_partition_tiles_for_units(units, static_cast<int64_t>(max_blocks_per_seq) * m);
+    pb = tiles / m > 0 ? tiles / m : 1;
+  }
+  return merge_layout(units, head_dim, ceil_div64(max_blocks_per_seq, pb)).total();
+}
+
+pkv_status pkv_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* q_start,
+                                 int32_t max_q_len, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                                 int32_t num_blocks, float scale, void* out, pkv_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+  return prefill_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, q_start, max_q_len, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype,
+                       workspace, workspace_bytes, partition_blocks, stream, nullptr, nullptr, false);
+}
+
+pkv_status pkv_prefill_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                                     const float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* q_start, int32_t max_q_len, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale,
+                                     void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     int32_t partition_blocks, void* stream) {
+  return prefill_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, q_start, max_q_len, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype,
+                       workspace, workspace_bytes, partition_blocks, stream, k_scales, v_scales, true);
 }
 
 pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

@@ -496,3 +496,82 @@ def test_nhd_append_is_the_transposed_hnd_append(bs):
     assert np.array_equal(np.swapaxes(k_n, 1, 2), kc) and np.array_equal(np.swapaxes(v_n, 1, 2), vc)
     # the written rows are where the slot formula says, token-major
     assert np.array_equal(k_n[1, 1], kn[1]) and np.array_equal(k_n[0, 3], kn[0])
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill
+# ---------------------------------------------------------------------------
+def _dense_causal(qs, ks, vs, scale, group):
+    """softmax(Q K^T * scale + M) V with the additive causal mask M (0 on and
+    below the diagonal, -inf above), per query head, in float64."""
+    T, Hq, D = qs.shape
+    out = np.zeros((T, Hq, D))
+    M = np.triu(np.full((T, T), -np.inf), 1)
+    for h in range(Hq):
+        j = h // group
+        s = qs[:, h] @ ks[:, j].T * scale + M
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h] = (w / w.sum(axis=1, keepdims=True)) @ vs[:, j]
+    return out
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_prefill_matches_dense_causal_attention_and_chunks_compose(layout):
+    import torch
+    rng = np.random.default_rng(77)
+    Hq, Hkv, D, bs = 8, 2, 64, 16
+    group = Hq // Hkv
+    n = 53
+    ks = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    vs = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    qs = rng.standard_normal((n, Hq, D)).astype(np.float32)
+    scale = D ** -0.5
+    nb = -(-n // bs)
+    perm = rng.permutation(nb + 2)[:nb]
+    kc = np.full((nb + 2, Hkv, bs, D), np.nan, np.float32)
+    vc = np.full_like(kc, np.nan)
+    for t in range(n):
+        kc[perm[t // bs], :, t % bs] = ks[t]
+        vc[perm[t // bs], :, t % bs] = vs[t]
+    if layout == "NHD":
+        kc, vc = np.ascontiguousarray(np.swapaxes(kc, 1, 2)), np.ascontiguousarray(np.swapaxes(vc, 1, 2))
+    table = perm[None, :].astype(np.int32)
+    full = oracle.prefill_attention(qs, kc, vc, table, [0, n], [n], scale, Hkv, bs, "f32", layout)
+    dense = _dense_causal(qs.astype(np.float64), ks.astype(np.float64), vs.astype(np.float64), scale, group)
+    assert np.max(np.abs(full - dense)) < 1e-12
+    # a library routine: torch's causal SDPA in float64, K/V repeated per group
+    qt = torch.from_numpy(qs.astype(np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(ks.astype(np.float64)).repeat_interleave(group, 1).permute(1, 0, 2)
+    vt = torch.from_numpy(vs.astype(np.float64)).repeat_interleave(group, 1).permute(1, 0, 2)
+    sd = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    assert np.max(np.abs(full - sd.permute(1, 0, 2).numpy())) < 1e-12
+    # chunks [0, 20), [20, 37), [37, 53), each over the cache filled up to its end
+    parts = []
+    for lo, hi in ((0, 20), (20, 37), (37, 53)):
+        parts.append(oracle.prefill_attention(qs[lo:hi], kc, vc, table, [0, hi - lo], [hi], scale, Hkv, bs, "f32",
+                                              layout))
+    assert np.array_equal(np.concatenate(parts), full)
+    # planted mistake: every token also sees the next position
+    wrong = np.stack([oracle.decode_attention_seq(qs[i], kc, vc, table[0], min(i + 2, n), scale, Hkv, bs, "f32",
+                                                  layout) for i in range(n)])
+    assert np.max(np.abs(wrong - dense)) > 1e-3
+
+
+def test_prefill_packs_sequences_and_truncates():
+    rng = np.random.default_rng(3)
+    Hq, Hkv, D, bs = 4, 4, 64, 16
+    lens = [5, 40]
+    qlen = [5, 7]
+    NB = 4
+    kc = rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32)
+    table = np.array([[3, 0, 0], [1, 2, 0]], np.int32)
+    q = rng.standard_normal((12, Hq, D)).astype(np.float32)
+    out = oracle.prefill_attention(q, kc, vc, table, [0, 5, 12], lens, 0.125, Hkv, bs, "f32")
+    for b, (q0, L) in enumerate(((0, 5), (5, 7))):
+        for i in range(L):
+            want = oracle.decode_attention_seq(q[q0 + i], kc, vc, table[b], lens[b] - L + i + 1, 0.125, Hkv, bs, "f32")
+            assert np.array_equal(out[q0 + i], want)
+    # a chunk longer than its sequence is cut to the sequence's length: the rows past it are not written
+    out2 = oracle.prefill_attention(q, kc, vc, table, [0, 7, 12], [5, 40], 0.125, Hkv, bs, "f32")
+    assert np.array_equal(out2[:5], out[:5]) and not out2[5:7].any()
