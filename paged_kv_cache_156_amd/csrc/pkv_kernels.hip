@@ -390,6 +390,13 @@ enum Mode : int {
   kModePrefill = 2,  // chunked prefill: causal attention of a chunk's query tokens, in-kernel merge
 };
 
+// Row groups (16 query rows each) a prefill wave processes against every
+// loaded K/V tile: 4 for 16-bit queries, 2 for fp32 (register budget); one for
+// the decode modes.
+template <typename T, int kMode>
+constexpr int kPrefillRowGroups = kMode == kModePrefill ? (sizeof(T) == 2 ? 4 : 2) : 1;
+constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 : 4; }
+
 // kMode = kModeSplit: one partition of attention (a split sequence leaves
 // partials for merge_kernel). kModeStep: the fused decode step -- the partition that
 // holds position n-1 also appends the newest token's K/V (written to its slot
@@ -419,6 +426,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
   using R = typename RegsOf<T, D, kFp8>::type;
   constexpr bool k16 = sizeof(T) == 2;
+  // groups of 16 query rows per wave, all against the same K/V tiles (prefill
+  // reuses each loaded tile for kR row groups; decode has one group per wave)
+  constexpr int kR = kPrefillRowGroups<T, kMode>;
   static_assert(!kFp8 || k16, "FP8 caches are read with 16-bit queries");
   constexpr int kRowB = kFp8 ? D : S::kRowBytes;  // one head's cached row, bytes
   const int lane = threadIdx.x;
@@ -454,24 +464,35 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
   int n = a.context_lens[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  // prefill: this wave's 16 query rows, their key limits, and the wave's span
-  int q_tok0 = 0, my_limit = 0, min_limit = 0;
-  bool row_ok = true;
-  int row_tok = 0, row_hin = 0;
+  // prefill: this wave's 16 * kR query rows, their key limits, and the wave's span
+  int q_tok0 = 0, min_limit = 0;
+  int my_limit[kR], row_tok[kR], row_hin[kR];
+  bool row_ok[kR];
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    my_limit[rg] = 0;
+    row_tok[rg] = 0;
+    row_hin[rg] = 0;
+    row_ok[rg] = true;
+  }
   if constexpr (kPrefill) {
     q_tok0 = a.q_start[b];
     int q_len = a.q_start[b + 1] - q_tok0;
     q_len = q_len < 0 ? 0 : min(q_len, min(a.max_q_len, n));
     const int rows = q_len * a.group;
-    const int r = ui * kTile + ln;
-    row_ok = r < rows;
-    row_tok = r / a.group;
-    row_hin = r - row_tok * a.group;
-    const int first = n - q_len;  // position of the chunk's first token
-    my_limit = row_ok ? first + row_tok + 1 : 0;
-    min_limit = first + (ui * kTile) / a.group + 1;
+    const int r0 = ui * kTile * kR;  // the wave's first row
+    const int first = n - q_len;     // position of the chunk's first token
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) {
+      const int r = r0 + rg * kTile + ln;
+      row_ok[rg] = r < rows;
+      row_tok[rg] = r / a.group;
+      row_hin[rg] = r - row_tok[rg] * a.group;
+      my_limit[rg] = row_ok[rg] ? first + row_tok[rg] + 1 : 0;
+    }
+    min_limit = first + r0 / a.group + 1;
     // the wave reads keys up to its last row's position (none if it has no rows)
-    n = ui * kTile < rows ? first + min(ui * kTile + kTile - 1, rows - 1) / a.group + 1 : 0;
+    n = r0 < rows ? first + min(r0 + kTile * kR - 1, rows - 1) / a.group + 1 : 0;
     if (n == 0) return;  // no rows: the unit does nothing (its merge counter stays untouched)
   }
   const int nblk_seq = (n + kTile - 1) / kTile;  // tiles the wave reads
@@ -485,23 +506,24 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   // this lane's query row (column of the score tile): a head of the GQA group
   // (decode) or a (token, head) pair of the chunk (prefill); qidx indexes the
   // [*, Hq] rows of q and out
-  const int hin = kPrefill ? row_hin : hg * 16 + ln;  // head index inside the GQA group
-  const bool head_ok = kPrefill ? row_ok : hin < a.group;
-  const int hq = j * a.group + (head_ok ? hin : 0);
-  const size_t qidx = kPrefill ? (static_cast<size_t>(q_tok0) + (head_ok ? row_tok : 0)) * a.num_heads + hq
-                               : static_cast<size_t>(b) * a.num_heads + hq;
-
-  // Q as the B operand, same chunk permutation as K
-  u32x4 qv[S::kNK];
-  {
-    const char* qrow = a.q + qidx * S::kRowBytes;
+  bool head_ok[kR];
+  size_t qidx[kR];
+  u32x4 qv[kR][S::kNK];  // Q as the B operand, same chunk permutation as K
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    const int hin = kPrefill ? row_hin[rg] : hg * 16 + ln;  // head index inside the GQA group
+    head_ok[rg] = kPrefill ? row_ok[rg] : hin < a.group;
+    const int hq = j * a.group + (head_ok[rg] ? hin : 0);
+    qidx[rg] = kPrefill ? (static_cast<size_t>(q_tok0) + (head_ok[rg] ? row_tok[rg] : 0)) * a.num_heads + hq
+                        : static_cast<size_t>(b) * a.num_heads + hq;
+    const char* qrow = a.q + qidx[rg] * S::kRowBytes;
 #pragma unroll
     for (int c = 0; c < S::kNK; ++c) {
       // byte offset of 16-byte chunk c: same-type caches (4c + q4) * 16 (the K
       // tile's chunk order); FP8 caches (T is 16-bit) elements q4 * D/4 + 8c
       const int off = kFp8 ? (q4 * (D / 4) + 8 * c) * 2 : (4 * c + q4) * 16;
       static_assert(kFp8 ? (D / 4) * 2 <= S::kRowBytes : true, "query slice must lie inside the row");
-      qv[c] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0, 0, 0, 0};
+      qv[rg][c] = head_ok[rg] ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -605,11 +627,16 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  f32x4 acc[S::kE];
+  f32x4 acc[kR][S::kE];
+  float m_run[kR];  // running max of scaled scores (log2 units)
+  float l_run[kR];  // this lane's share of the running denominator
 #pragma unroll
-  for (int mt = 0; mt < S::kE; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;  // running max of scaled scores (log2 units)
-  float l_run = 0.f;      // this lane's share of the running denominator
+  for (int rg = 0; rg < kR; ++rg) {
+#pragma unroll
+    for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rg] = kNegInf;
+    l_run[rg] = 0.f;
+  }
 
   // First cache row of the partition's tile t and how many of its token rows
   // to fetch: 0 past the partition end or for an out-of-range id (nothing is
@@ -671,17 +698,20 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       rp = &rr;
     }
     BlockRegs<T, D>& r = *rp;
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) {
     // scores
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (k16) {
 #pragma unroll
-      for (int c = 0; c < S::kNK; ++c) s = mfma_qk16<T>(r.k[c], qv[c], s);
+      for (int c = 0; c < S::kNK; ++c) s = mfma_qk16<T>(r.k[c], qv[rg][c], s);
     } else {
 #pragma unroll
       for (int c = 0; c < S::kNK; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(r.k[c][e]), __uint_as_float(qv[c][e]), s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(r.k[c][e]), __uint_as_float(qv[rg][c][e]), s, 0, 0,
+                                                   0);
     }
     float sc[4];
 #pragma unroll
@@ -699,7 +729,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       const int key0 = (blk0 + t) * kTile;
       if (key0 + kTile > min_limit) {  // wave-uniform: some row's causal limit falls inside this tile
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = key0 + 4 * q4 + i < my_limit ? sc[i] : kNegInf;
+        for (int i = 0; i < 4; ++i) sc[i] = key0 + 4 * q4 + i < my_limit[rg] ? sc[i] : kNegInf;
       }
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -709,16 +739,16 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     // block maximum exceeds it by more than kRescaleSlack (log2 units), so the
     // weights stay <= 2^kRescaleSlack and the accumulator is rescaled rarely.
     // Any reference gives the same softmax; this one keeps exp2 in range.
-    const bool grow = mx > m_run + kRescaleSlack;
+    const bool grow = mx > m_run[rg] + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
-      const float m_new = grow ? mx : m_run;
-      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = grow ? mx : m_run[rg];
+      const float alpha = m_run[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
 #pragma unroll
-      for (int mt = 0; mt < S::kE; ++mt) acc[mt] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
+      for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= alpha;
+      l_run[rg] *= alpha;
+      m_run[rg] = m_new;
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
@@ -734,7 +764,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         ph[i] = to_bits16<T>(pv);
         pl[i] = to_bits16<T>(pv - from_bits16<T>(ph[i]));
       }
-      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      l_run[rg] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       const u32x2 pw_hi = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
       const u32x2 pw_lo = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)};
 #pragma unroll
@@ -742,17 +772,18 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
         const u32x2 av = {__builtin_amdgcn_perm(r.v[1][mt >> 1], r.v[0][mt >> 1], sel),
                           __builtin_amdgcn_perm(r.v[3][mt >> 1], r.v[2][mt >> 1], sel)};
-        acc[mt] = mfma_pv16<T>(av, pw_hi, acc[mt]);
-        acc[mt] = mfma_pv16<T>(av, pw_lo, acc[mt]);
+        acc[rg][mt] = mfma_pv16<T>(av, pw_hi, acc[rg][mt]);
+        acc[rg][mt] = mfma_pv16<T>(av, pw_lo, acc[rg][mt]);
       }
     } else {
-      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      l_run[rg] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int mt = 0; mt < S::kE; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(r.v[i][mt]), pr[i], acc[mt], 0, 0, 0);
+          acc[rg][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(r.v[i][mt]), pr[i], acc[rg][mt], 0, 0, 0);
     }
+    }  // row groups
   };
 
   // Stream the partition's blocks through a register ring that keeps kAhead
@@ -786,15 +817,22 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  // combine the four lanes' partial denominators of each head
-  float l_tot = l_run + xor_shuffle(l_run, 16);
-  l_tot += xor_shuffle(l_tot, 32);
-  if (!head_ok) return;
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  // combine the four lanes' partial denominators of each row
+  float l_tot[kR], inv[kR];
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    l_tot[rg] = l_run[rg] + xor_shuffle(l_run[rg], 16);
+    l_tot[rg] += xor_shuffle(l_tot[rg], 32);
+    inv[rg] = l_tot[rg] > 0.f ? 1.0f / l_tot[rg] : 0.f;
+  }
+  if constexpr (kR == 1) {
+    if (!head_ok[0]) return;  // padding heads of the group: nothing to store
+  }
 
-  // this lane's 4 x E output values (d = (4*q4 + i) * E + mt), scaled, to `out`
-  auto write_out = [&](float scale_by) {
-    char* orow = a.out + qidx * S::kRowBytes;
+  // this lane's 4 x E output values of row group rg (d = (4*q4 + i) * E + mt), scaled, to `out`
+  auto write_out = [&](int rg, float scale_by) {
+    if (!head_ok[rg]) return;
+    char* orow = a.out + qidx[rg] * S::kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = (4 * q4 + i) * S::kE;
@@ -802,110 +840,127 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       if constexpr (k16) {
 #pragma unroll
         for (int mt = 0; mt < S::kE; mt += 2)
-          w[mt >> 1] = to_bits16<T>(acc[mt][i] * scale_by) | (to_bits16<T>(acc[mt + 1][i] * scale_by) << 16);
+          w[mt >> 1] =
+              to_bits16<T>(acc[rg][mt][i] * scale_by) | (to_bits16<T>(acc[rg][mt + 1][i] * scale_by) << 16);
       } else {
 #pragma unroll
-        for (int mt = 0; mt < S::kE; ++mt) w[mt] = __float_as_uint(acc[mt][i] * scale_by);
+        for (int mt = 0; mt < S::kE; ++mt) w[mt] = __float_as_uint(acc[rg][mt][i] * scale_by);
       }
       store_dwords<S::kVDW>(orow + d0 * S::kElt, w);
     }
   };
 
   if (nparts == 1) {
-    write_out(inv);
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) write_out(rg, inv[rg]);
     return;
   }
   if constexpr (kMode == kModeSplit) {
+    static_assert(kR == 1, "the split path has one row group");
     // partials for merge_kernel: [B, Hq, P, D] and [B, Hq, P]
-    const size_t row0 = (static_cast<size_t>(b) * a.num_heads + hq) * a.num_parts;
+    const size_t row0 = qidx[0] * a.num_parts;  // qidx = b * Hq + hq
     float* o = a.ws_o + (row0 + p) * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = (4 * q4 + i) * S::kE;
 #pragma unroll
       for (int mt = 0; mt < S::kE; mt += 4)
-        *reinterpret_cast<f32x4*>(o + d0 + mt) =
-            f32x4{acc[mt][i] * inv, acc[mt + 1][i] * inv, acc[mt + 2][i] * inv, acc[mt + 3][i] * inv};
+        *reinterpret_cast<f32x4*>(o + d0 + mt) = f32x4{acc[0][mt][i] * inv[0], acc[0][mt + 1][i] * inv[0],
+                                                       acc[0][mt + 2][i] * inv[0], acc[0][mt + 3][i] * inv[0]};
     }
-    if (q4 == 0) a.ws_lse[row0 + p] = m_run + __builtin_amdgcn_logf(l_tot);
+    if (q4 == 0) a.ws_lse[row0 + p] = m_run[0] + __builtin_amdgcn_logf(l_tot[0]);
   } else {
-    // Fused merge. Partials are stored lane-major per work unit (each store
-    // instruction writes 64 lanes x 16 bytes contiguously) with device-coherent
-    // stores (sc1: written through the XCD's L2), then the wave drains its
-    // stores and counts its arrival. The last partition of the sequence to
-    // arrive reads all partials back with device-coherent loads, combines them
-    // (exact log-sum-exp merge, one online pass over groups of four partitions
-    // whose loads are issued together) and resets the counter for the next
-    // call. No L2 write-back or invalidate is needed.
+    // Fused merge. Partials are stored lane-major per (work unit, row group)
+    // (each store instruction writes 64 lanes x 16 bytes contiguously) with
+    // device-coherent stores (sc1: written through the XCD's L2), then the
+    // wave drains its stores and counts its arrival. The last partition of the
+    // unit to arrive reads all partials back with device-coherent loads,
+    // combines them (exact log-sum-exp merge, one online pass over groups of
+    // four partitions whose loads are issued together) and resets the counter
+    // for the next call. No L2 write-back or invalidate is needed.
     constexpr int kChunks = S::kE;  // 16-byte chunks per lane: 4*E floats
     const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * units_per_head + ui;
     const size_t part_stride = static_cast<size_t>(kChunks) * 64 * 16;
-    char* ob = reinterpret_cast<char*>(a.ws_o) + unit * a.num_parts * part_stride;
-    char* lb = reinterpret_cast<char*>(a.ws_lse) + unit * a.num_parts * 64;
-    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(ob, static_cast<int>(nparts * part_stride));
-    const __amdgpu_buffer_rsrc_t rl = tile_rsrc(lb, nparts * 64);
+    auto rsrc_o = [&](int rg) {
+      char* ob = reinterpret_cast<char*>(a.ws_o) + (unit * kR + rg) * a.num_parts * part_stride;
+      return tile_rsrc(ob, static_cast<int>(nparts * part_stride));
+    };
+    auto rsrc_l = [&](int rg) {
+      char* lb = reinterpret_cast<char*>(a.ws_lse) + (unit * kR + rg) * a.num_parts * 64;
+      return tile_rsrc(lb, nparts * 64);
+    };
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      float v[4];
+    for (int rg = 0; rg < kR; ++rg) {
+      const __amdgpu_buffer_rsrc_t ro = rsrc_o(rg);
+      const __amdgpu_buffer_rsrc_t rl = rsrc_l(rg);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = 4 * k + e;  // value index i * E + mt
-        v[e] = acc[idx % S::kE][idx / S::kE] * inv;
+      for (int k = 0; k < kChunks; ++k) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * k + e;  // value index i * E + mt
+          v[e] = acc[rg][idx % S::kE][idx / S::kE] * inv[rg];
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                     __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                               ro, (p * kChunks + k) * 1024 + lane * 16, 0, kCacheDeviceCoherent);
       }
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                   __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                             ro, (p * kChunks + k) * 1024 + lane * 16, 0, kCacheDeviceCoherent);
+      if (q4 == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run[rg] + __builtin_amdgcn_logf(l_tot[rg])), rl,
+                                              p * 64 + ln * 4, 0, kCacheDeviceCoherent);
     }
-    if (q4 == 0)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run + __builtin_amdgcn_logf(l_tot)), rl,
-                                            p * 64 + ln * 4, 0, kCacheDeviceCoherent);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);  // every store above has completed
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     int32_t* ctr = a.counters + unit;
     int prev = 0;
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0 is always active here (head 0 of the group)
+    prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0 is active here (the unit's first row is real)
     if (prev != nparts - 1) return;
 #pragma unroll
-    for (int mt = 0; mt < S::kE; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float M = kNegInf, L = 0.f;
-    for (int pp0 = 0; pp0 < nparts; pp0 += 4) {
-      float ls[4];
-      u32x4 ov[4][kChunks];
+    for (int rg = 0; rg < kR; ++rg) {
+      const __amdgpu_buffer_rsrc_t ro = rsrc_o(rg);
+      const __amdgpu_buffer_rsrc_t rl = rsrc_l(rg);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {  // past the last partition these read as zero
-        ls[u] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rl, (pp0 + u) * 64 + ln * 4, 0, kCacheDeviceCoherent));
+      for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float M = kNegInf, L = 0.f;
+      for (int pp0 = 0; pp0 < nparts; pp0 += 4) {
+        float ls[4];
+        u32x4 ov[4][kChunks];
 #pragma unroll
-        for (int k = 0; k < kChunks; ++k) {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b128(ro, ((pp0 + u) * kChunks + k) * 1024 + lane * 16, 0,
-                                                               kCacheDeviceCoherent);
-          ov[u][k] = u32x4{x[0], x[1], x[2], x[3]};
+        for (int u = 0; u < 4; ++u) {  // past the last partition these read as zero
+          ls[u] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rl, (pp0 + u) * 64 + ln * 4, 0, kCacheDeviceCoherent));
+#pragma unroll
+          for (int k = 0; k < kChunks; ++k) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(ro, ((pp0 + u) * kChunks + k) * 1024 + lane * 16, 0,
+                                                                 kCacheDeviceCoherent);
+            ov[u][k] = u32x4{x[0], x[1], x[2], x[3]};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ls[u] = pp0 + u < nparts ? ls[u] : kNegInf;
+        const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
+        const float r = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+        M = m_new;
+        L *= r;
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __builtin_amdgcn_exp2f(ls[u] - M);  // 0 past the last partition
+          L += w;
+#pragma unroll
+          for (int k = 0; k < kChunks; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int idx = 4 * k + e;
+              acc[rg][idx % S::kE][idx / S::kE] += w * __uint_as_float(ov[u][k][e]);
+            }
         }
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ls[u] = pp0 + u < nparts ? ls[u] : kNegInf;
-      const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
-      const float r = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
-      M = m_new;
-      L *= r;
-#pragma unroll
-      for (int mt = 0; mt < S::kE; ++mt) acc[mt] *= r;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = __builtin_amdgcn_exp2f(ls[u] - M);  // 0 past the last partition
-        L += w;
-#pragma unroll
-        for (int k = 0; k < kChunks; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int idx = 4 * k + e;
-            acc[idx % S::kE][idx / S::kE] += w * __uint_as_float(ov[u][k][e]);
-          }
-      }
+      write_out(rg, 1.0f / L);
     }
-    write_out(1.0f / L);
     if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1158,9 +1213,10 @@ StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   const int64_t groups = ceil_div64(num_heads / num_kv_heads, 16);
   return merge_layout(static_cast<int64_t>(num_seqs) * num_kv_heads * groups, head_dim, parts);
 }
-// query tiles per (sequence, KV head) for a chunk of up to max_q_len tokens
-int64_t prefill_q_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len) {
-  return ceil_div64(static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads), kTile);
+// query tiles (kR groups of 16 rows each) per (sequence, KV head) for a chunk
+// of up to max_q_len tokens
+int64_t prefill_q_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len, int kR) {
+  return ceil_div64(static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads), kTile * kR);
 }
 
 // Validate, fill DecodeArgs and launch the requested phases. Pointers the
@@ -1282,7 +1338,8 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   if (!q || !k_cache || !v_cache || !block_tables || !q_start || !context_lens || !out) return PKV_EINVAL;
   if (fp8 && (!k_scales || !v_scales)) return PKV_EINVAL;
   if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;
-  const int64_t qt = prefill_q_tiles(num_heads, num_kv_heads, max_q_len);
+  const int kR = prefill_row_groups(dtype);
+  const int64_t qt = prefill_q_tiles(num_heads, num_kv_heads, max_q_len, kR);
   if (qt * num_kv_heads > 65535 || num_seqs > 65535) return PKV_EINVAL;
   DecodeArgs a{};
   a.q = static_cast<const char*>(q);
@@ -1315,7 +1372,7 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   a.k_scales = reinterpret_cast<const char*>(k_scales);
   a.v_scales = reinterpret_cast<const char*>(v_scales);
   if (a.num_parts > 1) {
-    const StepLayout L = merge_layout(units, head_dim, a.num_parts);
+    const StepLayout L = merge_layout(units * kR, head_dim, a.num_parts);  // one slot per row group
     if (!workspace || workspace_bytes < L.total()) return PKV_ESMALL;
     char* ws = static_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(ws);
@@ -1522,15 +1579,21 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_q_len <= 0 ||
       max_blocks_per_seq <= 0 || num_heads % num_kv_heads != 0 || !valid_block_size(block_size))
     return 0;
-  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads *
-                        prefill_q_tiles(num_heads, num_kv_heads, max_q_len);
-  const int32_t m = block_size / kTile;
-  int32_t pb = partition_blocks;
-  if (pb <= 0) {
-    const int32_t tiles = auto_partition_tiles_for_units(units, static_cast<int64_t>(max_blocks_per_seq) * m);
-    pb = tiles / m > 0 ? tiles / m : 1;
+  // enough for either row-group count (the launch's dtype decides which)
+  size_t need = 0;
+  for (int kR : {2, 4}) {
+    const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                          prefill_q_tiles(num_heads, num_kv_heads, max_q_len, kR);
+    const int32_t m = block_size / kTile;
+    int32_t pb = partition_blocks;
+    if (pb <= 0) {
+      const int32_t tiles = auto_partition_tiles_for_units(units, static_cast<int64_t>(max_blocks_per_seq) * m);
+      pb = tiles / m > 0 ? tiles / m : 1;
+    }
+    const size_t bytes = merge_layout(units * kR, head_dim, ceil_div64(max_blocks_per_seq, pb)).total();
+    need = bytes > need ? bytes : need;
   }
-  return merge_layout(units, head_dim, ceil_div64(max_blocks_per_seq, pb)).total();
+  return need;
 }
 
 pkv_status pkv_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
