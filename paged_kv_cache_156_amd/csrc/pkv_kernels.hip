@@ -67,6 +67,9 @@ constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two til
 #ifndef PKV_AHEAD_FP8
 #define PKV_AHEAD_FP8 2
 #endif
+#ifndef PKV_AHEAD_PREFILL
+#define PKV_AHEAD_PREFILL 2
+#endif
 #ifndef PKV_RING_ROTATIONS
 #define PKV_RING_ROTATIONS 3
 #endif
@@ -791,7 +794,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   // are issued unconditionally (past the partition end they fetch nothing, see
   // load_block) so that every iteration issues the same loads and the compiler
   // can wait on a precise outstanding-load count.
-  constexpr int kAhead = kFp8 ? PKV_AHEAD_FP8 : (sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT);
+  constexpr int kAhead = kPrefill ? (sizeof(T) == 2 ? PKV_AHEAD_PREFILL : PKV_AHEAD_32BIT)
+                                  : (kFp8 ? PKV_AHEAD_FP8 : (sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT));
   constexpr int kRing = kAhead + 1;
   R ring[kRing];
   int ring_rows[kRing];
