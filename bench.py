@@ -277,8 +277,9 @@ def main():
     ap.add_argument("--mode", choices=("fused", "split"), default="fused",
                     help="fused: one decode_step launch per layer (append + attention + merge); "
                          "split: kv_append, decode_partitions, decode_merge")
-    ap.add_argument("--kv", choices=("native", "fp8"), default="native",
-                    help="native: K/V cached in the configuration's dtype; fp8: E4M3 codes + fp32 per-row scales")
+    ap.add_argument("--kv", choices=("native", "fp8", "int8"), default="native",
+                    help="native: K/V cached in the configuration's dtype; fp8: E4M3 codes + fp32 per-row scales; "
+                         "int8: INT8 codes + fp32 per-row scales")
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="cache block layout: HND [NB, Hkv, bs, D] (default) or NHD [NB, bs, Hkv, D]")
     ap.add_argument("--block-size", type=int, default=0, help="tokens per cache block (0 = the configuration's, 16)")
@@ -325,7 +326,8 @@ def main():
     asg, slots, pool_stats = pool_assignment(cfg, lens, pkv, wl)
     log(f"block pool: {pool_stats}")
     t0 = time.time()
-    fp8 = args.kv == "fp8"
+    fp8 = args.kv in ("fp8", "int8")  # 8-bit codes with per-row scales
+    fmt = "int8" if args.kv == "int8" else "e4m3"
     if fp8:
         wkd = wl.make_device_workload_fp8(cfg, dev, layers=L, context_lens=lens, assignment=asg)
     else:
@@ -367,13 +369,13 @@ def main():
                 if fused:
                     pkv.decode_step_fp8(wkd.q[l], wkd.k_new[l], wkd.v_new[l], wkd.k_codes[l], wkd.v_codes[l],
                                         wkd.k_scales[l], wkd.v_scales[l], wkd.block_tables, wkd.context_lens_dev,
-                                        cfg.scale, outs[l], ws, pb, layout=lay)
+                                        cfg.scale, outs[l], ws, pb, layout=lay, fmt=fmt)
                 else:
                     pkv.kv_append_fp8(wkd.k_new[l], wkd.v_new[l], slots_d, wkd.k_codes[l], wkd.v_codes[l],
-                                      wkd.k_scales[l], wkd.v_scales[l], layout=lay)
+                                      wkd.k_scales[l], wkd.v_scales[l], layout=lay, fmt=fmt)
                     pkv.paged_decode_attention_fp8(wkd.q[l], wkd.k_codes[l], wkd.v_codes[l], wkd.k_scales[l],
                                                    wkd.v_scales[l], wkd.block_tables, wkd.context_lens_dev,
-                                                   cfg.scale, outs[l], ws, pb, layout=lay)
+                                                   cfg.scale, outs[l], ws, pb, layout=lay, fmt=fmt)
                 if events is not None:
                     events[l][1].record(stream)
                 continue
@@ -440,7 +442,7 @@ def main():
 
     traffic = None
     geom = "" if (lay == "HND" and bs == 16) else f"_{lay.lower()}_bs{bs}"
-    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}{'_fp8' if fp8 else ''}{geom}_{cfg.name}_traffic.json")
+    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}{'_' + args.kv if fp8 else ''}{geom}_{cfg.name}_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
@@ -479,7 +481,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (f"e4m3 K/V + f32 row scales, {cfg.dtype} q/out" if fp8 else cfg.dtype),
+        "dtype": (f"{fmt} K/V + f32 row scales, {cfg.dtype} q/out" if fp8 else cfg.dtype),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: batch {B}, context {'ragged' if cfg.context_len_range else int(lens[0])}, "
                                f"{Hq} query / {Hkv} KV heads, head_dim {D}, {lay} blocks of {bs}, {L} layers, one decode step "

@@ -281,6 +281,45 @@ pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_n
                                void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
 
 /*
+ * INT8 KV cache: the same calls over signed 8-bit integer codes. The pages
+ * name INT8 beside FP8 for KV storage ("KV Cache and Inference Optimization",
+ * section "KV quantization"); the scaling rule is the FP8 one with 127 as the
+ * largest code:
+ *   - codes: int8 in the cache layout, scales fp32 as for FP8;
+ *   - value attended over = code * scale;
+ *   - quantization of a new row x (fp32): amax = max |x|, scale = amax / 127,
+ *     inv = 127 / amax (1 and 1 when amax == 0), code = x * inv rounded to the
+ *     nearest integer (ties to even), clamped to +-127 (-128 is never produced).
+ * Queries and outputs are bf16 or fp16 (f32 is EUNSUPPORTED); codes convert
+ * exactly to those types. Arguments, layouts and errors as the _fp8 calls.
+ */
+pkv_status pkv_kv_append_int8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                              void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                              pkv_dtype dtype, void* stream);
+pkv_status pkv_paged_decode_attention_int8(const void* q, const void* k_cache, const void* v_cache,
+                                           const float* k_scales, const float* v_scales,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                                           pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                           int32_t partition_blocks, void* stream);
+pkv_status pkv_decode_step_int8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                float* k_scales, float* v_scales, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                pkv_layout layout, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream);
+pkv_status pkv_prefill_attention_int8(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                                      const float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* q_start, int32_t max_q_len, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale,
+                                      void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      int32_t partition_blocks, void* stream);
+
+/*
  * pkv_prefill_attention -- chunked prefill: causal attention of a chunk of
  * new query tokens per sequence over the paged cache. Prefill processes many
  * query positions at once as matrix products ("KV Cache and Inference

@@ -49,4 +49,8 @@ from .quant import (  # noqa: F401
     e4m3_encode,
     quantize_rows,
     dequantize_rows,
+    quantize_rows_int8,
+    int8_decode,
+    decode_codes,
+    quantize_rows_fmt,
 )

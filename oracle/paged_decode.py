@@ -170,42 +170,46 @@ def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new
 # (NHD: [NB, bs, Hkv, D] and [NB, bs, Hkv])
 # ---------------------------------------------------------------------------
 def gather_sequence_fp8(codes: np.ndarray, scales: np.ndarray, table_row: Sequence[int], n: int, kv_head: int,
-                        block_size: int, layout: str = "HND") -> np.ndarray:
-    """Contiguous float64 [n, D] of decode(code) * scale for one KV head."""
-    from .quant import e4m3_decode
+                        block_size: int, layout: str = "HND", fmt: str = "e4m3") -> np.ndarray:
+    """Contiguous float64 [n, D] of decode(code) * scale for one KV head
+    (codes in format ``fmt``: "e4m3" or "int8")."""
+    from .quant import decode_codes
     out = np.empty((n, codes.shape[-1]), dtype=np.float64)
     for i in range(n):
         _, off, pb, _ = slot_address(i, table_row, block_size)
-        out[i] = e4m3_decode(_at(codes, pb, off, kv_head, layout)) * np.float64(_at(scales, pb, off, kv_head, layout))
+        out[i] = decode_codes(_at(codes, pb, off, kv_head, layout), fmt) * np.float64(_at(scales, pb, off, kv_head,
+                                                                                          layout))
     return out
 
 
 def decode_attention_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray,
                          v_scales: np.ndarray, block_tables: np.ndarray, context_lens: Sequence[int], scale: float,
                          num_kv_heads: int, block_size: int, q_dtype: str,
-                         seqs: Optional[Sequence[int]] = None, layout: str = "HND") -> np.ndarray:
-    """Decode attention over FP8 caches: the same softmax attention, over the
-    dequantized cached values."""
+                         seqs: Optional[Sequence[int]] = None, layout: str = "HND",
+                         fmt: str = "e4m3") -> np.ndarray:
+    """Decode attention over 8-bit caches (FP8 E4M3 or INT8 codes): the same
+    softmax attention, over the dequantized cached values."""
     B, Hq, D = q.shape
     out = np.full((B, Hq, D), np.nan, dtype=np.float64)
     for b in (range(B) if seqs is None else seqs):
         n = int(context_lens[b])
         row = block_tables[b]
         out[b] = _attend_heads(upcast(q[b], q_dtype),
-                               lambda j: gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size, layout),
-                               lambda j: gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size, layout),
+                               lambda j: gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size, layout, fmt),
+                               lambda j: gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size, layout, fmt),
                                num_kv_heads, n, scale)
     return out
 
 
 def kv_append_fp8(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray, v_scales: np.ndarray,
                   k_new: np.ndarray, v_new: np.ndarray, slots: Sequence[int], block_size: int, in_dtype: str,
-                  layout: str = "HND") -> None:
+                  layout: str = "HND", fmt: str = "e4m3") -> None:
     """Quantize each new token's K and V rows (one scale per KV head row, see
-    ``oracle.quant``) and write codes and scales into the slot, in place."""
-    from .quant import quantize_rows
-    kq, ks = quantize_rows(upcast(k_new, in_dtype).astype(np.float32))
-    vq, vs = quantize_rows(upcast(v_new, in_dtype).astype(np.float32))
+    ``oracle.quant``; format ``fmt``) and write codes (raw bytes) and scales
+    into the slot, in place."""
+    from .quant import quantize_rows_fmt
+    kq, ks = quantize_rows_fmt(upcast(k_new, in_dtype).astype(np.float32), fmt)
+    vq, vs = quantize_rows_fmt(upcast(v_new, in_dtype).astype(np.float32), fmt)
     for i, s in enumerate(slots):
         s = int(s)
         if s < 0:

@@ -46,8 +46,9 @@ def prefill_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, b
 def prefill_attention_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray,
                           v_scales: np.ndarray, block_tables: np.ndarray, q_start: Sequence[int],
                           context_lens: Sequence[int], scale: float, num_kv_heads: int, block_size: int,
-                          q_dtype: str, layout: str = "HND") -> np.ndarray:
-    """As ``prefill_attention`` over FP8 caches (values decode(code) * scale)."""
+                          q_dtype: str, layout: str = "HND", fmt: str = "e4m3") -> np.ndarray:
+    """As ``prefill_attention`` over 8-bit caches (values decode(code) * scale,
+    codes in format ``fmt``)."""
     out = np.zeros(q.shape, dtype=np.float64)
     for b in range(len(context_lens)):
         q0, q1 = int(q_start[b]), int(q_start[b + 1])
@@ -56,8 +57,8 @@ def prefill_attention_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarra
         if q_len <= 0:
             continue
         row = block_tables[b]
-        K = [gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size, layout) for j in range(num_kv_heads)]
-        V = [gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size, layout) for j in range(num_kv_heads)]
+        K = [gather_sequence_fp8(k_codes, k_scales, row, n, j, block_size, layout, fmt) for j in range(num_kv_heads)]
+        V = [gather_sequence_fp8(v_codes, v_scales, row, n, j, block_size, layout, fmt) for j in range(num_kv_heads)]
         for i in range(q_len):
             m = n - q_len + i + 1
             out[q0 + i] = _attend_heads(upcast(q[q0 + i], q_dtype), lambda j: K[j][:m], lambda j: V[j][:m],

@@ -1,4 +1,4 @@
-"""FP8 (OCP E4M3) KV-cache quantization, as plain NumPy.
+"""FP8 (OCP E4M3) and INT8 KV-cache quantization, as plain NumPy.
 
 Test infrastructure only (see the package docstring).
 
@@ -18,6 +18,11 @@ same precision:
     value that rounds to zero gives -0);
   * the cached value a kernel attends over is decode(code) * scale (exact in
     float64).
+
+INT8 (the page's other named option) follows the same rule with 127 as the
+largest code: scale = amax / 127, inv = 127 / amax (float32; amax = 0 gives 1
+and 1), code = float32(x * inv) rounded to the nearest integer (ties to even),
+clamped to [-127, 127]; the value is code * scale.
 """
 from __future__ import annotations
 
@@ -85,3 +90,45 @@ def quantize_rows(x: np.ndarray):
 def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """float64 values decode(code) * scale."""
     return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+INT8_MAX = 127.0
+
+
+def quantize_rows_int8(x: np.ndarray):
+    """INT8 codes (int8, x's shape) and float32 scales of the last axis of ``x``,
+    following the module docstring step by step in float32."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1).astype(np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1), safe / np.float32(INT8_MAX)).astype(np.float32)
+    inv = np.where(zero, np.float32(1), np.float32(INT8_MAX) / safe).astype(np.float32)
+    y = (x * inv[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(y.astype(np.float64)), -INT8_MAX, INT8_MAX).astype(np.int8)
+    return codes, scale
+
+
+def int8_decode(codes: np.ndarray) -> np.ndarray:
+    """float64 values of int8 codes stored as raw bytes (uint8) or int8."""
+    return np.asarray(codes).view(np.int8).astype(np.float64) if np.asarray(codes).dtype == np.uint8 \
+        else np.asarray(codes, dtype=np.int8).astype(np.float64)
+
+
+def decode_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """float64 values of 8-bit codes in format ``fmt`` ("e4m3" or "int8")."""
+    if fmt == "e4m3":
+        return e4m3_decode(codes)
+    if fmt == "int8":
+        return int8_decode(codes)
+    raise ValueError(f"unknown code format {fmt!r}")
+
+
+def quantize_rows_fmt(x: np.ndarray, fmt: str):
+    """(codes as raw uint8 bytes, float32 scales) in format ``fmt``."""
+    if fmt == "e4m3":
+        return quantize_rows(x)
+    if fmt == "int8":
+        c, s = quantize_rows_int8(x)
+        return c.view(np.uint8), s
+    raise ValueError(f"unknown code format {fmt!r}")

@@ -62,11 +62,18 @@ SIGNATURES = [
                                               _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_decode_step_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_kv_append_int8", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    ("pkv_paged_decode_attention_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_decode_step_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_prefill_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     ("pkv_prefill_attention", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_prefill_attention_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_prefill_attention_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_copy_blocks", _i32, [_c.POINTER(_vp), _pi64, _i32, _i32, _vp, _i32, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
@@ -457,8 +464,19 @@ def _fp8_cache(codes, scales, name):
     return _dev(codes, name), _dev(scales, name + " scales")
 
 
-def kv_append_fp8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, stream=None, layout: str = "HND"):
-    """Quantize new K/V rows ([T, Hkv, D], f32/f16/bf16) into the FP8 caches."""
+CODE_FORMATS = ("e4m3", "int8")
+
+
+def _q8(name: str, fmt: str) -> str:
+    if fmt not in CODE_FORMATS:
+        raise ValueError(f"code format must be one of {CODE_FORMATS}, got {fmt!r}")
+    return name + ("_fp8" if fmt == "e4m3" else "_int8")
+
+
+def kv_append_fp8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, stream=None, layout: str = "HND",
+                  fmt: str = "e4m3"):
+    """Quantize new K/V rows ([T, Hkv, D], f32/f16/bf16) into 8-bit caches
+    (``fmt`` "e4m3" for FP8 codes, "int8" for INT8 codes)."""
     import torch
     T, Hkv, D = k.shape
     NB, Hkv2, bs, D2 = _geom(k_codes, layout)
@@ -466,10 +484,11 @@ def kv_append_fp8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, stre
         raise ValueError("shape mismatch between k/v and the caches")
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
-    st = load().pkv_kv_append_fp8(_dev(k, "k"), _dev(v, "v", k.dtype), _dev(slot_mapping, "slot_mapping", torch.int64),
-                                  T, kc, vc, ks, vs, NB, Hkv, D, bs, LAYOUT_CODES[layout], _torch_dtype_code(k),
-                                  _stream_ptr(stream))
-    _check(st, "pkv_kv_append_fp8")
+    fn = _q8("pkv_kv_append", fmt)
+    st = getattr(load(), fn)(_dev(k, "k"), _dev(v, "v", k.dtype), _dev(slot_mapping, "slot_mapping", torch.int64),
+                             T, kc, vc, ks, vs, NB, Hkv, D, bs, LAYOUT_CODES[layout], _torch_dtype_code(k),
+                             _stream_ptr(stream))
+    _check(st, fn)
 
 
 def _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace, layout):
@@ -489,30 +508,33 @@ def _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, works
 
 
 def paged_decode_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, scale: float,
-                               out, workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
+                               out, workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND",
+                               fmt: str = "e4m3"):
     a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace, layout)
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
-    st = load().pkv_paged_decode_attention_fp8(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"],
-                                               a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale),
-                                               a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
-                                               _stream_ptr(stream))
-    _check(st, "pkv_paged_decode_attention_fp8")
+    fn = _q8("pkv_paged_decode_attention", fmt)
+    st = getattr(load(), fn)(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"], a["Hq"], a["Hkv"],
+                             a["D"], a["bs"], a["lay"], a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
+                             int(partition_blocks), _stream_ptr(stream))
+    _check(st, fn)
     return out
 
 
 def decode_step_fp8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
-                    scale: float, out, workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND"):
+                    scale: float, out, workspace=None, partition_blocks: int = 0, stream=None, layout: str = "HND",
+                    fmt: str = "e4m3"):
     a = _fp8_decode_args(q, k_codes, v_codes, block_tables, context_lens, out, workspace, layout)
     if tuple(k_new.shape) != (a["B"], a["Hkv"], a["D"]) or tuple(v_new.shape) != tuple(k_new.shape):
         raise ValueError("k_new / v_new must be [B, Hkv, D]")
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
-    st = load().pkv_decode_step_fp8(_dev(q, "q"), _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype), kc,
-                                    vc, ks, vs, a["t"], a["mb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
-                                    a["lay"], a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"],
-                                    int(partition_blocks), _stream_ptr(stream))
-    _check(st, "pkv_decode_step_fp8")
+    fn = _q8("pkv_decode_step", fmt)
+    st = getattr(load(), fn)(_dev(q, "q"), _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype), kc, vc, ks,
+                             vs, a["t"], a["mb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"],
+                             a["NB"], float(scale), a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
+                             _stream_ptr(stream))
+    _check(st, fn)
     return out
 
 
@@ -569,15 +591,15 @@ def prefill_attention(q, k_cache, v_cache, block_tables, q_start, max_q_len, con
 
 def prefill_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, q_start, max_q_len, context_lens,
                           scale: float, out, workspace=None, partition_blocks: int = 0, stream=None,
-                          layout: str = "HND"):
+                          layout: str = "HND", fmt: str = "e4m3"):
     a = _prefill_args(q, q_start, max_q_len, k_codes, block_tables, context_lens, out, workspace, layout)
     if tuple(v_codes.shape) != tuple(k_codes.shape):
         raise ValueError("shape mismatch")
     kc, ks = _fp8_cache(k_codes, k_scales, "k_cache")
     vc, vs = _fp8_cache(v_codes, v_scales, "v_cache")
-    st = load().pkv_prefill_attention_fp8(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["qs"], a["mq"], a["lens"],
-                                          a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale),
-                                          a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
-                                          _stream_ptr(stream))
-    _check(st, "pkv_prefill_attention_fp8")
+    fn = _q8("pkv_prefill_attention", fmt)
+    st = getattr(load(), fn)(_dev(q, "q"), kc, vc, ks, vs, a["t"], a["mb"], a["qs"], a["mq"], a["lens"], a["B"],
+                             a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], float(scale), a["out"], a["code"],
+                             a["ws"], a["wsb"], int(partition_blocks), _stream_ptr(stream))
+    _check(st, fn)
     return out

@@ -288,40 +288,71 @@ __device__ __forceinline__ u32x2 fp8x4_to_16<_Float16>(unsigned w) {
                to_bits16<_Float16>(hi[0]) | (to_bits16<_Float16>(hi[1]) << 16)};
 }
 
-// FP8 raw block -> the 16-bit operand registers of the MFMA pipeline
-template <typename T, int D>
-__device__ __forceinline__ void fp8_to_16(const Fp8Regs<D>& r, BlockRegs<T, D>& o) {
+// four INT8 codes (one dword, lowest byte first, two's complement) -> two
+// dwords of 16-bit values, exactly (|code| <= 127 fits bf16 and fp16)
+template <typename T>
+__device__ __forceinline__ u32x2 int8x4_to_16(unsigned w) {
+  const int s = static_cast<int>(w);
+  const float f0 = static_cast<float>((s << 24) >> 24), f1 = static_cast<float>((s << 16) >> 24);
+  const float f2 = static_cast<float>((s << 8) >> 24), f3 = static_cast<float>(s >> 24);
+  return u32x2{to_bits16<T>(f0) | (to_bits16<T>(f1) << 16), to_bits16<T>(f2) | (to_bits16<T>(f3) << 16)};
+}
+
+// Cache code formats: kQ = 0 (no codes: the cache holds T), kQFp8 (OCP E4M3),
+// kQInt8 (signed 8-bit integers). Both code formats keep one fp32 scale per
+// token row of one KV head.
+constexpr int kQFp8 = 1;
+constexpr int kQInt8 = 2;
+template <int kQ, typename T>
+__device__ __forceinline__ u32x2 codes4_to_16(unsigned w) {
+  if constexpr (kQ == kQInt8) return int8x4_to_16<T>(w);
+  else return fp8x4_to_16<T>(w);
+}
+
+// 8-bit raw block -> the 16-bit operand registers of the MFMA pipeline
+template <int kQ, typename T, int D>
+__device__ __forceinline__ void codes_to_16(const Fp8Regs<D>& r, BlockRegs<T, D>& o) {
 #pragma unroll
-  for (int c = 0; c < Shape<T, D>::kNK; ++c) {  // chunk c = fp8 bytes 8c..8c+7 of the lane's slice
-    const u32x2 a = fp8x4_to_16<T>(r.k[c >> 1][(c & 1) * 2]);
-    const u32x2 b = fp8x4_to_16<T>(r.k[c >> 1][(c & 1) * 2 + 1]);
+  for (int c = 0; c < Shape<T, D>::kNK; ++c) {  // chunk c = code bytes 8c..8c+7 of the lane's slice
+    const u32x2 a = codes4_to_16<kQ, T>(r.k[c >> 1][(c & 1) * 2]);
+    const u32x2 b = codes4_to_16<kQ, T>(r.k[c >> 1][(c & 1) * 2 + 1]);
     o.k[c] = u32x4{a[0], a[1], b[0], b[1]};
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int w = 0; w < D / 64; ++w) {
-      const u32x2 a = fp8x4_to_16<T>(r.v[i][w]);
+      const u32x2 a = codes4_to_16<kQ, T>(r.v[i][w]);
       o.v[i][2 * w] = a[0];
       o.v[i][2 * w + 1] = a[1];
     }
 }
 
-// Quantize values of one token row to E4M3 given the row's absolute maximum:
-// scale = amax / 448, inv = 448 / amax (both fp32; amax == 0 -> 1, 1), and each
-// code is the nearest E4M3 value of x * inv (ties to even, clamped to +-448).
+// Quantize values of one token row given the row's absolute maximum and the
+// format's largest code Q (448 for E4M3, 127 for INT8): scale = amax / Q,
+// inv = Q / amax (both fp32; amax == 0 -> 1, 1), and each code is the nearest
+// code to x * inv (ties to even, clamped to +-Q).
 struct RowQuant {
   float scale, inv;
 };
+template <int kQ>
+constexpr float kQMax = kQ == kQInt8 ? 127.0f : 448.0f;
+template <int kQ>
 __device__ __forceinline__ RowQuant row_quant(float amax) {
   if (amax == 0.f) return {1.f, 1.f};
-  return {amax / 448.0f, 448.0f / amax};
+  return {amax / kQMax<kQ>, kQMax<kQ> / amax};
 }
+template <int kQ>
 __device__ __forceinline__ unsigned quant4(float x0, float x1, float x2, float x3, float inv) {
-  auto c = [inv](float x) { return fminf(fmaxf(x * inv, -448.0f), 448.0f); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x0), c(x1), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x2), c(x3), w, true);
-  return static_cast<unsigned>(w);
+  auto c = [inv](float x) { return fminf(fmaxf(x * inv, -kQMax<kQ>), kQMax<kQ>); };
+  if constexpr (kQ == kQInt8) {
+    auto b = [&](float x) { return static_cast<unsigned>(static_cast<int>(__builtin_rintf(c(x)))) & 0xffu; };
+    return b(x0) | (b(x1) << 8) | (b(x2) << 16) | (b(x3) << 24);
+  } else {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x0), c(x1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x2), c(x3), w, true);
+    return static_cast<unsigned>(w);
+  }
 }
 
 template <typename T>
@@ -339,7 +370,7 @@ __device__ __forceinline__ float elt_to_float<_Float16>(const char* p) {
   return from_bits16<_Float16>(*reinterpret_cast<const unsigned short*>(p));
 }
 
-template <typename T, int D, bool kFp8>
+template <typename T, int D, bool kCodes>
 struct RegsOf {
   using type = BlockRegs<T, D>;
 };
@@ -422,8 +453,9 @@ constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 
 // i sits at position n - q_len + i and attends to positions 0..n - q_len + i
 // (causal attention, "Understanding KV Cache" §1.2; prefill as a matrix
 // product over many query positions, "KV Cache and Inference Optimization").
-template <typename T, int D, int kMode, bool kFp8, bool kNHD>
+template <typename T, int D, int kMode, int kQ, bool kNHD>
 __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+  constexpr bool kFp8 = kQ != 0;  // the caches hold 8-bit codes with per-row scales
   constexpr bool kStep = kMode == kModeStep;
   constexpr bool kPrefill = kMode == kModePrefill;
   using S = Shape<T, D>;
@@ -552,14 +584,14 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       for (int e = 0; e < D / 4; ++e) am = fmaxf(am, fabsf(kx[e]));
       am = fmaxf(am, xor_shuffle(am, 16));
       am = fmaxf(am, xor_shuffle(am, 32));
-      const RowQuant kq = row_quant(am);
+      const RowQuant kq = row_quant<kQ>(am);
       ks_new = kq.scale;
 #pragma unroll
       for (int c = 0; c < D / 64; ++c) {
         unsigned w[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d)
-          w[d] = quant4(kx[16 * c + 4 * d], kx[16 * c + 4 * d + 1], kx[16 * c + 4 * d + 2], kx[16 * c + 4 * d + 3],
+          w[d] = quant4<kQ>(kx[16 * c + 4 * d], kx[16 * c + 4 * d + 1], kx[16 * c + 4 * d + 2], kx[16 * c + 4 * d + 3],
                         kq.inv);
         kn8[c] = u32x4{w[0], w[1], w[2], w[3]};
       }
@@ -572,10 +604,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       for (int e = 0; e < D / 16; ++e) vm = fmaxf(vm, fabsf(vx[e]));
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) vm = fmaxf(vm, xor_shuffle(vm, m));
-      const RowQuant vq = row_quant(vm);
+      const RowQuant vq = row_quant<kQ>(vm);
       vs_new = vq.scale;
 #pragma unroll
-      for (int w = 0; w < D / 64; ++w) vn8[w] = quant4(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq.inv);
+      for (int w = 0; w < D / 64; ++w)
+        vn8[w] = quant4<kQ>(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq.inv);
       // write codes and scales into the slot (head group 0 only)
       const int r0 = tile_r0(new_t);
       if (hg == 0 && r0 >= 0) {
@@ -695,7 +728,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     BlockRegs<T, D> conv;
     BlockRegs<T, D>* rp;
     if constexpr (kFp8) {
-      fp8_to_16<T, D>(rr, conv);
+      codes_to_16<kQ, T, D>(rr, conv);
       rp = &conv;
     } else {
       rp = &rr;
@@ -1077,8 +1110,8 @@ __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k,
 // FP8 append: one wave per (token, KV head, K or V) quantizes the row (scale =
 // row amax / 448) and writes codes and scale into the slot
 // ---------------------------------------------------------------------------
-template <typename Tin, int D>
-__global__ __launch_bounds__(64) void append_fp8_kernel(const char* __restrict__ k, const char* __restrict__ v,
+template <typename Tin, int D, int kQ>
+__global__ __launch_bounds__(64) void append_q8_kernel(const char* __restrict__ k, const char* __restrict__ v,
                                                         const int64_t* __restrict__ slots, char* k_cache,
                                                         char* v_cache, float* k_scales, float* v_scales,
                                                         int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
@@ -1100,12 +1133,12 @@ __global__ __launch_bounds__(64) void append_fp8_kernel(const char* __restrict__
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, xor_shuffle(am, m));
-  const RowQuant rq = row_quant(am);
+  const RowQuant rq = row_quant<kQ>(am);
   const int64_t pb = slot / block_size;
   const int64_t off = slot - pb * block_size;
   const int64_t row = nhd ? (pb * block_size + off) * num_kv_heads + j : (pb * num_kv_heads + j) * block_size + off;
   char* dst = (is_v ? v_cache : k_cache) + row * D + lane * kPer;
-  const unsigned codes = quant4(x[0], kPer > 1 ? x[kPer - 1] : 0.f, 0.f, 0.f, rq.inv);
+  const unsigned codes = quant4<kQ>(x[0], kPer > 1 ? x[kPer - 1] : 0.f, 0.f, 0.f, rq.inv);
   if constexpr (kPer == 2) *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(codes & 0xffffu);
   else *reinterpret_cast<unsigned char*>(dst) = static_cast<unsigned char>(codes & 0xffu);
   if (lane == 0) (is_v ? v_scales : k_scales)[row] = rq.scale;
@@ -1160,16 +1193,16 @@ int32_t partition_blocks_for(int32_t num_seqs, int32_t num_heads, int32_t num_kv
 
 enum Phase : unsigned { kPartitions = 1u, kMerge = 2u, kFusedStep = 4u };
 
-template <typename T, int D, bool kFp8, bool kNHD>
+template <typename T, int D, int kQ, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
   if (phases & kFusedStep) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
   if (phases & kPartitions) {
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kFp8, kNHD>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kQ, kNHD>), grid, dim3(64), 0, stream, a);
   }
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
@@ -1179,19 +1212,44 @@ pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases,
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-template <typename T, int D, bool kFp8 = false>
+template <typename T, int D, int kQ = 0>
 pkv_status launch_layout(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream, bool nhd) {
-  return nhd ? launch_decode<T, D, kFp8, true>(a, num_seqs, phases, stream)
-             : launch_decode<T, D, kFp8, false>(a, num_seqs, phases, stream);
+  return nhd ? launch_decode<T, D, kQ, true>(a, num_seqs, phases, stream)
+             : launch_decode<T, D, kQ, false>(a, num_seqs, phases, stream);
 }
 
-template <typename T, int D, bool kFp8 = false>
+template <typename T, int D, int kQ = 0>
 pkv_status launch_prefill(const DecodeArgs& a, int32_t num_seqs, hipStream_t stream, bool nhd) {
   dim3 grid(a.num_parts, a.num_kv_heads * a.q_tiles, num_seqs);
-  if (nhd) hipLaunchKernelGGL((decode_partition_kernel<T, D, kModePrefill, kFp8, true>), grid, dim3(64), 0, stream, a);
-  else hipLaunchKernelGGL((decode_partition_kernel<T, D, kModePrefill, kFp8, false>), grid, dim3(64), 0, stream, a);
+  if (nhd) hipLaunchKernelGGL((decode_partition_kernel<T, D, kModePrefill, kQ, true>), grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL((decode_partition_kernel<T, D, kModePrefill, kQ, false>), grid, dim3(64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
+
+// 16-bit query type x head size x code format (kQFp8 / kQInt8) for 8-bit caches
+template <template <typename, int, int> class L, typename... A>
+pkv_status dispatch_codes(pkv_dtype dtype, int head_dim, int q, A&&... args) {
+  if (dtype == PKV_BF16) {
+    if (q == kQInt8)
+      return head_dim == 128 ? L<__bf16, 128, kQInt8>::go(args...) : L<__bf16, 64, kQInt8>::go(args...);
+    return head_dim == 128 ? L<__bf16, 128, kQFp8>::go(args...) : L<__bf16, 64, kQFp8>::go(args...);
+  }
+  if (q == kQInt8)
+    return head_dim == 128 ? L<_Float16, 128, kQInt8>::go(args...) : L<_Float16, 64, kQInt8>::go(args...);
+  return head_dim == 128 ? L<_Float16, 128, kQFp8>::go(args...) : L<_Float16, 64, kQFp8>::go(args...);
+}
+template <typename T, int D, int kQ>
+struct LayoutLauncher {
+  static pkv_status go(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t s, bool nhd) {
+    return launch_layout<T, D, kQ>(a, num_seqs, phases, s, nhd);
+  }
+};
+template <typename T, int D, int kQ>
+struct PrefillLauncher {
+  static pkv_status go(const DecodeArgs& a, int32_t num_seqs, hipStream_t s, bool nhd) {
+    return launch_prefill<T, D, kQ>(a, num_seqs, s, nhd);
+  }
+};
 
 size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int64_t parts) {
   if (parts <= 1) return 0;
@@ -1232,7 +1290,8 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
                         size_t workspace_bytes, int32_t partition_blocks, unsigned phases, void* stream,
                         const void* k_new = nullptr,
                         const void* v_new = nullptr, const float* k_scales = nullptr,
-                        const float* v_scales = nullptr, bool fp8 = false) {
+                        const float* v_scales = nullptr, int codes = 0) {
+  const bool fp8 = codes != 0;  // 8-bit codes (E4M3 or INT8) with per-row scales
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
   if ((phases & kPartitions) && num_blocks <= 0) return PKV_EINVAL;
   if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
@@ -1299,13 +1358,7 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool nhd = layout == PKV_NHD;
-  if (fp8) {
-    if (dtype == PKV_BF16)
-      return head_dim == 128 ? launch_layout<__bf16, 128, true>(a, num_seqs, phases, s, nhd)
-                             : launch_layout<__bf16, 64, true>(a, num_seqs, phases, s, nhd);
-    return head_dim == 128 ? launch_layout<_Float16, 128, true>(a, num_seqs, phases, s, nhd)
-                           : launch_layout<_Float16, 64, true>(a, num_seqs, phases, s, nhd);
-  }
+  if (fp8) return dispatch_codes<LayoutLauncher>(dtype, head_dim, codes, a, num_seqs, phases, s, nhd);
   switch (dtype) {
     case PKV_BF16:
       return head_dim == 128 ? launch_layout<__bf16, 128>(a, num_seqs, phases, s, nhd)
@@ -1327,7 +1380,8 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
                          int32_t head_dim, int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale,
                          void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
                          int32_t partition_blocks, void* stream, const float* k_scales, const float* v_scales,
-                         bool fp8) {
+                         int codes) {
+  const bool fp8 = codes != 0;  // 8-bit codes (E4M3 or INT8) with per-row scales
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || max_q_len < 0)
     return PKV_EINVAL;
   if (num_blocks <= 0 || num_heads % num_kv_heads != 0 || elt_bytes(dtype) == 0) return PKV_EINVAL;
@@ -1385,13 +1439,7 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool nhd = layout == PKV_NHD;
-  if (fp8) {
-    if (dtype == PKV_BF16)
-      return head_dim == 128 ? launch_prefill<__bf16, 128, true>(a, num_seqs, s, nhd)
-                             : launch_prefill<__bf16, 64, true>(a, num_seqs, s, nhd);
-    return head_dim == 128 ? launch_prefill<_Float16, 128, true>(a, num_seqs, s, nhd)
-                           : launch_prefill<_Float16, 64, true>(a, num_seqs, s, nhd);
-  }
+  if (fp8) return dispatch_codes<PrefillLauncher>(dtype, head_dim, codes, a, num_seqs, s, nhd);
   switch (dtype) {
     case PKV_BF16:
       return head_dim == 128 ? launch_prefill<__bf16, 128>(a, num_seqs, s, nhd)
@@ -1404,6 +1452,41 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
                              : launch_prefill<float, 64>(a, num_seqs, s, nhd);
   }
   return PKV_EINVAL;
+}
+
+// quantizing append of either code format
+template <int kQ>
+pkv_status append_codes(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                        void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                        pkv_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0) return PKV_EINVAL;
+  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
+  if (elt_bytes(dtype) == 0) return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (num_kv_heads > 65535 || num_tokens > 65535) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales) return PKV_EINVAL;
+  dim3 grid(num_kv_heads, num_tokens, 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, static_cast<const char*>(k), static_cast<const char*>(v),
+                       slot_mapping, static_cast<char*>(k_cache), static_cast<char*>(v_cache), k_scales, v_scales,
+                       num_kv_heads, block_size, num_slots, static_cast<int32_t>(layout == PKV_NHD));
+  };
+  switch (dtype) {
+    case PKV_F32:
+      head_dim == 128 ? go(append_q8_kernel<float, 128, kQ>) : go(append_q8_kernel<float, 64, kQ>);
+      break;
+    case PKV_F16:
+      head_dim == 128 ? go(append_q8_kernel<_Float16, 128, kQ>) : go(append_q8_kernel<_Float16, 64, kQ>);
+      break;
+    case PKV_BF16:
+      head_dim == 128 ? go(append_q8_kernel<__bf16, 128, kQ>) : go(append_q8_kernel<__bf16, 64, kQ>);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
 }  // namespace
@@ -1529,27 +1612,16 @@ pkv_status pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_m
                              void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
                              pkv_dtype dtype, void* stream) {
-  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0) return PKV_EINVAL;
-  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
-  if (elt_bytes(dtype) == 0) return PKV_EINVAL;
-  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
-  if (num_kv_heads > 65535 || num_tokens > 65535) return PKV_EINVAL;
-  if (num_tokens == 0) return PKV_OK;
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales) return PKV_EINVAL;
-  dim3 grid(num_kv_heads, num_tokens, 2);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, static_cast<const char*>(k), static_cast<const char*>(v),
-                       slot_mapping, static_cast<char*>(k_cache), static_cast<char*>(v_cache), k_scales, v_scales,
-                       num_kv_heads, block_size, num_slots, static_cast<int32_t>(layout == PKV_NHD));
-  };
-  switch (dtype) {
-    case PKV_F32: head_dim == 128 ? go(append_fp8_kernel<float, 128>) : go(append_fp8_kernel<float, 64>); break;
-    case PKV_F16: head_dim == 128 ? go(append_fp8_kernel<_Float16, 128>) : go(append_fp8_kernel<_Float16, 64>); break;
-    case PKV_BF16: head_dim == 128 ? go(append_fp8_kernel<__bf16, 128>) : go(append_fp8_kernel<__bf16, 64>); break;
-  }
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+  return append_codes<kQFp8>(k, v, slot_mapping, num_tokens, k_cache, v_cache, k_scales, v_scales, num_blocks,
+                             num_kv_heads, head_dim, block_size, layout, dtype, stream);
+}
+
+pkv_status pkv_kv_append_int8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                              void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                              pkv_dtype dtype, void* stream) {
+  return append_codes<kQInt8>(k, v, slot_mapping, num_tokens, k_cache, v_cache, k_scales, v_scales, num_blocks,
+                              num_kv_heads, head_dim, block_size, layout, dtype, stream);
 }
 
 pkv_status pkv_paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -1563,7 +1635,7 @@ pkv_status pkv_paged_decode_attention_fp8(const void* q, const void* k_cache, co
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
                       workspace_bytes, partition_blocks, kPartitions | kMerge, stream, nullptr, nullptr, k_scales,
-                      v_scales, true);
+                      v_scales, kQFp8);
 }
 
 pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -1574,7 +1646,7 @@ pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_n
                                void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream) {
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
-                      workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, true);
+                      workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, kQFp8);
 }
 
 size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -1608,7 +1680,7 @@ pkv_status pkv_prefill_attention(const void* q, const void* k_cache, const void*
                                  size_t workspace_bytes, int32_t partition_blocks, void* stream) {
   return prefill_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, q_start, max_q_len, context_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype,
-                       workspace, workspace_bytes, partition_blocks, stream, nullptr, nullptr, false);
+                       workspace, workspace_bytes, partition_blocks, stream, nullptr, nullptr, 0);
 }
 
 pkv_status pkv_prefill_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
@@ -1620,7 +1692,44 @@ pkv_status pkv_prefill_attention_fp8(const void* q, const void* k_cache, const v
                                      int32_t partition_blocks, void* stream) {
   return prefill_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, q_start, max_q_len, context_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype,
-                       workspace, workspace_bytes, partition_blocks, stream, k_scales, v_scales, true);
+                       workspace, workspace_bytes, partition_blocks, stream, k_scales, v_scales, kQFp8);
+}
+
+pkv_status pkv_paged_decode_attention_int8(const void* q, const void* k_cache, const void* v_cache,
+                                           const float* k_scales, const float* v_scales,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           pkv_layout layout, int32_t num_blocks, float scale, void* out,
+                                           pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                           int32_t partition_blocks, void* stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kPartitions | kMerge, stream, nullptr, nullptr, k_scales,
+                      v_scales, kQInt8);
+}
+
+pkv_status pkv_decode_step_int8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                float* k_scales, float* v_scales, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                pkv_layout layout, int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                void* workspace, size_t workspace_bytes, int32_t partition_blocks, void* stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
+                      workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new, k_scales, v_scales, kQInt8);
+}
+
+pkv_status pkv_prefill_attention_int8(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                                      const float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* q_start, int32_t max_q_len, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, pkv_layout layout, int32_t num_blocks, float scale,
+                                      void* out, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      int32_t partition_blocks, void* stream) {
+  return prefill_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, q_start, max_q_len, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype,
+                       workspace, workspace_bytes, partition_blocks, stream, k_scales, v_scales, kQInt8);
 }
 
 pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

@@ -1,4 +1,5 @@
-"""GPU parity of the FP8 (E4M3) KV cache path against the CPU reference.
+"""GPU parity of the 8-bit KV cache paths (FP8 E4M3 and INT8 codes with fp32
+per-row scales) against the CPU reference.
 
 The quantizing append (separate kernel and fused into the decode step) must
 match the reference bit for bit: codes and fp32 scales. Attention over the
@@ -51,14 +52,17 @@ def to_dev(torch, dev, wk):
                 lens=torch.from_numpy(wk.context_lens.astype(np.int32)).to(dev))
 
 
-def oracle_fp8(wk):
+FMTS = ["e4m3", "int8"]
+
+
+def oracle_fp8(wk, fmt="e4m3"):
     """Reference append (quantize) + attention over the dequantized cache."""
     cfg = wk.cfg
     kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
     slots = oracle.slot_mapping(wk.block_tables, wk.context_lens - 1, cfg.block_size)
-    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, cfg.block_size, cfg.dtype)
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, cfg.block_size, cfg.dtype, fmt=fmt)
     ref = oracle.decode_attention_fp8(wk.q, kc, vc, ks, vs, wk.block_tables, wk.context_lens, cfg.scale,
-                                      cfg.num_kv_heads, cfg.block_size, cfg.dtype)
+                                      cfg.num_kv_heads, cfg.block_size, cfg.dtype, fmt=fmt)
     return ref, kc, vc, ks, vs
 
 
@@ -69,11 +73,12 @@ def assert_caches_equal(torch, d, kc, vc, ks, vs, what):
     assert d["vs"].cpu().numpy().tobytes() == vs.tobytes(), f"{what}: V scales differ"
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_fp8_append_bit_exact(torch_dev, in_dtype, D):
+def test_fp8_append_bit_exact(torch_dev, in_dtype, D, fmt):
     torch, dev = torch_dev
-    note(f"fp8 append: {in_dtype} rows, D={D}")
+    note(f"{fmt} append: {in_dtype} rows, D={D}")
     cfg = wl.DecodeConfig("fp8app", 0, 1, 6, 8, 4, D, 16, in_dtype, context_lens=(1, 16, 17, 40, 300, 33))
     wk = wl.make_host_workload_fp8(cfg)
     # scale some rows up and down so amax spans many binades
@@ -81,14 +86,15 @@ def test_fp8_append_bit_exact(torch_dev, in_dtype, D):
     d = to_dev(torch, dev, wk)
     slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
     slots[2] = -1  # a padding token
-    pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"])
+    pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"], fmt=fmt)
     torch.cuda.synchronize()
     kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
-    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, 16, in_dtype)
-    assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 append")
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, 16, in_dtype, fmt=fmt)
+    assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} append")
 
 
-def test_fp8_append_extreme_rows(torch_dev):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_append_extreme_rows(torch_dev, fmt):
     """Rows with a zero amax, a single huge value, and subnormal-range values."""
     torch, dev = torch_dev
     cfg = wl.DecodeConfig("fp8ext", 0, 1, 4, 4, 2, 128, 16, "f32", context_lens=(3, 20, 33, 50))
@@ -100,45 +106,47 @@ def test_fp8_append_extreme_rows(torch_dev):
     wk.v_new[3, 0] = -0.0
     d = to_dev(torch, dev, wk)
     slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
-    pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"])
+    pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"], fmt=fmt)
     torch.cuda.synchronize()
     kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
-    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, 16, "f32")
-    assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 append, extreme rows")
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, slots, 16, "f32", fmt=fmt)
+    assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} append, extreme rows")
 
 
 EDGE_LENS = (1, 2, 15, 16, 17, 33, 128, 129, 257, 600, 1100, 2049)
 SHAPES = [(4, 2, 64), (32, 8, 128), (8, 8, 64), (64, 8, 128), (28, 4, 128), (64, 2, 128)]
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_fp8_attention_and_fused_step(torch_dev, q_dtype, shape):
+def test_fp8_attention_and_fused_step(torch_dev, q_dtype, shape, fmt):
     torch, dev = torch_dev
     Hq, Hkv, D = shape
     cfg = wl.DecodeConfig("fp8", 0, 1, len(EDGE_LENS), Hq, Hkv, D, 16, q_dtype, context_lens=EDGE_LENS)
     wk = wl.make_host_workload_fp8(cfg, seed=3000 + Hq + Hkv + D)
-    ref, kc, vc, ks, vs = oracle_fp8(wk)
+    ref, kc, vc, ks, vs = oracle_fp8(wk, fmt)
     for pb in (0, 1, 3, 64, 128):
-        note(f"fp8 {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: append + attention")
+        note(f"{fmt} {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: append + attention")
         d = to_dev(torch, dev, wk)
         slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
-        pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"])
+        pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"],
+                          fmt=fmt)
         out = torch.full_like(d["q"], float("nan"))
         ws = pkv.alloc_workspace(d["q"], d["kc"], d["t"], pb)
         pkv.paged_decode_attention_fp8(d["q"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"], cfg.scale,
-                                       out, ws, pb)
+                                       out, ws, pb, fmt=fmt)
         torch.cuda.synchronize()
         assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 split path")
         check_close(oracle.upcast(wl.torch_to_raw(out, q_dtype), q_dtype), ref, f"fp8 split {shape} pb={pb}")
-        note(f"fp8 {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: fused step x2")
+        note(f"{fmt} {q_dtype} Hq={Hq} Hkv={Hkv} D={D} pb={pb}: fused step x2")
         d = to_dev(torch, dev, wk)
         ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], pb)
         outs = []
         for _ in range(2):
             out = torch.full_like(d["q"], float("nan"))
             pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
-                                cfg.scale, out, ws, pb)
+                                cfg.scale, out, ws, pb, fmt=fmt)
             torch.cuda.synchronize()
             outs.append(wl.torch_to_raw(out, q_dtype))
         assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 fused step")

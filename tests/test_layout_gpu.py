@@ -93,9 +93,10 @@ def test_layout_and_block_size_parity(torch_dev, layout, bs, dtype, shape):
         assert outs[0].tobytes() == outs[1].tobytes()
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 @pytest.mark.parametrize("bs", [16, 32, 128])
-def test_fp8_layout_and_block_size_parity(torch_dev, layout, bs):
+def test_fp8_layout_and_block_size_parity(torch_dev, layout, bs, fmt):
     torch, dev = torch_dev
     Hq, Hkv, D, dtype = 32, 8, 128, "bf16"
     cfg = wl.DecodeConfig("geom8", 0, 1, len(LENS), Hq, Hkv, D, bs, dtype, context_lens=LENS)
@@ -105,26 +106,27 @@ def test_fp8_layout_and_block_size_parity(torch_dev, layout, bs):
     to_s = lambda x: to(x[..., None])[..., 0].copy()
     kc_o, vc_o, ks_o, vs_o = to(wk.k_codes).copy(), to(wk.v_codes).copy(), to_s(wk.k_scales), to_s(wk.v_scales)
     slots = oracle.slot_mapping(wk.block_tables, wk.context_lens - 1, bs)
-    oracle.kv_append_fp8(kc_o, vc_o, ks_o, vs_o, wk.k_new, wk.v_new, slots, bs, dtype, layout)
+    oracle.kv_append_fp8(kc_o, vc_o, ks_o, vs_o, wk.k_new, wk.v_new, slots, bs, dtype, layout, fmt=fmt)
     ref = oracle.decode_attention_fp8(wk.q, kc_o, vc_o, ks_o, vs_o, wk.block_tables, wk.context_lens, cfg.scale, Hkv,
-                                      bs, dtype, layout=layout)
+                                      bs, dtype, layout=layout, fmt=fmt)
     t = torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev)
     lens = torch.from_numpy(wk.context_lens.astype(np.int32)).to(dev)
     q = wl.raw_to_torch(wk.q, dtype, dev)
     kn, vn = wl.raw_to_torch(wk.k_new, dtype, dev), wl.raw_to_torch(wk.v_new, dtype, dev)
     for pb in partition_choices(bs):
         for fused in (False, True):
-            note(f"fp8 {layout} bs={bs} pb={pb} fused={fused}")
+            note(f"{fmt} {layout} bs={bs} pb={pb} fused={fused}")
             kc, vc = torch.from_numpy(to(wk.k_codes).copy()).to(dev), torch.from_numpy(to(wk.v_codes).copy()).to(dev)
             ks, vs = torch.from_numpy(to_s(wk.k_scales)).to(dev), torch.from_numpy(to_s(wk.v_scales)).to(dev)
             out = torch.full_like(q, float("nan"))
             if fused:
                 ws = pkv.alloc_step_workspace(q, kc, t, pb, layout=layout)
-                pkv.decode_step_fp8(q, kn, vn, kc, vc, ks, vs, t, lens, cfg.scale, out, ws, pb, layout=layout)
+                pkv.decode_step_fp8(q, kn, vn, kc, vc, ks, vs, t, lens, cfg.scale, out, ws, pb, layout=layout, fmt=fmt)
             else:
-                pkv.kv_append_fp8(kn, vn, torch.from_numpy(slots).to(dev), kc, vc, ks, vs, layout=layout)
+                pkv.kv_append_fp8(kn, vn, torch.from_numpy(slots).to(dev), kc, vc, ks, vs, layout=layout, fmt=fmt)
                 ws = pkv.alloc_workspace(q, kc, t, pb, layout=layout)
-                pkv.paged_decode_attention_fp8(q, kc, vc, ks, vs, t, lens, cfg.scale, out, ws, pb, layout=layout)
+                pkv.paged_decode_attention_fp8(q, kc, vc, ks, vs, t, lens, cfg.scale, out, ws, pb, layout=layout,
+                                               fmt=fmt)
             torch.cuda.synchronize()
             assert kc.cpu().numpy().tobytes() == kc_o.tobytes() and vc.cpu().numpy().tobytes() == vc_o.tobytes()
             assert ks.cpu().numpy().tobytes() == ks_o.tobytes() and vs.cpu().numpy().tobytes() == vs_o.tobytes()

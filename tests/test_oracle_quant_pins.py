@@ -130,3 +130,62 @@ def test_fp8_append_writes_quantized_rows_only():
         mask[s // 16, :, s % 16] = False
     assert np.array_equal(wk.k_codes[mask], before[0][mask]) and np.array_equal(wk.v_codes[mask], before[1][mask])
     assert np.array_equal(wk.k_scales[mask], before[2][mask], equal_nan=True)
+
+
+# ---------------------------------------------------------------------------
+# INT8 codes
+# ---------------------------------------------------------------------------
+def test_int8_hand_worked_codes_and_ties():
+    # amax 1 -> inv 127: 0.5 * 127 = 63.5 -> 64 (tie to even), 0.25 * 127 = 31.75 -> 32
+    codes, scale = q.quantize_rows_int8(np.array([[0.5, -1.0, 0.25, 0.0, -0.5]], np.float32))
+    assert codes.tolist() == [[64, -127, 32, 0, -64]] and scale[0] == np.float32(1 / 127)
+    # exact ties of x * inv: amax 127 -> inv 1, scale 1
+    codes, scale = q.quantize_rows_int8(np.array([[2.5, 3.5, -2.5, -3.5, 127.0, 0.5, 1.5]], np.float32))
+    assert codes.tolist() == [[2, 4, -2, -4, 127, 0, 2]] and scale[0] == 1.0
+    c0, s0 = q.quantize_rows_int8(np.zeros((1, 8), np.float32))
+    assert not c0.any() and s0[0] == 1.0
+    assert q.int8_decode(np.array([0x81, 0x7F, 0x00, 0xFF], np.uint8)).tolist() == [-127, 127, 0, -1]
+
+
+def test_int8_rounding_matches_library_and_bound():
+    import torch
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((256, 128)) * rng.uniform(1e-3, 50, (256, 1))).astype(np.float32)
+    codes, scale = q.quantize_rows_int8(x)
+    inv = np.where(np.abs(x).max(-1) == 0, 1, np.float32(127) / np.abs(x).max(-1)).astype(np.float32)
+    # torch.round rounds half to even (a library routine), applied to the same float32 products
+    ref = torch.round(torch.from_numpy((x * inv[:, None]).astype(np.float32))).clamp(-127, 127).to(torch.int8)
+    assert np.array_equal(codes, ref.numpy())
+    # the row maximum maps to +-127 and every value is within half a step
+    top = np.take_along_axis(codes, np.argmax(np.abs(x), -1)[:, None], -1)[:, 0]
+    assert np.all(np.abs(top) == 127)
+    err = np.abs(codes.astype(np.float64) * scale[:, None] - x)
+    assert np.all(err <= scale[:, None].astype(np.float64) * (0.5 + 1e-6))
+    # planted mistake: truncation breaks the half-step bound
+    trunc = np.trunc(x * inv[:, None]).astype(np.float64) * scale[:, None]
+    assert np.any(np.abs(trunc - x) > scale[:, None] * 0.5 * (1 + 1e-6))
+
+
+def test_int8_attention_reference_is_the_dequantized_attention():
+    rng = np.random.default_rng(12)
+    NB, Hkv, bs, D = 6, 2, 16, 64
+    kc = rng.integers(0, 256, (NB, Hkv, bs, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (NB, Hkv, bs, D), dtype=np.uint8)
+    ks = rng.uniform(0.001, 0.1, (NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.001, 0.1, (NB, Hkv, bs)).astype(np.float32)
+    qv = wl.draw_values(rng, (2, 4, D), "bf16")
+    table = np.array([[3, 1, 0], [5, 2, 4]], np.int32)
+    lens = [20, 40]
+    got = da.decode_attention_fp8(qv, kc, vc, ks, vs, table, lens, 0.125, Hkv, bs, "bf16", fmt="int8")
+    kd = kc.view(np.int8).astype(np.float64) * ks[..., None]
+    vd = vc.view(np.int8).astype(np.float64) * vs[..., None]
+    qf = da.upcast(qv, "bf16")
+    for b, n in enumerate(lens):
+        rows = [(table[b][t // bs], t % bs) for t in range(n)]
+        for h in range(4):
+            j = h // 2
+            K = np.stack([kd[pb, j, o] for pb, o in rows])
+            V = np.stack([vd[pb, j, o] for pb, o in rows])
+            s_ = K @ qf[b, h] * 0.125
+            w = np.exp(s_ - s_.max())
+            assert np.max(np.abs(got[b, h] - (w / w.sum()) @ V)) < 1e-12

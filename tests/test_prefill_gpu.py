@@ -77,8 +77,9 @@ def test_prefill_parity(torch_dev, layout, bs, dtype, shape):
         assert outs[0].tobytes() == outs[1].tobytes(), "repeated call differs"
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
-def test_prefill_fp8_parity(torch_dev, layout):
+def test_prefill_fp8_parity(torch_dev, layout, fmt):
     torch, dev = torch_dev
     Hq, Hkv, D, bs, dtype = 32, 8, 128, 16, "bf16"
     lens, q_start, max_q = chunk_layout()
@@ -86,24 +87,24 @@ def test_prefill_fp8_parity(torch_dev, layout):
     wk = wl.make_host_workload_fp8(cfg, seed=7100)
     kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
     oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, oracle.slot_mapping(wk.block_tables, lens - 1, bs), bs,
-                         dtype)
+                         dtype, fmt=fmt)
     to = lambda x: wl.to_layout(x, layout)
     to_s = lambda x: to(x[..., None])[..., 0].copy()
     kc, vc, ks, vs = to(kc), to(vc), to_s(ks), to_s(vs)
     q = wl.draw_values(np.random.default_rng(2), (int(q_start[-1]), Hq, D), dtype)
     ref = oracle.prefill_attention_fp8(q, kc, vc, ks, vs, wk.block_tables, q_start, lens, cfg.scale, Hkv, bs, dtype,
-                                       layout)
+                                       layout, fmt=fmt)
     dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     qd = wl.raw_to_torch(q, dtype, dev)
     t, ld, qs = dv(wk.block_tables.astype(np.int32)), dv(lens), dv(q_start)
     for pb in (0, 2):
-        note(f"prefill fp8 {layout} pb={pb}")
+        note(f"prefill {fmt} {layout} pb={pb}")
         ws = pkv.alloc_prefill_workspace(qs, Hq, dv(kc), t, max_q, pb, layout=layout)
         out = torch.full_like(qd, float("nan"))
         pkv.prefill_attention_fp8(qd, dv(kc), dv(vc), dv(ks), dv(vs), t, qs, max_q, ld, cfg.scale, out, ws, pb,
-                                  layout=layout)
+                                  layout=layout, fmt=fmt)
         torch.cuda.synchronize()
-        check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype, f"prefill fp8 {layout} pb={pb}")
+        check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype, f"prefill {fmt} {layout} pb={pb}")
 
 
 def test_prefill_full_prompt_equals_decode_steps(torch_dev):
