@@ -67,6 +67,9 @@ constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two til
 #ifndef PKV_AHEAD_FP8
 #define PKV_AHEAD_FP8 2
 #endif
+#ifndef PKV_PREFILL_PAIRS
+#define PKV_PREFILL_PAIRS 1
+#endif
 #ifndef PKV_AHEAD_PREFILL
 #define PKV_AHEAD_PREFILL 2
 #endif
@@ -427,9 +430,12 @@ enum Mode : int {
 // Row groups (16 query rows each) a prefill wave processes against every
 // loaded K/V tile: 4 for 16-bit queries, 2 for fp32 (register budget); one for
 // the decode modes.
+#ifndef PKV_PREFILL_ROWS
+#define PKV_PREFILL_ROWS 4
+#endif
 template <typename T, int kMode>
-constexpr int kPrefillRowGroups = kMode == kModePrefill ? (sizeof(T) == 2 ? 4 : 2) : 1;
-constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 : 4; }
+constexpr int kPrefillRowGroups = kMode == kModePrefill ? (sizeof(T) == 2 ? PKV_PREFILL_ROWS : 2) : 1;
+constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 : PKV_PREFILL_ROWS; }
 
 // kMode = kModeSplit: one partition of attention (a split sequence leaves
 // partials for merge_kernel). kModeStep: the fused decode step -- the partition that
@@ -822,6 +828,105 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }  // row groups
   };
 
+  // Prefill with 16-bit queries takes tiles in pairs: one softmax step (one
+  // cross-lane maximum, one rescale decision) per 32 keys, and one 16x16x32
+  // PV MFMA per output block over both tiles. The MFMA's K index runs over
+  // tile a's rows 4*q4 .. 4*q4+3, then tile b's: each lane already holds those
+  // V rows and those weights, so neither operand moves between lanes.
+  constexpr bool kPairs = kPrefill && k16 && PKV_PREFILL_PAIRS;
+  auto process_pair = [&](R& ra, int va, int ta, R& rb, int vb, int tb) {
+    BlockRegs<T, D> ca, cb;
+    BlockRegs<T, D>* pa;
+    BlockRegs<T, D>* pb2;
+    if constexpr (kFp8) {
+      codes_to_16<kQ, T, D>(ra, ca);
+      codes_to_16<kQ, T, D>(rb, cb);
+      pa = &ca;
+      pb2 = &cb;
+    } else {
+      pa = &ra;
+      pb2 = &rb;
+    }
+    BlockRegs<T, D>& A = *pa;
+    BlockRegs<T, D>& Bt = *pb2;
+    // V operands over both tiles, shared by the row groups
+    u32x4 av[S::kE];
+#pragma unroll
+    for (int mt = 0; mt < S::kE; ++mt) {
+      const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
+      av[mt] = u32x4{__builtin_amdgcn_perm(A.v[1][mt >> 1], A.v[0][mt >> 1], sel),
+                     __builtin_amdgcn_perm(A.v[3][mt >> 1], A.v[2][mt >> 1], sel),
+                     __builtin_amdgcn_perm(Bt.v[1][mt >> 1], Bt.v[0][mt >> 1], sel),
+                     __builtin_amdgcn_perm(Bt.v[3][mt >> 1], Bt.v[2][mt >> 1], sel)};
+    }
+    const int key_a = (blk0 + ta) * kTile, key_b = (blk0 + tb) * kTile;
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < S::kNK; ++c) {
+        sa = mfma_qk16<T>(A.k[c], qv[rg][c], sa);
+        sb = mfma_qk16<T>(Bt.k[c], qv[rg][c], sb);
+      }
+      float sc[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (kFp8) {
+          sc[i] = sa[i] * ra.ks[i] * a.qk_scale;
+          sc[4 + i] = sb[i] * rb.ks[i] * a.qk_scale;
+        } else {
+          sc[i] = sa[i] * a.qk_scale;
+          sc[4 + i] = sb[i] * a.qk_scale;
+        }
+      }
+      // rows past a tile's valid count were not fetched; keys past a row's
+      // position are masked (both tests are wave-uniform to enter)
+      if (va < kTile || key_a + kTile > min_limit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[i] = (4 * q4 + i < va && key_a + 4 * q4 + i < my_limit[rg]) ? sc[i] : kNegInf;
+      }
+      if (vb < kTile || key_b + kTile > min_limit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 + i] = (4 * q4 + i < vb && key_b + 4 * q4 + i < my_limit[rg]) ? sc[4 + i] : kNegInf;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mx = fmaxf(mx, xor_shuffle(mx, 16));
+      mx = fmaxf(mx, xor_shuffle(mx, 32));
+      const bool grow = mx > m_run[rg] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+        const float m_new = grow ? mx : m_run[rg];
+        const float alpha = m_run[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= alpha;
+        l_run[rg] *= alpha;
+        m_run[rg] = m_new;
+      }
+      const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
+      unsigned ph[8], pl[8];
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(sc[i] - m_use);
+        lsum += pr;
+        float pv = pr;
+        if constexpr (kFp8) pv *= i < 4 ? ra.vs[i] : rb.vs[i - 4];
+        ph[i] = to_bits16<T>(pv);
+        pl[i] = to_bits16<T>(pv - from_bits16<T>(ph[i]));
+      }
+      l_run[rg] += lsum;
+      const u32x4 pw_hi = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16), ph[4] | (ph[5] << 16), ph[6] | (ph[7] << 16)};
+      const u32x4 pw_lo = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16), pl[4] | (pl[5] << 16), pl[6] | (pl[7] << 16)};
+#pragma unroll
+      for (int mt = 0; mt < S::kE; ++mt) {
+        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
+        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo, acc[rg][mt]);
+      }
+    }
+  };
+
   // Stream the partition's blocks through a register ring that keeps kAhead
   // blocks of K/V loads in flight while the oldest block is consumed. Loads
   // are issued unconditionally (past the partition end they fetch nothing, see
@@ -830,9 +935,32 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   constexpr int kAhead = kPrefill ? (sizeof(T) == 2 ? PKV_AHEAD_PREFILL : PKV_AHEAD_32BIT)
                                   : (kFp8 ? PKV_AHEAD_FP8 : (sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT));
   constexpr int kRing = kAhead + 1;
-  R ring[kRing];
-  int ring_rows[kRing];
-  if (nblk > 0) {  // wave-uniform; nblk == 0 only for an empty sequence
+  R ring[kPairs ? 4 : kRing];
+  int ring_rows[kPairs ? 4 : kRing];
+  if constexpr (kPairs) {
+    // two tiles in flight while two are consumed: slots {0,1} and {2,3} alternate
+    if (nblk > 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const size_t tile = block_src(u, ring_rows[u]);
+        load_ring(ring[u], tile, ring_rows[u]);
+      }
+      for (int t0 = 0; t0 < nblk; t0 += 4) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int cur = 2 * pp, nxt = 2 - 2 * pp;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const size_t tile = block_src(t0 + 2 * pp + 2 + u, ring_rows[nxt + u]);
+            load_ring(ring[nxt + u], tile, ring_rows[nxt + u]);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
+          if (t0 + 2 * pp < nblk)
+            process_pair(ring[cur], ring_rows[cur], t0 + 2 * pp, ring[cur + 1], ring_rows[cur + 1], t0 + 2 * pp + 1);
+        }
+      }
+    }
+  } else if (nblk > 0) {  // wave-uniform; nblk == 0 only for an empty sequence
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
       const size_t tile = block_src(u, ring_rows[u]);
@@ -1657,7 +1785,7 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
     return 0;
   // enough for either row-group count (the launch's dtype decides which)
   size_t need = 0;
-  for (int kR : {2, 4}) {
+  for (int kR : {2, PKV_PREFILL_ROWS}) {
     const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads *
                           prefill_q_tiles(num_heads, num_kv_heads, max_q_len, kR);
     const int32_t m = block_size / kTile;
