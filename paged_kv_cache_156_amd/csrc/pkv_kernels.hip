@@ -67,6 +67,9 @@ constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two til
 #ifndef PKV_AHEAD_FP8
 #define PKV_AHEAD_FP8 2
 #endif
+#ifndef PKV_DECODE_PAIRS
+#define PKV_DECODE_PAIRS 1
+#endif
 #ifndef PKV_PREFILL_PAIRS
 #define PKV_PREFILL_PAIRS 1
 #endif
@@ -700,9 +703,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  auto process = [&](R& rr, int valid, int t) {  // valid: token rows of this block in range
+  // fused step: the tile holding position n-1 gets the appended token's row
+  // from registers (it was not fetched)
+  auto patch_new = [&](R& rr, int& valid, int t) {
     if constexpr (kStep) {
-      if (t == new_t) {  // wave-uniform: patch in the appended token
+      if (t == new_t) {  // wave-uniform
         valid = new_row + 1;
         if constexpr (kFp8) {
           if (ln == new_row) {
@@ -731,6 +736,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         }
       }
     }
+  };
+  auto process = [&](R& rr, int valid, int t) {  // valid: token rows of this block in range
+    patch_new(rr, valid, t);
     BlockRegs<T, D> conv;
     BlockRegs<T, D>* rp;
     if constexpr (kFp8) {
@@ -828,13 +836,15 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }  // row groups
   };
 
-  // Prefill with 16-bit queries takes tiles in pairs: one softmax step (one
+  // With 16-bit queries tiles are taken in pairs: one softmax step (one
   // cross-lane maximum, one rescale decision) per 32 keys, and one 16x16x32
   // PV MFMA per output block over both tiles. The MFMA's K index runs over
   // tile a's rows 4*q4 .. 4*q4+3, then tile b's: each lane already holds those
   // V rows and those weights, so neither operand moves between lanes.
-  constexpr bool kPairs = kPrefill && k16 && PKV_PREFILL_PAIRS;
+  constexpr bool kPairs = k16 && (kPrefill ? PKV_PREFILL_PAIRS : PKV_DECODE_PAIRS);
   auto process_pair = [&](R& ra, int va, int ta, R& rb, int vb, int tb) {
+    patch_new(ra, va, ta);
+    patch_new(rb, vb, tb);
     BlockRegs<T, D> ca, cb;
     BlockRegs<T, D>* pa;
     BlockRegs<T, D>* pb2;
@@ -881,15 +891,15 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       }
       // rows past a tile's valid count were not fetched; keys past a row's
       // position are masked (both tests are wave-uniform to enter)
-      if (va < kTile || key_a + kTile > min_limit) {
+      if (va < kTile || (kPrefill && key_a + kTile > min_limit)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          sc[i] = (4 * q4 + i < va && key_a + 4 * q4 + i < my_limit[rg]) ? sc[i] : kNegInf;
+          sc[i] = (4 * q4 + i < va && (!kPrefill || key_a + 4 * q4 + i < my_limit[rg])) ? sc[i] : kNegInf;
       }
-      if (vb < kTile || key_b + kTile > min_limit) {
+      if (vb < kTile || (kPrefill && key_b + kTile > min_limit)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          sc[4 + i] = (4 * q4 + i < vb && key_b + 4 * q4 + i < my_limit[rg]) ? sc[4 + i] : kNegInf;
+          sc[4 + i] = (4 * q4 + i < vb && (!kPrefill || key_b + 4 * q4 + i < my_limit[rg])) ? sc[4 + i] : kNegInf;
       }
       float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -939,6 +949,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   int ring_rows[kPairs ? 4 : kRing];
   if constexpr (kPairs) {
     // two tiles in flight while two are consumed: slots {0,1} and {2,3} alternate
+    // (the same bytes in flight as the single-tile ring with two tiles ahead)
     if (nblk > 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
