@@ -67,6 +67,9 @@ constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two til
 #ifndef PKV_AHEAD_FP8
 #define PKV_AHEAD_FP8 2
 #endif
+#ifndef PKV_PARTITION_TARGET
+#define PKV_PARTITION_TARGET 512
+#endif
 #ifndef PKV_DECODE_PAIRS
 #define PKV_DECODE_PAIRS 1
 #endif
@@ -1300,9 +1303,10 @@ int64_t ceil_div64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 int32_t auto_partition_tiles_for_units(int64_t units, int64_t max_tiles) {
   if (units <= 0 || max_tiles <= 0) return 16;
   // Long partitions amortise each wave's start-up (table and Q loads, then the
-  // first dependent K/V loads) and the merge; about four single-wave
-  // workgroups per CU (256 CUs) keep enough loads in flight.
-  const int64_t target = 1024;
+  // first dependent K/V loads) and the merge (one wave combines all of a
+  // unit's partitions, four at a time); the halving stops once there are
+  // PKV_PARTITION_TARGET waves (two per CU at the default).
+  const int64_t target = PKV_PARTITION_TARGET;
   int32_t pb = 64;
   while (pb > 8 && units * ceil_div64(max_tiles, pb) < target) pb /= 2;
   return pb;
