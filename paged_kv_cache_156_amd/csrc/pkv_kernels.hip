@@ -67,6 +67,9 @@ constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two til
 #ifndef PKV_AHEAD_FP8
 #define PKV_AHEAD_FP8 2
 #endif
+#ifndef PKV_XCD_ROTATE
+#define PKV_XCD_ROTATE 1
+#endif
 #ifndef PKV_PARTITION_TARGET
 #define PKV_PARTITION_TARGET 512
 #endif
@@ -481,7 +484,13 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int q4 = lane >> 4;
   const int ln = lane & 15;
-  const int p = blockIdx.x;
+  // Partition of this workgroup. Workgroups go to the eight XCDs round-robin
+  // by linear id, so with a partition count that is a multiple of 8 partition
+  // p of every unit would land on XCD p % 8, and the low partitions, which
+  // every sequence has, would crowd the first XCDs. Rotating the partitions
+  // by the unit index starts each unit on another XCD.
+  const int p = PKV_XCD_ROTATE ? static_cast<int>((blockIdx.x + blockIdx.y + gridDim.y * blockIdx.z) % gridDim.x)
+                               : static_cast<int>(blockIdx.x);
   const int units_per_head = kPrefill ? a.q_tiles : a.head_groups;  // work units per (sequence, KV head)
   const int j = blockIdx.y / units_per_head;
   const int ui = blockIdx.y - j * units_per_head;  // head group (decode) or query tile (prefill)
