@@ -97,6 +97,15 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 
+// maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four quarters of
+// the wave) with gfx950's cross-row swaps: no LDS round trip
+__device__ __forceinline__ float quarter_max(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // float -> 16-bit storage, round to nearest even; returns the bits
 template <typename T>
 __device__ __forceinline__ unsigned to_bits16(float x);
@@ -117,6 +126,28 @@ __device__ __forceinline__ float from_bits16<__bf16>(unsigned b) {
 template <>
 __device__ __forceinline__ float from_bits16<_Float16>(unsigned b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(b)));
+}
+
+// Two weights as a packed 16-bit head (hi) and the packed 16-bit rounding of
+// what the head leaves out (lo): hi + lo carries about 16 significant bits.
+// Any rounding of the head works (the residual is exact in fp32), so fp16
+// uses the packed round-toward-zero conversion.
+using f32x2 = float __attribute__((ext_vector_type(2)));
+using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ void split16_pair(float p0, float p1, unsigned& hi, unsigned& lo);
+template <>
+__device__ __forceinline__ void split16_pair<__bf16>(float p0, float p1, unsigned& hi, unsigned& lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
+}
+template <>
+__device__ __forceinline__ void split16_pair<_Float16>(float p0, float p1, unsigned& hi, unsigned& lo) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(h[0]),
+                                                                p1 - static_cast<float>(h[1])));
 }
 
 // one QK MFMA step on a 16-byte chunk (16-bit types: 8 elements)
@@ -428,6 +459,107 @@ struct DecodeArgs {
   int32_t max_q_len;       // bound on q_start[b+1] - q_start[b]
   int32_t q_tiles;         // 16-row query tiles per (sequence, KV head): ceil(max_q_len * group / 16)
 };
+
+// Fused merge of a wave's kR row groups (16 query rows each) over the
+// partitions of its work unit `unit`, from the partition kernel itself.
+// Partials are stored lane-major per (work unit, row group) (each store
+// instruction writes 64 lanes x 16 bytes contiguously) with device-coherent
+// stores (sc1: written through the XCD's L2), then the wave drains its stores
+// and counts its arrival. The last partition of the unit to arrive reads all
+// partials back with device-coherent loads, combines them (exact log-sum-exp
+// merge, one online pass over groups of four partitions whose loads are
+// issued together), writes the rows through `write_out(rg, 1 / L)` and resets
+// the counter for the next call. No L2 write-back or invalidate is needed.
+template <int D, int kR, typename WriteOut>
+__device__ __forceinline__ void fused_merge(const DecodeArgs& a, size_t unit, int p, int nparts, int lane,
+                                            f32x4 (&acc)[kR][D / 16], const float (&m_run)[kR],
+                                            const float (&l_tot)[kR], const float (&inv)[kR], WriteOut& write_out) {
+  constexpr int kE = D / 16;
+  constexpr int kChunks = kE;  // 16-byte chunks per lane: 4*E floats
+  const int ln = lane & 15;
+  const size_t part_stride = static_cast<size_t>(kChunks) * 64 * 16;
+  auto rsrc_o = [&](int rg) {
+    char* ob = reinterpret_cast<char*>(a.ws_o) + (unit * kR + rg) * a.num_parts * part_stride;
+    return tile_rsrc(ob, static_cast<int>(nparts * part_stride));
+  };
+  auto rsrc_l = [&](int rg) {
+    char* lb = reinterpret_cast<char*>(a.ws_lse) + (unit * kR + rg) * a.num_parts * 64;
+    return tile_rsrc(lb, nparts * 64);
+  };
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    const __amdgpu_buffer_rsrc_t ro = rsrc_o(rg);
+    const __amdgpu_buffer_rsrc_t rl = rsrc_l(rg);
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * k + e;  // value index i * E + mt
+        v[e] = acc[rg][idx % kE][idx / kE] * inv[rg];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                   __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                             ro, (p * kChunks + k) * 1024 + lane * 16, 0, kCacheDeviceCoherent);
+    }
+    if (lane < 16)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run[rg] + __builtin_amdgcn_logf(l_tot[rg])), rl,
+                                            p * 64 + ln * 4, 0, kCacheDeviceCoherent);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // every store above has completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int32_t* ctr = a.counters + unit;
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0 is active here (the unit's first row is real)
+  if (prev != nparts - 1) return;
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    const __amdgpu_buffer_rsrc_t ro = rsrc_o(rg);
+    const __amdgpu_buffer_rsrc_t rl = rsrc_l(rg);
+#pragma unroll
+    for (int mt = 0; mt < kE; ++mt) acc[rg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float M = kNegInf, L = 0.f;
+    for (int pp0 = 0; pp0 < nparts; pp0 += 4) {
+      float ls[4];
+      u32x4 ov[4][kChunks];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // past the last partition these read as zero
+        ls[u] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rl, (pp0 + u) * 64 + ln * 4, 0, kCacheDeviceCoherent));
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(ro, ((pp0 + u) * kChunks + k) * 1024 + lane * 16, 0,
+                                                               kCacheDeviceCoherent);
+          ov[u][k] = u32x4{x[0], x[1], x[2], x[3]};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ls[u] = pp0 + u < nparts ? ls[u] : kNegInf;
+      const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
+      const float r = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+      M = m_new;
+      L *= r;
+#pragma unroll
+      for (int mt = 0; mt < kE; ++mt) acc[rg][mt] *= r;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __builtin_amdgcn_exp2f(ls[u] - M);  // 0 past the last partition
+        L += w;
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int idx = 4 * k + e;
+            acc[rg][idx % kE][idx / kE] += w * __uint_as_float(ov[u][k][e]);
+          }
+      }
+    }
+    write_out(rg, 1.0f / L);
+  }
+  if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // What one launch of the tile kernel computes.
 enum Mode : int {
@@ -1058,99 +1190,360 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     }
     if (q4 == 0) a.ws_lse[row0 + p] = m_run[0] + __builtin_amdgcn_logf(l_tot[0]);
   } else {
-    // Fused merge. Partials are stored lane-major per (work unit, row group)
-    // (each store instruction writes 64 lanes x 16 bytes contiguously) with
-    // device-coherent stores (sc1: written through the XCD's L2), then the
-    // wave drains its stores and counts its arrival. The last partition of the
-    // unit to arrive reads all partials back with device-coherent loads,
-    // combines them (exact log-sum-exp merge, one online pass over groups of
-    // four partitions whose loads are issued together) and resets the counter
-    // for the next call. No L2 write-back or invalidate is needed.
-    constexpr int kChunks = S::kE;  // 16-byte chunks per lane: 4*E floats
     const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * units_per_head + ui;
-    const size_t part_stride = static_cast<size_t>(kChunks) * 64 * 16;
-    auto rsrc_o = [&](int rg) {
-      char* ob = reinterpret_cast<char*>(a.ws_o) + (unit * kR + rg) * a.num_parts * part_stride;
-      return tile_rsrc(ob, static_cast<int>(nparts * part_stride));
-    };
-    auto rsrc_l = [&](int rg) {
-      char* lb = reinterpret_cast<char*>(a.ws_lse) + (unit * kR + rg) * a.num_parts * 64;
-      return tile_rsrc(lb, nparts * 64);
-    };
-#pragma unroll
-    for (int rg = 0; rg < kR; ++rg) {
-      const __amdgpu_buffer_rsrc_t ro = rsrc_o(rg);
-      const __amdgpu_buffer_rsrc_t rl = rsrc_l(rg);
-#pragma unroll
-      for (int k = 0; k < kChunks; ++k) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = 4 * k + e;  // value index i * E + mt
-          v[e] = acc[rg][idx % S::kE][idx / S::kE] * inv[rg];
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                     __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                               ro, (p * kChunks + k) * 1024 + lane * 16, 0, kCacheDeviceCoherent);
-      }
-      if (q4 == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run[rg] + __builtin_amdgcn_logf(l_tot[rg])), rl,
-                                              p * 64 + ln * 4, 0, kCacheDeviceCoherent);
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // every store above has completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    int32_t* ctr = a.counters + unit;
-    int prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0 is active here (the unit's first row is real)
-    if (prev != nparts - 1) return;
-#pragma unroll
-    for (int rg = 0; rg < kR; ++rg) {
-      const __amdgpu_buffer_rsrc_t ro = rsrc_o(rg);
-      const __amdgpu_buffer_rsrc_t rl = rsrc_l(rg);
-#pragma unroll
-      for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float M = kNegInf, L = 0.f;
-      for (int pp0 = 0; pp0 < nparts; pp0 += 4) {
-        float ls[4];
-        u32x4 ov[4][kChunks];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {  // past the last partition these read as zero
-          ls[u] = __uint_as_float(
-              __builtin_amdgcn_raw_buffer_load_b32(rl, (pp0 + u) * 64 + ln * 4, 0, kCacheDeviceCoherent));
-#pragma unroll
-          for (int k = 0; k < kChunks; ++k) {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b128(ro, ((pp0 + u) * kChunks + k) * 1024 + lane * 16, 0,
-                                                                 kCacheDeviceCoherent);
-            ov[u][k] = u32x4{x[0], x[1], x[2], x[3]};
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ls[u] = pp0 + u < nparts ? ls[u] : kNegInf;
-        const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
-        const float r = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
-        M = m_new;
-        L *= r;
-#pragma unroll
-        for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= r;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float w = __builtin_amdgcn_exp2f(ls[u] - M);  // 0 past the last partition
-          L += w;
-#pragma unroll
-          for (int k = 0; k < kChunks; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int idx = 4 * k + e;
-              acc[rg][idx % S::kE][idx / S::kE] += w * __uint_as_float(ov[u][k][e]);
-            }
-        }
-      }
-      write_out(rg, 1.0f / L);
-    }
-    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    fused_merge<D, kR>(a, unit, p, nparts, lane, acc, m_run, l_tot, inv, write_out);
   }
+}
+
+// ---------------------------------------------------------------------------
+// chunked prefill over 16-bit caches: K/V tiles shared through LDS
+// ---------------------------------------------------------------------------
+// Prefill multiplies many query rows against the same keys, so it is bound by
+// MFMA work and by the traffic that feeds the MFMAs, not by HBM bytes (page
+// "KV Cache and Inference Optimization": prefill is compute-bound, decode
+// memory-bound). A workgroup of kW waves, each holding kR groups of 16
+// (token, head) rows of one KV head's chunk, walks the partition's key tiles
+// two at a time. The workgroup copies a pair of tiles from the cache into LDS
+// -- K in MFMA fragment order (fragment f, lane l at byte 1024 f + 16 l), V in
+// row order -- double-buffered with one barrier per pair, and every wave runs
+// its QK and PV MFMAs from there: a tile is fetched once per workgroup instead
+// of once per wave. The register layouts, the online softmax and the 16-bit
+// head + residual weights are those of the decode kernel's tile pairs.
+//
+// Workgroups are numbered so that consecutive numbers land on one XCD
+// (workgroups are dealt to the XCDs round-robin by linear id) and the query
+// tiles of one (sequence, KV head, partition), which read the same K/V, are
+// consecutive: their tiles meet in that XCD's L2. The cache loads use the
+// default cache policy for the same reason.
+constexpr int kXcds = 8;  // MI355X: eight accelerator complex dies
+#ifndef PKV_PREFILL_LDS
+#define PKV_PREFILL_LDS 1
+#endif
+#ifndef PKV_PREFILL_LDS_ROWS
+#define PKV_PREFILL_LDS_ROWS 2  // 16-row groups per wave
+#endif
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4  // waves per workgroup (head size 128; 4 for 64)
+#endif
+constexpr int prefill_waves(int head_dim) { return head_dim == 64 ? 4 : PKV_PREFILL_WAVES; }
+
+template <typename T, int D, bool kNHD, int kW, int kR>
+__global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
+  using S = Shape<T, D>;
+  static_assert(sizeof(T) == 2, "the LDS prefill reads 16-bit caches");
+  constexpr int kNK = S::kNK;                        // K fragments per tile
+  constexpr int kKBytes = 2 * kNK * 1024;            // K of a tile pair, fragment order
+  constexpr int kVBytes = 2 * kTile * S::kRowBytes;  // V of a tile pair, row order
+  constexpr int kBuf = kKBytes + kVBytes;
+  constexpr int kThreads = 64 * kW;
+  constexpr int kKLoads = kKBytes / 16 / kThreads;  // 16-byte loads per thread per pair
+  constexpr int kVLoads = kVBytes / 16 / kThreads;
+  constexpr int kRowChunks = S::kRowBytes / 16;
+  constexpr int kVTileChunks = kTile * kRowChunks;
+  static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kVBytes,
+                "a tile pair splits evenly over the workgroup");
+  static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
+  __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4;
+  const int ln = lane & 15;
+
+  // work unit (sequence b, KV head j, query tile ui, partition p), numbered
+  // XCD-major: XCD x runs the x-th contiguous range of unit numbers
+  const unsigned nwg = gridDim.x * gridDim.y * gridDim.z;
+  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const unsigned xcd = lin % kXcds, per = nwg / kXcds, extra = nwg % kXcds;
+  unsigned id = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + lin / kXcds;
+  const int ui = static_cast<int>(id % static_cast<unsigned>(a.q_tiles));
+  id /= static_cast<unsigned>(a.q_tiles);
+  const int p = static_cast<int>(id % gridDim.x);
+  id /= gridDim.x;
+  const int j = static_cast<int>(id % static_cast<unsigned>(a.num_kv_heads));
+  const int b = static_cast<int>(id / static_cast<unsigned>(a.num_kv_heads));
+
+  // the chunk's query tokens are the last q_len of the sequence's n tokens
+  const int cap = a.cap_tokens;
+  int n = a.context_lens[b];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int q_tok0 = a.q_start[b];
+  int q_len = a.q_start[b + 1] - q_tok0;
+  q_len = q_len < 0 ? 0 : min(q_len, min(a.max_q_len, n));
+  const int rows = q_len * a.group;
+  const int first = n - q_len;  // position of the chunk's first token
+  constexpr int kWgRows = kW * kR * kTile;
+  const int wg_r0 = ui * kWgRows;
+  if (wg_r0 >= rows) return;  // the whole workgroup: no rows
+  // keys the workgroup reads: up to its last row's position
+  const int n_wg = first + min(wg_r0 + kWgRows - 1, rows - 1) / a.group + 1;
+  const int nblk_seq = (n_wg + kTile - 1) / kTile;
+  const int nparts = (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
+  if (p >= nparts) return;
+  const int blk0 = p * a.pb_per_part;
+  const int nblk = min(a.pb_per_part, nblk_seq - blk0);
+
+  // this wave's rows: kR groups of 16, row r = token r / g, head r % g
+  const int r0 = wg_r0 + w * kR * kTile;
+  const bool wave_rows = r0 < rows;
+  const int n_w = wave_rows ? first + min(r0 + kR * kTile - 1, rows - 1) / a.group + 1 : 0;
+  const int min_limit = first + r0 / a.group + 1;  // the smallest key limit of the wave's rows
+  int my_limit[kR];
+  bool head_ok[kR];
+  size_t qidx[kR];
+  u32x4 qv[kR][kNK];  // Q as the B operand, same chunk permutation as K
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    const int r = r0 + rg * kTile + ln;
+    head_ok[rg] = r < rows;
+    const int tok = head_ok[rg] ? r / a.group : 0;
+    const int hin = head_ok[rg] ? r - tok * a.group : 0;
+    my_limit[rg] = head_ok[rg] ? first + tok + 1 : 0;
+    qidx[rg] = (static_cast<size_t>(q_tok0) + tok) * a.num_heads + j * a.group + hin;
+    const char* qrow = a.q + qidx[rg] * S::kRowBytes;
+#pragma unroll
+    for (int cc = 0; cc < kNK; ++cc)
+      qv[rg][cc] = head_ok[rg] ? *reinterpret_cast<const u32x4*>(qrow + (4 * cc + q4) * 16) : u32x4{0, 0, 0, 0};
+  }
+  const float c = a.qk_scale;  // > 0: the host routes other scales to the one-wave kernel
+
+  // first cache row of each of the partition's tiles (lane i: tile blk0 + i
+  // and blk0 + 64 + i), -1 for a block id outside the pool
+  const size_t trow = static_cast<size_t>(b) * a.max_blocks;
+  const int m = a.tiles_per_block;
+  const int max_tiles = a.max_blocks * m;
+  auto tile_row0 = [&](int lt) -> int {
+    const int lb = lt / m;
+    const int bid = a.block_tables[trow + lb];
+    if (static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks)) return -1;
+    const int sub = lt - lb * m;
+    return kNHD ? (bid * m + sub) * kTile * a.num_kv_heads + j : ((bid * a.num_kv_heads + j) * m + sub) * kTile;
+  };
+  int my_r0 = -1, my_r02 = -1;
+  if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
+  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
+  const int rs = S::kRowBytes * (kNHD ? a.num_kv_heads : 1);  // bytes between a head's consecutive token rows
+  // first cache row of the partition's tile t and its rows to fetch: 0 past
+  // the partition end or for an id outside the pool (nothing is read then)
+  auto tile_src = [&](int t, int& valid) -> size_t {
+    const int tt = min(t, 127);
+    const int r = tt < 64 ? __builtin_amdgcn_readlane(my_r0, tt & 63) : __builtin_amdgcn_readlane(my_r02, tt & 63);
+    const bool ok = t < nblk && r >= 0;
+    valid = ok ? min(kTile, n_wg - (blk0 + t) * kTile) : 0;
+    return ok ? static_cast<size_t>(r) : 0;
+  };
+
+  // cache -> registers -> LDS for the tile pair of step s
+  u32x4 stage[kKLoads + kVLoads];
+  auto fetch = [&](int s) {
+    int va, vb;
+    const size_t ra = tile_src(2 * s, va);
+    const size_t rb = tile_src(2 * s + 1, vb);
+    const __amdgpu_buffer_rsrc_t rka = tile_rsrc(a.k_cache + ra * S::kRowBytes, va * rs);
+    const __amdgpu_buffer_rsrc_t rkb = tile_rsrc(a.k_cache + rb * S::kRowBytes, vb * rs);
+    const __amdgpu_buffer_rsrc_t rva = tile_rsrc(a.v_cache + ra * S::kRowBytes, va * rs);
+    const __amdgpu_buffer_rsrc_t rvb = tile_rsrc(a.v_cache + rb * S::kRowBytes, vb * rs);
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      // fragment f = w + kW i of the pair: tile f / kNK, chunk group cg = f % kNK;
+      // lane (q4, ln) takes token ln's 16-byte chunk 4 cg + q4
+      const int f = w + kW * i;
+      const int cg = f % kNK;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(f < kNK ? rka : rkb, ln * rs + (4 * cg + q4) * 16, 0, 0);
+      stage[i] = u32x4{x[0], x[1], x[2], x[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      const int cw = 64 * w + kThreads * i;  // the wave's first V chunk of the pair
+      const int u = cw / kVTileChunks;
+      const int ch = cw - u * kVTileChunks + lane;
+      const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(u == 0 ? rva : rvb, row * rs + col * 16, 0, 0);
+      stage[kKLoads + i] = u32x4{x[0], x[1], x[2], x[3]};
+    }
+  };
+  auto stash = [&](int buf) {
+    char* base = lds + buf * kBuf;
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) *reinterpret_cast<u32x4*>(base + (tid + kThreads * i) * 16) = stage[i];
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i)
+      *reinterpret_cast<u32x4*>(base + kKBytes + (tid + kThreads * i) * 16) = stage[kKLoads + i];
+  };
+
+  f32x4 acc[kR][S::kE];
+  float m_run[kR];  // running max of scaled scores (log2 units)
+  float l_run[kR];  // this lane's share of the running denominator
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+#pragma unroll
+    for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rg] = kNegInf;
+    l_run[rg] = 0.f;
+  }
+
+  auto compute = [&](int buf, int s) {
+    const int key_a = (blk0 + 2 * s) * kTile, key_b = key_a + kTile;
+    if (!wave_rows || key_a >= n_w) return;  // wave-uniform: the pair lies past every row's position
+    int va, vb;
+    tile_src(2 * s, va);
+    tile_src(2 * s + 1, vb);
+    const char* kl = lds + buf * kBuf;
+    const char* vl = kl + kKBytes;
+    f32x4 sa[kR], sb[kR];
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) sa[rg] = sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < kNK; ++cc) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kl + cc * 1024 + lane * 16);
+      const u32x4 kb = *reinterpret_cast<const u32x4*>(kl + (kNK + cc) * 1024 + lane * 16);
+#pragma unroll
+      for (int rg = 0; rg < kR; ++rg) {
+        sa[rg] = mfma_qk16<T>(ka, qv[rg][cc], sa[rg]);
+        sb[rg] = mfma_qk16<T>(kb, qv[rg][cc], sb[rg]);
+      }
+    }
+    // V rows 4*q4 + i of both tiles, this lane's E elements, packed into the
+    // A operand of each output block mt (K index: tile a's rows, then tile b's)
+    unsigned v_a[4][S::kVDW], v_b[4][S::kVDW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* ra = vl + (4 * q4 + i) * S::kRowBytes + ln * S::kE * 2;
+      const char* rb = ra + kTile * S::kRowBytes;
+      if constexpr (S::kVDW == 4) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ra);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(rb);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          v_a[i][d] = x[d];
+          v_b[i][d] = y[d];
+        }
+      } else {
+        static_assert(S::kVDW == 2, "16-bit rows of 64 or 128 elements");
+        const u32x2 x = *reinterpret_cast<const u32x2*>(ra);
+        const u32x2 y = *reinterpret_cast<const u32x2*>(rb);
+        v_a[i][0] = x[0];
+        v_a[i][1] = x[1];
+        v_b[i][0] = y[0];
+        v_b[i][1] = y[1];
+      }
+    }
+    u32x4 av[S::kE];
+#pragma unroll
+    for (int mt = 0; mt < S::kE; ++mt) {
+      const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
+      av[mt] = u32x4{__builtin_amdgcn_perm(v_a[1][mt >> 1], v_a[0][mt >> 1], sel),
+                     __builtin_amdgcn_perm(v_a[3][mt >> 1], v_a[2][mt >> 1], sel),
+                     __builtin_amdgcn_perm(v_b[1][mt >> 1], v_b[0][mt >> 1], sel),
+                     __builtin_amdgcn_perm(v_b[3][mt >> 1], v_b[2][mt >> 1], sel)};
+    }
+    // Raw scores; the scale c = qk_scale > 0 is applied inside the exponent
+    // (max(c s) = c max(s)). Masked keys score -inf.
+    float sc[kR][8], mx[kR];
+    bool grow_any = false;
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[rg][i] = sa[rg][i];
+        sc[rg][4 + i] = sb[rg][i];
+      }
+      // rows past a tile's valid count were not fetched (they read as zero);
+      // keys past a row's position are masked (both tests are wave-uniform)
+      if (va < kTile || key_a + kTile > min_limit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[rg][i] = (4 * q4 + i < va && key_a + 4 * q4 + i < my_limit[rg]) ? sc[rg][i] : kNegInf;
+      }
+      if (vb < kTile || key_b + kTile > min_limit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[rg][4 + i] = (4 * q4 + i < vb && key_b + 4 * q4 + i < my_limit[rg]) ? sc[rg][4 + i] : kNegInf;
+      }
+      const float m8 = fmaxf(fmaxf(fmaxf(sc[rg][0], sc[rg][1]), fmaxf(sc[rg][2], sc[rg][3])),
+                             fmaxf(fmaxf(sc[rg][4], sc[rg][5]), fmaxf(sc[rg][6], sc[rg][7])));
+      mx[rg] = quarter_max(m8) * c;  // -inf stays -inf (c > 0)
+      grow_any |= mx[rg] > m_run[rg] + kRescaleSlack;
+    }
+    // one wave-uniform rescale decision for all row groups of the pair
+    if (__builtin_amdgcn_ballot_w64(grow_any)) {
+#pragma unroll
+      for (int rg = 0; rg < kR; ++rg) {
+        const bool grow = mx[rg] > m_run[rg] + kRescaleSlack;
+        const float m_new = grow ? mx[rg] : m_run[rg];
+        const float alpha = m_run[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= alpha;
+        l_run[rg] *= alpha;
+        m_run[rg] = m_new;
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) {
+      const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
+      float pr[8];
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rg][i], c, -m_use));
+        lsum += pr[i];
+      }
+      l_run[rg] += lsum;
+      unsigned hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split16_pair<T>(pr[2 * i], pr[2 * i + 1], hi[i], lo[i]);
+      const u32x4 pw_hi = {hi[0], hi[1], hi[2], hi[3]}, pw_lo = {lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+      for (int mt = 0; mt < S::kE; ++mt) {
+        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
+        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo, acc[rg][mt]);
+      }
+    }
+  };
+
+  // double-buffered pairs: the next pair's loads are in flight while this
+  // pair is consumed; one barrier per pair orders both LDS buffers
+  const int nsteps = (nblk + 1) / 2;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (more) fetch(s + 1);
+    compute(s & 1, s);
+    if (more) stash((s + 1) & 1);
+    __syncthreads();
+  }
+  if (!wave_rows) return;
+
+  float l_tot[kR], inv[kR];
+#pragma unroll
+  for (int rg = 0; rg < kR; ++rg) {
+    l_tot[rg] = l_run[rg] + xor_shuffle(l_run[rg], 16);
+    l_tot[rg] += xor_shuffle(l_tot[rg], 32);
+    inv[rg] = l_tot[rg] > 0.f ? 1.0f / l_tot[rg] : 0.f;
+  }
+  // this lane's 4 x E output values of row group rg (d = (4*q4 + i) * E + mt)
+  auto write_out = [&](int rg, float scale_by) {
+    if (!head_ok[rg]) return;
+    char* orow = a.out + qidx[rg] * S::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unsigned wv[S::kVDW];
+#pragma unroll
+      for (int mt = 0; mt < S::kE; mt += 2)
+        wv[mt >> 1] = to_bits16<T>(acc[rg][mt][i] * scale_by) | (to_bits16<T>(acc[rg][mt + 1][i] * scale_by) << 16);
+      store_dwords<S::kVDW>(orow + (4 * q4 + i) * S::kE * 2, wv);
+    }
+  };
+  if (nparts == 1) {
+#pragma unroll
+    for (int rg = 0; rg < kR; ++rg) write_out(rg, inv[rg]);
+    return;
+  }
+  const size_t unit = ((static_cast<size_t>(b) * a.num_kv_heads + j) * a.q_tiles + ui) * kW + w;  // one per wave
+  fused_merge<D, kR>(a, unit, p, nparts, lane, acc, m_run, l_tot, inv, write_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1309,14 +1702,14 @@ int elt_bytes(pkv_dtype dt) {
 
 int64_t ceil_div64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-int32_t auto_partition_tiles_for_units(int64_t units, int64_t max_tiles) {
+int32_t auto_partition_tiles_for_units(int64_t units, int64_t max_tiles, int32_t longest = 64) {
   if (units <= 0 || max_tiles <= 0) return 16;
-  // Long partitions amortise each wave's start-up (table and Q loads, then the
-  // first dependent K/V loads) and the merge (one wave combines all of a
-  // unit's partitions, four at a time); the halving stops once there are
-  // PKV_PARTITION_TARGET waves (two per CU at the default).
+  // Long partitions amortise each workgroup's start-up (table and Q loads,
+  // then the first dependent K/V loads) and the merge (one wave combines all
+  // of a unit's partitions, four at a time); the halving from `longest` stops
+  // once there are PKV_PARTITION_TARGET workgroups (two per CU at the default).
   const int64_t target = PKV_PARTITION_TARGET;
-  int32_t pb = 64;
+  int32_t pb = longest;
   while (pb > 8 && units * ceil_div64(max_tiles, pb) < target) pb /= 2;
   return pb;
 }
@@ -1378,6 +1771,15 @@ pkv_status launch_prefill(const DecodeArgs& a, int32_t num_seqs, hipStream_t str
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
+template <typename T, int D>
+pkv_status launch_prefill_lds(const DecodeArgs& a, int32_t num_seqs, hipStream_t stream, bool nhd) {
+  dim3 grid(a.num_parts, a.num_kv_heads * a.q_tiles, num_seqs);
+  constexpr int kW = prefill_waves(D), kR = PKV_PREFILL_LDS_ROWS;
+  if (nhd) hipLaunchKernelGGL((prefill_lds_kernel<T, D, true, kW, kR>), grid, dim3(64 * kW), 0, stream, a);
+  else hipLaunchKernelGGL((prefill_lds_kernel<T, D, false, kW, kR>), grid, dim3(64 * kW), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
 // 16-bit query type x head size x code format (kQFp8 / kQInt8) for 8-bit caches
 template <template <typename, int, int> class L, typename... A>
 pkv_status dispatch_codes(pkv_dtype dtype, int head_dim, int q, A&&... args) {
@@ -1427,10 +1829,52 @@ StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   const int64_t groups = ceil_div64(num_heads / num_kv_heads, 16);
   return merge_layout(static_cast<int64_t>(num_seqs) * num_kv_heads * groups, head_dim, parts);
 }
-// query tiles (kR groups of 16 rows each) per (sequence, KV head) for a chunk
-// of up to max_q_len tokens
-int64_t prefill_q_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len, int kR) {
-  return ceil_div64(static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads), kTile * kR);
+// How a prefill launch splits its rows. The LDS kernel serves 16-bit caches
+// and positive finite scales: a work unit is a workgroup of
+// prefill_waves(head_dim) waves with PKV_PREFILL_LDS_ROWS row groups each. 8-bit and fp32 caches take the one-wave tile kernel with
+// prefill_row_groups(dtype) row groups per unit.
+struct PrefillPlan {
+  bool lds;
+  int32_t rows_per_unit;   // (token, head) rows of one KV head per work unit
+  int32_t slots_per_unit;  // 16-row groups per unit: partial slots and counters
+  int32_t longest;         // longest automatic partition, 16-row tiles
+};
+PrefillPlan prefill_plan(pkv_dtype dtype, int codes, int32_t head_dim, float scale) {
+  const float c = scale * kLog2e;  // the LDS kernel applies c > 0 inside the exponent
+  if (PKV_PREFILL_LDS && codes == 0 && dtype != PKV_F32 && c > 0.f && c <= 3.0e38f) {
+    const int32_t groups = prefill_waves(head_dim) * PKV_PREFILL_LDS_ROWS;
+    return {true, groups * kTile, groups, kMaxPartitionBlocks};
+  }
+  const int32_t kR = prefill_row_groups(dtype);
+  return {false, kR * kTile, kR, 64};
+}
+// query tiles (work units) per (sequence, KV head) for a chunk of up to
+// max_q_len tokens
+int64_t prefill_q_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_q_len, const PrefillPlan& plan) {
+  return ceil_div64(static_cast<int64_t>(max_q_len) * (num_heads / num_kv_heads), plan.rows_per_unit);
+}
+// partition size in cache blocks (`requested` if > 0) and the workspace a
+// launch with this plan needs
+struct PrefillSplit {
+  int64_t q_tiles, units;
+  int32_t pb, parts;
+  size_t ws_bytes;
+};
+PrefillSplit prefill_split(const PrefillPlan& plan, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t max_q_len, int32_t max_blocks, int32_t block_size,
+                           int32_t requested) {
+  PrefillSplit r{};
+  r.q_tiles = prefill_q_tiles(num_heads, num_kv_heads, max_q_len, plan);
+  r.units = static_cast<int64_t>(num_seqs) * num_kv_heads * r.q_tiles;
+  const int32_t m = block_size / kTile;
+  r.pb = requested;
+  if (r.pb <= 0) {
+    const int32_t tiles = auto_partition_tiles_for_units(r.units, static_cast<int64_t>(max_blocks) * m, plan.longest);
+    r.pb = tiles / m > 0 ? tiles / m : 1;
+  }
+  r.parts = static_cast<int32_t>(ceil_div64(max_blocks, r.pb));
+  r.ws_bytes = merge_layout(r.units * plan.slots_per_unit, head_dim, r.parts).total();
+  return r;
 }
 
 // Validate, fill DecodeArgs and launch the requested phases. Pointers the
@@ -1548,8 +1992,10 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   if (!q || !k_cache || !v_cache || !block_tables || !q_start || !context_lens || !out) return PKV_EINVAL;
   if (fp8 && (!k_scales || !v_scales)) return PKV_EINVAL;
   if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;
-  const int kR = prefill_row_groups(dtype);
-  const int64_t qt = prefill_q_tiles(num_heads, num_kv_heads, max_q_len, kR);
+  const PrefillPlan plan = prefill_plan(dtype, codes, head_dim, scale);
+  const PrefillSplit split = prefill_split(plan, num_seqs, num_heads, num_kv_heads, head_dim, max_q_len,
+                                           max_blocks_per_seq, block_size, partition_blocks);
+  const int64_t qt = split.q_tiles;
   if (qt * num_kv_heads > 65535 || num_seqs > 65535) return PKV_EINVAL;
   DecodeArgs a{};
   a.q = static_cast<const char*>(q);
@@ -1568,21 +2014,15 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   a.max_q_len = max_q_len;
   a.q_tiles = static_cast<int32_t>(qt);
   const int32_t m = block_size / kTile;
-  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * qt;
-  int32_t pb = partition_blocks;
-  if (pb == 0) {
-    const int32_t tiles = auto_partition_tiles_for_units(units, static_cast<int64_t>(max_blocks_per_seq) * m);
-    pb = tiles / m > 0 ? tiles / m : 1;
-  }
   a.tiles_per_block = m;
-  a.pb_per_part = pb * m;
-  a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, pb));
+  a.pb_per_part = split.pb * m;
+  a.num_parts = split.parts;
   a.cap_tokens = max_blocks_per_seq * block_size;
   a.qk_scale = scale * kLog2e;
   a.k_scales = reinterpret_cast<const char*>(k_scales);
   a.v_scales = reinterpret_cast<const char*>(v_scales);
   if (a.num_parts > 1) {
-    const StepLayout L = merge_layout(units * kR, head_dim, a.num_parts);  // one slot per row group
+    const StepLayout L = merge_layout(split.units * plan.slots_per_unit, head_dim, a.num_parts);  // slot per row group
     if (!workspace || workspace_bytes < L.total()) return PKV_ESMALL;
     char* ws = static_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(ws);
@@ -1592,6 +2032,13 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool nhd = layout == PKV_NHD;
   if (fp8) return dispatch_codes<PrefillLauncher>(dtype, head_dim, codes, a, num_seqs, s, nhd);
+  if (plan.lds) {
+    if (dtype == PKV_BF16)
+      return head_dim == 128 ? launch_prefill_lds<__bf16, 128>(a, num_seqs, s, nhd)
+                             : launch_prefill_lds<__bf16, 64>(a, num_seqs, s, nhd);
+    return head_dim == 128 ? launch_prefill_lds<_Float16, 128>(a, num_seqs, s, nhd)
+                           : launch_prefill_lds<_Float16, 64>(a, num_seqs, s, nhd);
+  }
   switch (dtype) {
     case PKV_BF16:
       return head_dim == 128 ? launch_prefill<__bf16, 128>(a, num_seqs, s, nhd)
@@ -1807,18 +2254,12 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_q_len <= 0 ||
       max_blocks_per_seq <= 0 || num_heads % num_kv_heads != 0 || !valid_block_size(block_size))
     return 0;
-  // enough for either row-group count (the launch's dtype decides which)
+  // enough for every plan (the launch's dtype and cache format decide which)
   size_t need = 0;
-  for (int kR : {2, PKV_PREFILL_ROWS}) {
-    const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads *
-                          prefill_q_tiles(num_heads, num_kv_heads, max_q_len, kR);
-    const int32_t m = block_size / kTile;
-    int32_t pb = partition_blocks;
-    if (pb <= 0) {
-      const int32_t tiles = auto_partition_tiles_for_units(units, static_cast<int64_t>(max_blocks_per_seq) * m);
-      pb = tiles / m > 0 ? tiles / m : 1;
-    }
-    const size_t bytes = merge_layout(units * kR, head_dim, ceil_div64(max_blocks_per_seq, pb)).total();
+  for (const PrefillPlan& plan : {prefill_plan(PKV_BF16, 0, head_dim, 1.f), prefill_plan(PKV_BF16, kQFp8, head_dim, 1.f),
+                                  prefill_plan(PKV_F32, 0, head_dim, 1.f)}) {
+    const size_t bytes = prefill_split(plan, num_seqs, num_heads, num_kv_heads, head_dim, max_q_len,
+                                       max_blocks_per_seq, block_size, partition_blocks).ws_bytes;
     need = bytes > need ? bytes : need;
   }
   return need;

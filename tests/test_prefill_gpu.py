@@ -130,3 +130,29 @@ def test_prefill_full_prompt_equals_decode_steps(torch_dev):
     for i in (0, 1, 15, 16, 17, 69):
         ref = oracle.decode_attention_seq(q[i], kc, vc, wk.block_tables[0], i + 1, cfg.scale, Hkv, bs, dtype)
         check_close(got[i], ref, dtype, f"row {i}")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.35])
+def test_prefill_any_scale(torch_dev, scale):
+    """Scales other than the usual positive 1/sqrt(d): negative and zero
+    scales take the one-wave kernel, positive ones the LDS kernel; all match
+    the reference (scale 0 is uniform attention over each row's keys)."""
+    torch, dev = torch_dev
+    Hq, Hkv, D, bs, dtype = 32, 8, 128, 16, "bf16"
+    lens, q_start, max_q = chunk_layout()
+    cfg = wl.DecodeConfig("prefill_scale", 0, 1, len(lens), Hq, Hkv, D, bs, dtype, context_lens=tuple(lens))
+    wk = wl.make_host_workload(cfg, seed=7300)
+    kc, vc = wk.k_cache.copy(), wk.v_cache.copy()
+    oracle.kv_append(kc, vc, wk.k_new, wk.v_new, oracle.slot_mapping(wk.block_tables, lens - 1, bs), bs)
+    q = wl.draw_values(np.random.default_rng(3), (int(q_start[-1]), Hq, D), dtype)
+    ref = oracle.prefill_attention(q, kc, vc, wk.block_tables, q_start, lens, scale, Hkv, bs, dtype)
+    kcd, vcd = wl.raw_to_torch(kc, dtype, dev), wl.raw_to_torch(vc, dtype, dev)
+    qd = wl.raw_to_torch(q, dtype, dev)
+    t = torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev)
+    qs = torch.from_numpy(q_start).to(dev)
+    note(f"prefill scale {scale}")
+    ws = pkv.alloc_prefill_workspace(qs, Hq, kcd, t, max_q, 0)
+    out = torch.full_like(qd, float("nan"))
+    pkv.prefill_attention(qd, kcd, vcd, t, qs, max_q, torch.from_numpy(lens).to(dev), scale, out, ws, 0)
+    torch.cuda.synchronize()
+    check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype, f"prefill scale {scale}")
