@@ -97,13 +97,20 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 
+using lds_void = __attribute__((address_space(3))) void;
+__device__ __forceinline__ lds_void* lds_ptr(char* p) { return (lds_void*)(p); }
+
+// IEEE maximum (a NaN operand gives NaN): unlike fmaxf it needs no operand
+// canonicalisation, and three-operand forms exist (v_maximum3_f32)
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four quarters of
 // the wave) with gfx950's cross-row swaps: no LDS round trip
 __device__ __forceinline__ float quarter_max(float x) {
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  x = fmax_nan(__uint_as_float(h[0]), __uint_as_float(h[1]));
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // float -> 16-bit storage, round to nearest even; returns the bits
@@ -470,8 +477,16 @@ struct DecodeArgs {
 // merge, one online pass over groups of four partitions whose loads are
 // issued together), writes the rows through `write_out(rg, 1 / L)` and resets
 // the counter for the next call. No L2 write-back or invalidate is needed.
+// The workspace comes as plain values (the layout: partials ws_o, lse values
+// ws_lse, counters; num_parts slots per unit row group).
+struct MergeSpace {
+  float* ws_o;
+  float* ws_lse;
+  int32_t* counters;
+  int32_t num_parts;
+};
 template <int D, int kR, typename WriteOut>
-__device__ __forceinline__ void fused_merge(const DecodeArgs& a, size_t unit, int p, int nparts, int lane,
+__device__ __forceinline__ void fused_merge(const MergeSpace a, size_t unit, int p, int nparts, int lane,
                                             f32x4 (&acc)[kR][D / 16], const float (&m_run)[kR],
                                             const float (&l_tot)[kR], const float (&inv)[kR], WriteOut& write_out) {
   constexpr int kE = D / 16;
@@ -1191,7 +1206,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     if (q4 == 0) a.ws_lse[row0 + p] = m_run[0] + __builtin_amdgcn_logf(l_tot[0]);
   } else {
     const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * units_per_head + ui;
-    fused_merge<D, kR>(a, unit, p, nparts, lane, acc, m_run, l_tot, inv, write_out);
+    fused_merge<D, kR>(MergeSpace{a.ws_o, a.ws_lse, a.counters, a.num_parts}, unit, p, nparts, lane, acc, m_run,
+                       l_tot, inv, write_out);
   }
 }
 
@@ -1243,8 +1259,22 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kVBytes,
                 "a tile pair splits evenly over the workgroup");
   static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
-  __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+  // three LDS buffers as separate objects: the compiler then tracks which
+  // buffer each cache -> LDS load writes and waits only for the right ones
+  __shared__ __attribute__((aligned(16))) char lds0[kBuf];
+  __shared__ __attribute__((aligned(16))) char lds1[kBuf];
+  __shared__ __attribute__((aligned(16))) char lds2[kBuf];
 
+  // The lambdas below capture only locals: a lambda that referenced `a`
+  // would take its address, and next to the cache -> LDS loads (which may
+  // write memory as far as the compiler knows) the arguments would then be
+  // copied to scratch and reloaded per lane.
+  const char* const k_cache = a.k_cache;
+  const char* const v_cache = a.v_cache;
+  const int32_t* const tables = a.block_tables;
+  char* const out = a.out;
+  const int num_blocks = a.num_blocks;
+  const int num_kv_heads = a.num_kv_heads;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1315,10 +1345,10 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   const int max_tiles = a.max_blocks * m;
   auto tile_row0 = [&](int lt) -> int {
     const int lb = lt / m;
-    const int bid = a.block_tables[trow + lb];
-    if (static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks)) return -1;
+    const int bid = tables[trow + lb];
+    if (static_cast<unsigned>(bid) >= static_cast<unsigned>(num_blocks)) return -1;
     const int sub = lt - lb * m;
-    return kNHD ? (bid * m + sub) * kTile * a.num_kv_heads + j : ((bid * a.num_kv_heads + j) * m + sub) * kTile;
+    return kNHD ? (bid * m + sub) * kTile * num_kv_heads + j : ((bid * num_kv_heads + j) * m + sub) * kTile;
   };
   int my_r0 = -1, my_r02 = -1;
   if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
@@ -1334,24 +1364,25 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     return ok ? static_cast<size_t>(r) : 0;
   };
 
-  // cache -> registers -> LDS for the tile pair of step s
-  u32x4 stage[kKLoads + kVLoads];
-  auto fetch = [&](int s) {
+  const int nsteps = (nblk + 1) / 2;  // tile pairs of the partition
+  // cache -> LDS for the tile pair of step s, straight into LDS buffer `dst`
+  // (buffer loads with the LDS flag: lane l's 16 bytes land at M0 + 16 l)
+  auto fetch = [&](int s, char* dst) __attribute__((always_inline)) {
     int va, vb;
     const size_t ra = tile_src(2 * s, va);
     const size_t rb = tile_src(2 * s + 1, vb);
-    const __amdgpu_buffer_rsrc_t rka = tile_rsrc(a.k_cache + ra * S::kRowBytes, va * rs);
-    const __amdgpu_buffer_rsrc_t rkb = tile_rsrc(a.k_cache + rb * S::kRowBytes, vb * rs);
-    const __amdgpu_buffer_rsrc_t rva = tile_rsrc(a.v_cache + ra * S::kRowBytes, va * rs);
-    const __amdgpu_buffer_rsrc_t rvb = tile_rsrc(a.v_cache + rb * S::kRowBytes, vb * rs);
+    const __amdgpu_buffer_rsrc_t rka = tile_rsrc(k_cache + ra * S::kRowBytes, va * rs);
+    const __amdgpu_buffer_rsrc_t rkb = tile_rsrc(k_cache + rb * S::kRowBytes, vb * rs);
+    const __amdgpu_buffer_rsrc_t rva = tile_rsrc(v_cache + ra * S::kRowBytes, va * rs);
+    const __amdgpu_buffer_rsrc_t rvb = tile_rsrc(v_cache + rb * S::kRowBytes, vb * rs);
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       // fragment f = w + kW i of the pair: tile f / kNK, chunk group cg = f % kNK;
       // lane (q4, ln) takes token ln's 16-byte chunk 4 cg + q4
       const int f = w + kW * i;
       const int cg = f % kNK;
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(f < kNK ? rka : rkb, ln * rs + (4 * cg + q4) * 16, 0, 0);
-      stage[i] = u32x4{x[0], x[1], x[2], x[3]};
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(f < kNK ? rka : rkb, lds_ptr(dst + f * 1024), 16,
+                                               ln * rs + (4 * cg + q4) * 16, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
@@ -1359,17 +1390,19 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
       const int u = cw / kVTileChunks;
       const int ch = cw - u * kVTileChunks + lane;
       const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(u == 0 ? rva : rvb, row * rs + col * 16, 0, 0);
-      stage[kKLoads + i] = u32x4{x[0], x[1], x[2], x[3]};
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(u == 0 ? rva : rvb, lds_ptr(dst + kKBytes + cw * 16), 16,
+                                               row * rs + col * 16, 0, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-    char* base = lds + buf * kBuf;
-#pragma unroll
-    for (int i = 0; i < kKLoads; ++i) *reinterpret_cast<u32x4*>(base + (tid + kThreads * i) * 16) = stage[i];
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i)
-      *reinterpret_cast<u32x4*>(base + kKBytes + (tid + kThreads * i) * 16) = stage[kKLoads + i];
+  // every wave's loads into the next buffer have landed once each wave has
+  // drained its own (all but the kLoads just issued) and the barrier is passed
+  constexpr int kLoads = kKLoads + kVLoads;
+  static_assert(kLoads < 16, "vmcnt field");
+  auto sync_pair = [&]() __attribute__((always_inline)) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xF70 | kLoads);  // vmcnt <= kLoads (expcnt, lgkmcnt: no wait)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
   f32x4 acc[kR][S::kE];
@@ -1383,17 +1416,12 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     l_run[rg] = 0.f;
   }
 
-  auto compute = [&](int buf, int s) {
-    const int key_a = (blk0 + 2 * s) * kTile, key_b = key_a + kTile;
-    if (!wave_rows || key_a >= n_w) return;  // wave-uniform: the pair lies past every row's position
-    int va, vb;
-    tile_src(2 * s, va);
-    tile_src(2 * s + 1, vb);
-    const char* kl = lds + buf * kBuf;
-    const char* vl = kl + kKBytes;
-    f32x4 sa[kR], sb[kR];
+  // QK^T of pair s (its K fragments at kl) for every row group; zero for a
+  // pair past the partition or past every row's position
+  auto scores = [&](const char* kl, int s, f32x4 (&sa)[kR], f32x4 (&sb)[kR]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg) sa[rg] = sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!wave_rows || s >= nsteps || (blk0 + 2 * s) * kTile >= n_w) return;  // wave-uniform
 #pragma unroll
     for (int cc = 0; cc < kNK; ++cc) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(kl + cc * 1024 + lane * 16);
@@ -1404,6 +1432,15 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         sb[rg] = mfma_qk16<T>(kb, qv[rg][cc], sb[rg]);
       }
     }
+  };
+  // online-softmax step and PV product of pair s (its V rows at vl)
+  auto attend = [&](const char* vl, int s, const f32x4 (&sa)[kR], const f32x4 (&sb)[kR])
+                    __attribute__((always_inline)) {
+    const int key_a = (blk0 + 2 * s) * kTile, key_b = key_a + kTile;
+    if (!wave_rows || key_a >= n_w) return;  // wave-uniform: the pair lies past every row's position
+    int va, vb;
+    tile_src(2 * s, va);
+    tile_src(2 * s + 1, vb);
     // V rows 4*q4 + i of both tiles, this lane's E elements, packed into the
     // A operand of each output block mt (K index: tile a's rows, then tile b's)
     unsigned v_a[4][S::kVDW], v_b[4][S::kVDW];
@@ -1461,8 +1498,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i)
           sc[rg][4 + i] = (4 * q4 + i < vb && key_b + 4 * q4 + i < my_limit[rg]) ? sc[rg][4 + i] : kNegInf;
       }
-      const float m8 = fmaxf(fmaxf(fmaxf(sc[rg][0], sc[rg][1]), fmaxf(sc[rg][2], sc[rg][3])),
-                             fmaxf(fmaxf(sc[rg][4], sc[rg][5]), fmaxf(sc[rg][6], sc[rg][7])));
+      const float m8 = fmax_nan(fmax_nan(fmax_nan(sc[rg][0], sc[rg][1]), fmax_nan(sc[rg][2], sc[rg][3])),
+                                fmax_nan(fmax_nan(sc[rg][4], sc[rg][5]), fmax_nan(sc[rg][6], sc[rg][7])));
       mx[rg] = quarter_max(m8) * c;  // -inf stays -inf (c > 0)
       grow_any |= mx[rg] > m_run[rg] + kRescaleSlack;
     }
@@ -1494,27 +1531,33 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) split16_pair<T>(pr[2 * i], pr[2 * i + 1], hi[i], lo[i]);
       const u32x4 pw_hi = {hi[0], hi[1], hi[2], hi[3]}, pw_lo = {lo[0], lo[1], lo[2], lo[3]};
-#pragma unroll
+  #pragma unroll
       for (int mt = 0; mt < S::kE; ++mt) {
         acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
         acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo, acc[rg][mt]);
       }
-    }
+      }
   };
 
-  // double-buffered pairs: the next pair's loads are in flight while this
-  // pair is consumed; one barrier per pair orders both LDS buffers
-  const int nsteps = (nblk + 1) / 2;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) fetch(s + 1);
-    compute(s & 1, s);
-    if (more) stash((s + 1) & 1);
-    __syncthreads();
+  // Three buffers, loads two pairs ahead: step s consumes buffer s % 3 while
+  // pairs s+1 and s+2 load; its barrier makes pair s+1 visible and frees
+  // buffer s % 3 for pair s+3. Past the partition end the loads fetch nothing.
+  fetch(0, lds0);
+  fetch(1, lds1);
+  sync_pair();
+  auto step = [&](int s, const char* cur, char* ahead) __attribute__((always_inline)) {
+    fetch(s + 2, ahead);
+    f32x4 sa[kR], sb[kR];
+    scores(cur, s, sa, sb);
+    attend(cur + kKBytes, s, sa, sb);
+    sync_pair();
+  };
+  for (int s0 = 0; s0 < nsteps; s0 += 3) {
+    step(s0, lds0, lds2);
+    if (s0 + 1 < nsteps) step(s0 + 1, lds1, lds0);
+    if (s0 + 2 < nsteps) step(s0 + 2, lds2, lds1);
   }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // no load into LDS outlives the workgroup
   if (!wave_rows) return;
 
   float l_tot[kR], inv[kR];
@@ -1527,7 +1570,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   // this lane's 4 x E output values of row group rg (d = (4*q4 + i) * E + mt)
   auto write_out = [&](int rg, float scale_by) {
     if (!head_ok[rg]) return;
-    char* orow = a.out + qidx[rg] * S::kRowBytes;
+    char* orow = out + qidx[rg] * S::kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       unsigned wv[S::kVDW];
@@ -1543,7 +1586,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     return;
   }
   const size_t unit = ((static_cast<size_t>(b) * a.num_kv_heads + j) * a.q_tiles + ui) * kW + w;  // one per wave
-  fused_merge<D, kR>(a, unit, p, nparts, lane, acc, m_run, l_tot, inv, write_out);
+  fused_merge<D, kR>(MergeSpace{a.ws_o, a.ws_lse, a.counters, a.num_parts}, unit, p, nparts, lane, acc, m_run, l_tot,
+                     inv, write_out);
 }
 
 // ---------------------------------------------------------------------------
