@@ -113,6 +113,17 @@ __device__ __forceinline__ float quarter_max(float x) {
   return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// the maximum over the four lanes of a score column (the decode kernel's
+// quarter-waves), by permlane swaps or, for comparison, two LDS shuffles
+#ifndef PKV_PERMLANE_MAX
+#define PKV_PERMLANE_MAX 1
+#endif
+__device__ __forceinline__ float row_max4(float x) {
+  if (PKV_PERMLANE_MAX) return quarter_max(x);
+  x = fmaxf(x, xor_shuffle(x, 16));
+  return fmaxf(x, xor_shuffle(x, 32));
+}
+
 // float -> 16-bit storage, round to nearest even; returns the bits
 template <typename T>
 __device__ __forceinline__ unsigned to_bits16(float x);
@@ -941,9 +952,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) sc[i] = key0 + 4 * q4 + i < my_limit[rg] ? sc[i] : kNegInf;
       }
     }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, xor_shuffle(mx, 16));
-    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    const float mx = row_max4(fmax_nan(fmax_nan(sc[0], sc[1]), fmax_nan(sc[2], sc[3])));
     // Lazy rescaling: the reference maximum m_run only moves when a head's
     // block maximum exceeds it by more than kRescaleSlack (log2 units), so the
     // weights stay <= 2^kRescaleSlack and the accumulator is rescaled rarely.
@@ -965,17 +974,18 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       // P^T operand: each weight is split into a 16-bit head plus a 16-bit
       // residual (two MFMAs against the same V tile), so the weights carry
       // about 16 significant bits instead of 8 (bf16) or 11 (fp16)
-      unsigned ph[4], pl[4];
+      float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float pv = pr[i];
-        if constexpr (kFp8) pv *= rr.vs[i];  // FP8: the V scale rides on the weight
-        ph[i] = to_bits16<T>(pv);
-        pl[i] = to_bits16<T>(pv - from_bits16<T>(ph[i]));
+        pv[i] = pr[i];
+        if constexpr (kFp8) pv[i] *= rr.vs[i];  // FP8: the V scale rides on the weight
       }
       l_run[rg] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      const u32x2 pw_hi = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
-      const u32x2 pw_lo = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)};
+      unsigned hi[2], lo[2];
+      split16_pair<T>(pv[0], pv[1], hi[0], lo[0]);
+      split16_pair<T>(pv[2], pv[3], hi[1], lo[1]);
+      const u32x2 pw_hi = {hi[0], hi[1]};
+      const u32x2 pw_lo = {lo[0], lo[1]};
 #pragma unroll
       for (int mt = 0; mt < S::kE; ++mt) {
         const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
@@ -1060,10 +1070,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i)
           sc[4 + i] = (4 * q4 + i < vb && (!kPrefill || key_b + 4 * q4 + i < my_limit[rg])) ? sc[4 + i] : kNegInf;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      mx = fmaxf(mx, xor_shuffle(mx, 16));
-      mx = fmaxf(mx, xor_shuffle(mx, 32));
+      const float mx = row_max4(fmax_nan(fmax_nan(fmax_nan(sc[0], sc[1]), fmax_nan(sc[2], sc[3])),
+                                         fmax_nan(fmax_nan(sc[4], sc[5]), fmax_nan(sc[6], sc[7]))));
       const bool grow = mx > m_run[rg] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
         const float m_new = grow ? mx : m_run[rg];
@@ -1074,20 +1082,20 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         m_run[rg] = m_new;
       }
       const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
-      unsigned ph[8], pl[8];
+      float pv[8];
       float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float pr = __builtin_amdgcn_exp2f(sc[i] - m_use);
         lsum += pr;
-        float pv = pr;
-        if constexpr (kFp8) pv *= i < 4 ? ra.vs[i] : rb.vs[i - 4];
-        ph[i] = to_bits16<T>(pv);
-        pl[i] = to_bits16<T>(pv - from_bits16<T>(ph[i]));
+        pv[i] = pr;
+        if constexpr (kFp8) pv[i] *= i < 4 ? ra.vs[i] : rb.vs[i - 4];
       }
       l_run[rg] += lsum;
-      const u32x4 pw_hi = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16), ph[4] | (ph[5] << 16), ph[6] | (ph[7] << 16)};
-      const u32x4 pw_lo = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16), pl[4] | (pl[5] << 16), pl[6] | (pl[7] << 16)};
+      unsigned hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split16_pair<T>(pv[2 * i], pv[2 * i + 1], hi[i], lo[i]);
+      const u32x4 pw_hi = {hi[0], hi[1], hi[2], hi[3]}, pw_lo = {lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
       for (int mt = 0; mt < S::kE; ++mt) {
         acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
