@@ -168,6 +168,19 @@ __device__ __forceinline__ void split16_pair<_Float16>(float p0, float p1, unsig
                                                                 p1 - static_cast<float>(h[1])));
 }
 
+// Two floats that T represents exactly -> one packed dword (first value in
+// the low half), with one packed conversion (the rounding mode is moot).
+template <typename T>
+__device__ __forceinline__ unsigned pack16_exact(float a, float b);
+template <>
+__device__ __forceinline__ unsigned pack16_exact<__bf16>(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+template <>
+__device__ __forceinline__ unsigned pack16_exact<_Float16>(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 // one QK MFMA step on a 16-byte chunk (16-bit types: 8 elements)
 template <typename T>
 __device__ __forceinline__ f32x4 mfma_qk16(u32x4 a, u32x4 b, f32x4 c);
@@ -345,8 +358,7 @@ template <>
 __device__ __forceinline__ u32x2 fp8x4_to_16<_Float16>(unsigned w) {
   const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
   const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return u32x2{to_bits16<_Float16>(lo[0]) | (to_bits16<_Float16>(lo[1]) << 16),
-               to_bits16<_Float16>(hi[0]) | (to_bits16<_Float16>(hi[1]) << 16)};
+  return u32x2{pack16_exact<_Float16>(lo[0], lo[1]), pack16_exact<_Float16>(hi[0], hi[1])};
 }
 
 // four INT8 codes (one dword, lowest byte first, two's complement) -> two
@@ -356,7 +368,7 @@ __device__ __forceinline__ u32x2 int8x4_to_16(unsigned w) {
   const int s = static_cast<int>(w);
   const float f0 = static_cast<float>((s << 24) >> 24), f1 = static_cast<float>((s << 16) >> 24);
   const float f2 = static_cast<float>((s << 8) >> 24), f3 = static_cast<float>(s >> 24);
-  return u32x2{to_bits16<T>(f0) | (to_bits16<T>(f1) << 16), to_bits16<T>(f2) | (to_bits16<T>(f3) << 16)};
+  return u32x2{pack16_exact<T>(f0, f1), pack16_exact<T>(f2, f3)};
 }
 
 // Cache code formats: kQ = 0 (no codes: the cache holds T), kQFp8 (OCP E4M3),
