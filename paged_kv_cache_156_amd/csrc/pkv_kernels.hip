@@ -82,6 +82,12 @@ constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two til
 #ifndef PKV_AHEAD_PREFILL
 #define PKV_AHEAD_PREFILL 2
 #endif
+#ifndef PKV_PAIR_RING  // tile pairs held in the register ring (16-bit caches)
+#define PKV_PAIR_RING 2
+#endif
+#ifndef PKV_PAIR_RING_8BIT  // the same for 8-bit caches
+#define PKV_PAIR_RING_8BIT 2
+#endif
 #ifndef PKV_RING_ROTATIONS
 #define PKV_RING_ROTATIONS 3
 #endif
@@ -1124,24 +1130,24 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   constexpr int kAhead = kPrefill ? (sizeof(T) == 2 ? PKV_AHEAD_PREFILL : PKV_AHEAD_32BIT)
                                   : (kFp8 ? PKV_AHEAD_FP8 : (sizeof(T) == 2 ? PKV_AHEAD_16BIT : PKV_AHEAD_32BIT));
   constexpr int kRing = kAhead + 1;
-  R ring[kPairs ? 4 : kRing];
-  int ring_rows[kPairs ? 4 : kRing];
+  // pairs held by the ring: kNP - 1 pairs in flight while one is consumed
+  constexpr int kNP = kFp8 ? PKV_PAIR_RING_8BIT : PKV_PAIR_RING;
+  R ring[kPairs ? 2 * kNP : kRing];
+  int ring_rows[kPairs ? 2 * kNP : kRing];
   if constexpr (kPairs) {
-    // two tiles in flight while two are consumed: slots {0,1} and {2,3} alternate
-    // (the same bytes in flight as the single-tile ring with two tiles ahead)
     if (nblk > 0) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2 * (kNP - 1); ++u) {
         const size_t tile = block_src(u, ring_rows[u]);
         load_ring(ring[u], tile, ring_rows[u]);
       }
-      for (int t0 = 0; t0 < nblk; t0 += 4) {
+      for (int t0 = 0; t0 < nblk; t0 += 2 * kNP) {
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int cur = 2 * pp, nxt = 2 - 2 * pp;
+        for (int pp = 0; pp < kNP; ++pp) {
+          const int cur = 2 * pp, nxt = 2 * ((pp + kNP - 1) % kNP);  // slot of the pair kNP - 1 ahead
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const size_t tile = block_src(t0 + 2 * pp + 2 + u, ring_rows[nxt + u]);
+            const size_t tile = block_src(t0 + 2 * (pp + kNP - 1) + u, ring_rows[nxt + u]);
             load_ring(ring[nxt + u], tile, ring_rows[nxt + u]);
           }
           __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
