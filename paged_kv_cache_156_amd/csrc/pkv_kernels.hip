@@ -644,8 +644,20 @@ constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 
 // i sits at position n - q_len + i and attends to positions 0..n - q_len + i
 // (causal attention, "Understanding KV Cache" §1.2; prefill as a matrix
 // product over many query positions, "KV Cache and Inference Optimization").
+// NHD decode may run up to PKV_NHD_WAVES waves per workgroup (the launch's
+// blockDim), one per KV head of a group of consecutive heads: the heads of a
+// cache block are interleaved row by row, so the workgroup's waves together
+// read each block's contiguous [rows, heads, D] bytes at about the same time.
+// Four waves stay within one wave per SIMD, so the register budget is that
+// of a one-wave workgroup. Every other launch is one wave per workgroup.
+#ifndef PKV_NHD_WAVES
+#define PKV_NHD_WAVES 4
+#endif
+template <int kMode, bool kNHD>
+constexpr int kDecodeWaves = (kNHD && kMode != kModePrefill) ? PKV_NHD_WAVES : 1;
+
 template <typename T, int D, int kMode, int kQ, bool kNHD>
-__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((64 * kDecodeWaves<kMode, kNHD>)) void decode_partition_kernel(DecodeArgs a) {
   constexpr bool kFp8 = kQ != 0;  // the caches hold 8-bit codes with per-row scales
   constexpr bool kStep = kMode == kModeStep;
   constexpr bool kPrefill = kMode == kModePrefill;
@@ -657,7 +669,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   constexpr int kR = kPrefillRowGroups<T, kMode>;
   static_assert(!kFp8 || k16, "FP8 caches are read with 16-bit queries");
   constexpr int kRowB = kFp8 ? D : S::kRowBytes;  // one head's cached row, bytes
-  const int lane = threadIdx.x;
+  constexpr int kMaxW = kDecodeWaves<kMode, kNHD>;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
   const int q4 = lane >> 4;
   const int ln = lane & 15;
   // Partition of this workgroup. Workgroups go to the eight XCDs round-robin
@@ -668,8 +681,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   const int p = PKV_XCD_ROTATE ? static_cast<int>((blockIdx.x + blockIdx.y + gridDim.y * blockIdx.z) % gridDim.x)
                                : static_cast<int>(blockIdx.x);
   const int units_per_head = kPrefill ? a.q_tiles : a.head_groups;  // work units per (sequence, KV head)
-  const int j = blockIdx.y / units_per_head;
-  const int ui = blockIdx.y - j * units_per_head;  // head group (decode) or query tile (prefill)
+  const int jg = blockIdx.y / units_per_head;       // KV head, or group of blockDim / 64 heads
+  const int ui = blockIdx.y - jg * units_per_head;  // head group (decode) or query tile (prefill)
+  const int j = kMaxW == 1 ? jg
+                           : jg * static_cast<int>(blockDim.x >> 6) +
+                                 __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int hg = kPrefill ? 0 : ui;
   const int b = blockIdx.z;
 
@@ -1808,17 +1824,39 @@ int32_t partition_blocks_for(int32_t num_seqs, int32_t num_heads, int32_t num_kv
 
 enum Phase : unsigned { kPartitions = 1u, kMerge = 2u, kFusedStep = 4u };
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+// Waves per NHD decode workgroup: the most (up to PKV_NHD_WAVES, dividing the
+// KV head count) that still leave a workgroup for every compute unit.
+int nhd_waves(int64_t waves, int32_t num_kv_heads) {
+  for (int w = PKV_NHD_WAVES; w > 1; w /= 2)
+    if (num_kv_heads % w == 0 && waves / w >= device_cus()) return w;
+  return 1;
+}
+
 template <typename T, int D, int kQ, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
+  static_assert(kDecodeWaves<kModeSplit, kNHD> == kDecodeWaves<kModeStep, kNHD>, "one bound for both modes");
+  const int w = kNHD ? nhd_waves(static_cast<int64_t>(a.num_parts) * a.num_kv_heads * a.head_groups * num_seqs,
+                                 a.num_kv_heads)
+                     : 1;
+  const dim3 grid(a.num_parts, static_cast<unsigned>(a.num_kv_heads / w * a.head_groups), num_seqs);
   if (phases & kFusedStep) {
-    dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64 * w), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
-  if (phases & kPartitions) {
-    dim3 grid(a.num_parts, a.num_kv_heads * a.head_groups, num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kQ, kNHD>), grid, dim3(64), 0, stream, a);
-  }
+  if (phases & kPartitions)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kQ, kNHD>), grid, dim3(64 * w), 0, stream, a);
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3(static_cast<unsigned>(ceil_div64(waves, 4))), dim3(256), 0, stream,
