@@ -644,20 +644,21 @@ constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 
 // i sits at position n - q_len + i and attends to positions 0..n - q_len + i
 // (causal attention, "Understanding KV Cache" §1.2; prefill as a matrix
 // product over many query positions, "KV Cache and Inference Optimization").
-// NHD decode may run up to PKV_NHD_WAVES waves per workgroup (the launch's
-// blockDim), one per KV head of a group of consecutive heads: the heads of a
-// cache block are interleaved row by row, so the workgroup's waves together
-// read each block's contiguous [rows, heads, D] bytes at about the same time.
-// Four waves stay within one wave per SIMD, so the register budget is that
-// of a one-wave workgroup. Every other launch is one wave per workgroup.
-#ifndef PKV_NHD_WAVES
-#define PKV_NHD_WAVES 4
+// Decode may run up to PKV_DECODE_WAVES waves per workgroup (the launch's
+// blockDim), one per KV head of a group of consecutive heads. For NHD caches,
+// whose blocks interleave the heads row by row, the waves together read each
+// block's contiguous [rows, heads, D] bytes at about the same time; for HND
+// caches they read the adjacent per-head tiles of the same blocks. Four waves
+// stay within one wave per SIMD, so the register budget is that of a one-wave
+// workgroup. Prefill launches one wave per workgroup.
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
 #endif
-template <int kMode, bool kNHD>
-constexpr int kDecodeWaves = (kNHD && kMode != kModePrefill) ? PKV_NHD_WAVES : 1;
+template <int kMode>
+constexpr int kDecodeWaves = kMode == kModePrefill ? 1 : PKV_DECODE_WAVES;
 
 template <typename T, int D, int kMode, int kQ, bool kNHD>
-__global__ __launch_bounds__((64 * kDecodeWaves<kMode, kNHD>)) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_kernel(DecodeArgs a) {
   constexpr bool kFp8 = kQ != 0;  // the caches hold 8-bit codes with per-row scales
   constexpr bool kStep = kMode == kModeStep;
   constexpr bool kPrefill = kMode == kModePrefill;
@@ -669,7 +670,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode, kNHD>)) void decode_parti
   constexpr int kR = kPrefillRowGroups<T, kMode>;
   static_assert(!kFp8 || k16, "FP8 caches are read with 16-bit queries");
   constexpr int kRowB = kFp8 ? D : S::kRowBytes;  // one head's cached row, bytes
-  constexpr int kMaxW = kDecodeWaves<kMode, kNHD>;
+  constexpr int kMaxW = kDecodeWaves<kMode>;
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int q4 = lane >> 4;
   const int ln = lane & 15;
@@ -1836,20 +1837,19 @@ int device_cus() {
   }
   return cus[dev];
 }
-// Waves per NHD decode workgroup: the most (up to PKV_NHD_WAVES, dividing the
+// Waves per decode workgroup: the most (up to PKV_DECODE_WAVES, dividing the
 // KV head count) that still leave a workgroup for every compute unit.
-int nhd_waves(int64_t waves, int32_t num_kv_heads) {
-  for (int w = PKV_NHD_WAVES; w > 1; w /= 2)
+int decode_waves(int64_t waves, int32_t num_kv_heads) {
+  for (int w = PKV_DECODE_WAVES; w > 1; w /= 2)
     if (num_kv_heads % w == 0 && waves / w >= device_cus()) return w;
   return 1;
 }
 
 template <typename T, int D, int kQ, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
-  static_assert(kDecodeWaves<kModeSplit, kNHD> == kDecodeWaves<kModeStep, kNHD>, "one bound for both modes");
-  const int w = kNHD ? nhd_waves(static_cast<int64_t>(a.num_parts) * a.num_kv_heads * a.head_groups * num_seqs,
-                                 a.num_kv_heads)
-                     : 1;
+  static_assert(kDecodeWaves<kModeSplit> == kDecodeWaves<kModeStep>, "one bound for both modes");
+  const int w = decode_waves(static_cast<int64_t>(a.num_parts) * a.num_kv_heads * a.head_groups * num_seqs,
+                             a.num_kv_heads);
   const dim3 grid(a.num_parts, static_cast<unsigned>(a.num_kv_heads / w * a.head_groups), num_seqs);
   if (phases & kFusedStep) {
     hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64 * w), 0, stream, a);
