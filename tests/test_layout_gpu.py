@@ -132,3 +132,98 @@ def test_fp8_layout_and_block_size_parity(torch_dev, layout, bs, fmt):
             assert ks.cpu().numpy().tobytes() == ks_o.tobytes() and vs.cpu().numpy().tobytes() == vs_o.tobytes()
             check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype,
                         f"fp8 {layout} bs={bs} pb={pb} fused={fused}")
+
+
+# ---------------------------------------------------------------------------
+# full-size shapes in NHD: enough waves for several waves per decode workgroup
+# ---------------------------------------------------------------------------
+def sampled_reference(torch, wkd, seqs):
+    """Reference outputs of the sampled sequences from their HND blocks (the
+    logical rows do not depend on the layout) plus the appended token."""
+    cfg = wkd.cfg
+    dt = cfg.dtype
+    out = {}
+    for b in seqs:
+        idx = torch.from_numpy(wkd.assignment.blocks[b].astype(np.int64)).to(wkd.k_cache[0].device)
+        kc = wl.torch_to_raw(wkd.k_cache[0].index_select(0, idx), dt)
+        vc = wl.torch_to_raw(wkd.v_cache[0].index_select(0, idx), dt)
+        table = np.arange(len(idx), dtype=np.int32)[None, :]
+        n = int(wkd.context_lens[b])
+        slots = oracle.slot_mapping(table, [n - 1], cfg.block_size)
+        oracle.kv_append(kc, vc, wl.torch_to_raw(wkd.k_new[0][b:b + 1], dt), wl.torch_to_raw(wkd.v_new[0][b:b + 1], dt),
+                         slots, cfg.block_size)
+        out[b] = oracle.decode_attention(wl.torch_to_raw(wkd.q[0][b:b + 1], dt), kc, vc, table, [n], cfg.scale,
+                                         cfg.num_kv_heads, cfg.block_size, dt)[0]
+    return out
+
+
+@pytest.mark.parametrize("mode", ["split", "fused"])
+@pytest.mark.parametrize("cfg_name", ["llama3_70b", "llama3_8b_layer"])
+def test_nhd_full_size_sampled(torch_dev, cfg_name, mode):
+    """The 70B shape (1024 waves: four per workgroup) and the 8B layer (512
+    waves: two per workgroup) with NHD caches; sampled sequences, every query
+    head, against the reference; the appended rows land bit for bit."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME[cfg_name]
+    note(f"NHD full-size {cfg.name} {mode}")
+    wkd = wl.make_device_workload(cfg, dev, layers=1)
+    lens = wkd.context_lens
+    B = len(lens)
+    seqs = sorted({0, B // 2, B - 1})
+    ref = sampled_reference(torch, wkd, seqs)
+    kc = wkd.k_cache[0].transpose(1, 2).contiguous()
+    vc = wkd.v_cache[0].transpose(1, 2).contiguous()
+    out = torch.full_like(wkd.q[0], float("nan"))
+    if mode == "split":
+        slots = pkv.slot_mapping_from_tables(wkd.assignment.table(), lens - 1, cfg.block_size)
+        pkv.kv_append(wkd.k_new[0], wkd.v_new[0], torch.from_numpy(slots).to(dev), kc, vc, layout="NHD")
+        ws = pkv.alloc_workspace(wkd.q[0], kc, wkd.block_tables, layout="NHD")
+        pkv.paged_decode_attention(wkd.q[0], kc, vc, wkd.block_tables, wkd.context_lens_dev, cfg.scale, out, ws,
+                                   layout="NHD")
+    else:
+        ws = pkv.alloc_step_workspace(wkd.q[0], kc, wkd.block_tables, layout="NHD")
+        pkv.decode_step(wkd.q[0], wkd.k_new[0], wkd.v_new[0], kc, vc, wkd.block_tables, wkd.context_lens_dev,
+                        cfg.scale, out, ws, layout="NHD")
+    torch.cuda.synchronize()
+    o = oracle.upcast(wl.torch_to_raw(out, cfg.dtype), cfg.dtype)
+    assert np.isfinite(o).all()
+    for b, r in ref.items():
+        check_close(o[b], r, cfg.dtype, f"NHD {cfg.name} {mode} seq {b}")
+        n = int(lens[b])
+        blk = int(wkd.assignment.blocks[b][(n - 1) // cfg.block_size])
+        got = wl.torch_to_raw(kc[blk, (n - 1) % cfg.block_size], cfg.dtype)
+        assert got.tobytes() == wl.torch_to_raw(wkd.k_new[0][b], cfg.dtype).tobytes()
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+def test_nhd_8bit_full_size_70b_sampled(torch_dev, fmt):
+    """8-bit codes in NHD at the 70B shape (four waves per workgroup), fused
+    step, sampled sequences against the reference over the HND copies."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME["llama3_70b"]
+    note(f"NHD {fmt} full-size 70B fused")
+    wkd = wl.make_device_workload_fp8(cfg, dev, layers=1)
+    seqs = [0, 16, 31]
+    refs = {}
+    for b in seqs:
+        idx = torch.from_numpy(wkd.assignment.blocks[b].astype(np.int64)).to(dev)
+        kc, vc = wkd.k_codes[0].index_select(0, idx).cpu().numpy(), wkd.v_codes[0].index_select(0, idx).cpu().numpy()
+        ks, vs = wkd.k_scales[0].index_select(0, idx).cpu().numpy(), wkd.v_scales[0].index_select(0, idx).cpu().numpy()
+        table = np.arange(len(idx), dtype=np.int32)[None, :]
+        n = int(wkd.context_lens[b])
+        slots = oracle.slot_mapping(table, [n - 1], 16)
+        oracle.kv_append_fp8(kc, vc, ks, vs, wl.torch_to_raw(wkd.k_new[0][b:b + 1], "bf16"),
+                             wl.torch_to_raw(wkd.v_new[0][b:b + 1], "bf16"), slots, 16, "bf16", fmt=fmt)
+        refs[b] = oracle.decode_attention_fp8(wl.torch_to_raw(wkd.q[0][b:b + 1], "bf16"), kc, vc, ks, vs, table, [n],
+                                              cfg.scale, cfg.num_kv_heads, 16, "bf16", fmt=fmt)[0]
+    nhd = lambda x: x.transpose(1, 2).contiguous()
+    kc, vc, ks, vs = nhd(wkd.k_codes[0]), nhd(wkd.v_codes[0]), nhd(wkd.k_scales[0]), nhd(wkd.v_scales[0])
+    out = torch.full_like(wkd.q[0], float("nan"))
+    ws = pkv.alloc_step_workspace(wkd.q[0], kc, wkd.block_tables, layout="NHD")
+    pkv.decode_step_fp8(wkd.q[0], wkd.k_new[0], wkd.v_new[0], kc, vc, ks, vs, wkd.block_tables, wkd.context_lens_dev,
+                        cfg.scale, out, ws, layout="NHD", fmt=fmt)
+    torch.cuda.synchronize()
+    o = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
+    assert np.isfinite(o).all()
+    for b, r in refs.items():
+        check_close(o[b], r, "bf16", f"NHD {fmt} 70B seq {b}")
