@@ -85,11 +85,20 @@ def cpu_samples(wkd, max_seqs=32):
     return samples
 
 
+def cpu_threads():
+    """BLAS threads for the CPU reference: the host's cores, capped by the
+    OMP_NUM_THREADS share the environment grants this process."""
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() else n
+
+
 def run_cpu_baseline(samples, cfg, budget_s):
-    """Time the CPU reference, one thread, until ``budget_s`` of work is done."""
+    """Time the CPU reference (BLAS on cpu_threads() threads) until
+    ``budget_s`` of work is done."""
     import oracle
     from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):
+    with threadpool_limits(cpu_threads()):
         return _run_cpu(samples, cfg, budget_s, oracle)
 
 
@@ -238,17 +247,20 @@ def run_prefill(args):
         vh = wl.torch_to_raw(vc.index_select(0, idx), "bf16")
         qh = wl.torch_to_raw(q[:C], "bf16")
         table = np.arange(len(blocks), dtype=np.int32)[None, :]
+        from threadpoolctl import threadpool_limits
         rows, spent, pairs_cpu = 1, 0.0, 0
-        while spent < min(args.cpu_budget, 10.0) and rows <= C:
-            t = _t.perf_counter()
-            oracle.prefill_attention(qh[:rows], kh, vh, table, [0, rows], [P + rows], cfg.scale, Hkv, bs, "bf16",
-                                     args.layout)
-            spent = _t.perf_counter() - t
-            pairs_cpu = sum(P + i + 1 for i in range(rows))
-            rows *= 2
-        cpu = {"value": round(4 * Hq * D * pairs_cpu / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-               "kind": "oracle", "sample": f"{rows // 2} query tokens of one sequence's chunk, fp64 NumPy, one thread, "
-                                           f"{spent:.1f}s"}
+        nt = cpu_threads()
+        with threadpool_limits(nt):
+            while spent < min(args.cpu_budget, 10.0) and rows <= C:
+                t = _t.perf_counter()
+                oracle.prefill_attention(qh[:rows], kh, vh, table, [0, rows], [P + rows], cfg.scale, Hkv, bs, "bf16",
+                                         args.layout)
+                spent = _t.perf_counter() - t
+                pairs_cpu = sum(P + i + 1 for i in range(rows))
+                rows *= 2
+        cpu = {"value": round(4 * Hq * D * pairs_cpu / spent / 1e12, 6), "unit": "TFLOP/s", "cores": nt,
+               "kind": "oracle", "sample": f"{rows // 2} query tokens of one sequence's chunk, fp64 NumPy with {nt} "
+                                           f"BLAS thread(s), {spent:.1f}s"}
     result = {
         "metric": "chunked-prefill paged attention TFLOP/s (QK^T + PV over the causal triangle)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -422,6 +434,14 @@ def main():
     torch.cuda.synchronize()
     part_ms = [ev[l][0].elapsed_time(ev[l][1]) for ev in events for l in range(L)]
     event_avg_ms = float(np.mean(part_ms))
+    # and once more with an event pair around every step: median and minimum
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step_ev[k][0].record(stream)
+        step()
+        step_ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
     # In fused mode the step is exactly one launch of the kernel per layer, so
     # the timed region's events give its average launch duration directly (an
     # event pair around each launch adds several microseconds of its own).
@@ -453,11 +473,12 @@ def main():
     if samples:
         done, cpu_bytes, cpu_t = run_cpu_baseline(samples, cfg, args.cpu_budget)
         seq_layer_s = cpu_t / done
-        cpu = {"value": round(cpu_bytes / cpu_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        nt = cpu_threads()
+        cpu = {"value": round(cpu_bytes / cpu_t / 1e9, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
                "seqs_per_s": round(1.0 / (seq_layer_s * L), 4),
                "sample": f"{done} sequence-layer(s) (cycling over layer 0's first {len(samples)} sequences) of "
-                         f"{cfg.name}, append + attention in fp64 NumPy on one thread, {cpu_t:.1f}s; seqs/s "
-                         f"extrapolated to {L} layers"}
+                         f"{cfg.name}, append + attention in fp64 NumPy with {nt} BLAS thread(s), {cpu_t:.1f}s; "
+                         f"seqs/s extrapolated to {L} layers"}
         log(f"cpu baseline: {cpu}")
 
     if args.copy_calibration_mib:
@@ -478,6 +499,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
