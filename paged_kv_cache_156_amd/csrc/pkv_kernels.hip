@@ -8,8 +8,9 @@
 // through the block table (page "KV Cache and Inference Optimization",
 // section "PagedAttention"; slot rule of "Understanding KV Cache" §3.3).
 //
-// Work decomposition (one wavefront = one workgroup):
-//   (sequence b, KV head j, head group hg, context partition p).
+// Work decomposition: one wavefront per
+//   (sequence b, KV head j, head group hg, context partition p),
+// up to four such waves (consecutive KV heads) per workgroup.
 // A partition is `pb_per_part` consecutive 16-token blocks of one sequence;
 // the wave streams them once, so each K/V byte is read from HBM exactly once
 // for the whole GQA group. Up to 16 query heads of the group form the N (or M)
@@ -32,7 +33,8 @@
 //    the B operand P^T of the PV product, so P never moves between lanes.
 //  * Output lane (q4, h) holds d = (4*q4 + i) * E + mt: 4E contiguous values.
 // Softmax is online per head (running max m and sum l, log2 domain), with
-// the maxima shared by the four lanes of a head through two xor-shuffles.
+// the maxima shared by the four lanes of a head through two cross-row lane
+// swaps (v_permlane32_swap, v_permlane16_swap).
 // For 16-bit inputs the weights enter the PV MFMA as a 16-bit head plus a
 // 16-bit residual: rounding them once to bf16 would cost ~2^-9 relative per
 // weight, enough to break a 2e-3 absolute bound on short contexts.
@@ -1939,8 +1941,9 @@ StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 }
 // How a prefill launch splits its rows. The LDS kernel serves 16-bit caches
 // and positive finite scales: a work unit is a workgroup of
-// prefill_waves(head_dim) waves with PKV_PREFILL_LDS_ROWS row groups each. 8-bit and fp32 caches take the one-wave tile kernel with
-// prefill_row_groups(dtype) row groups per unit.
+// prefill_waves(head_dim) waves with PKV_PREFILL_LDS_ROWS row groups each.
+// 8-bit and fp32 caches (and other scales) take the one-wave tile kernel
+// with prefill_row_groups(dtype) row groups per unit.
 struct PrefillPlan {
   bool lds;
   int32_t rows_per_unit;   // (token, head) rows of one KV head per work unit
