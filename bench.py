@@ -177,7 +177,8 @@ def run_copy_blocks(args):
                                f"128 dims bf16 (32 KiB per block per tensor), one launch", "pairs": n},
         "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": bytes_launch, "avg_launch_us": round(ms * 1e3, 2)},
+                     "alg_bytes_per_launch": bytes_launch, "avg_launch_us": round(ms * 1e3, 2),
+                     "kernel_sha": kernel_sha()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -271,7 +272,7 @@ def run_prefill(args):
                    "context": P, "partition_blocks": pb},
         "roofline": {"bound": "mfma", "kernel": "prefill_lds_kernel", "achieved": round(tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
-                     "alg_flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2)},
+                     "alg_flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2), "kernel_sha": kernel_sha()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
