@@ -14,7 +14,7 @@ from paged_kv_cache_156_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 # (tokens cached before the chunk, chunk length) per sequence
-CHUNKS = ((0, 1), (0, 37), (100, 16), (15, 3), (513, 64), (1000, 130), (2040, 9))
+CHUNKS = ((0, 1), (0, 37), (100, 16), (15, 3), (40, 0), (513, 64), (48, 16), (1000, 130), (2040, 9))
 
 
 @pytest.fixture(scope="module")
