@@ -344,9 +344,12 @@ pkv_status pkv_prefill_attention_int8(const void* q, const void* k_cache, const 
  *   workspace     >= pkv_prefill_workspace_bytes(...) bytes, zero-filled before
  *                 its first use; each completed call leaves its counters at
  *                 zero (calls sharing a workspace must not overlap)
- * Every other argument as pkv_paged_decode_attention. Work unit: 16 (query
- * token, query head) rows of one KV head, one context partition; split
- * contexts are merged in the kernel by the partition that finishes last.
+ * Every other argument as pkv_paged_decode_attention. Work unit: a group of
+ * (query token, query head) rows of one KV head and one context partition --
+ * 128 rows in a four-wave workgroup that shares each K/V tile through LDS for
+ * 16-bit caches and scale > 0, 64 (16-bit) or 32 (fp32) rows in one wave
+ * otherwise; split contexts are merged in the kernel by the partition that
+ * finishes last. The workspace size covers every variant.
  * Errors as pkv_paged_decode_attention.
  */
 size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
