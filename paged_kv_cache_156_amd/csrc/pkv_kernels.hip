@@ -1283,32 +1283,37 @@ constexpr int kXcds = 8;  // MI355X: eight accelerator complex dies
 #ifndef PKV_PREFILL_LDS_ROWS
 #define PKV_PREFILL_LDS_ROWS 2  // 16-row groups per wave
 #endif
+#ifndef PKV_PREFILL_TILES
+#define PKV_PREFILL_TILES 4  // 16-row key tiles per softmax step (2 or 4)
+#endif
 #ifndef PKV_PREFILL_WAVES
 #define PKV_PREFILL_WAVES 4  // waves per workgroup (head size 128; 4 for 64)
 #endif
 constexpr int prefill_waves(int head_dim) { return head_dim == 64 ? 4 : PKV_PREFILL_WAVES; }
 
-template <typename T, int D, bool kNHD, int kW, int kR>
+template <typename T, int D, bool kNHD, int kW, int kR, int kT>
 __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
   static_assert(sizeof(T) == 2, "the LDS prefill reads 16-bit caches");
-  constexpr int kNK = S::kNK;                        // K fragments per tile
-  constexpr int kKBytes = 2 * kNK * 1024;            // K of a tile pair, fragment order
-  constexpr int kVBytes = 2 * kTile * S::kRowBytes;  // V of a tile pair, row order
+  static_assert(kT == 2 || kT == 4, "two or four tiles per step");
+  constexpr int kNK = S::kNK;                         // K fragments per tile
+  constexpr int kKBytes = kT * kNK * 1024;            // K of a step's tiles, fragment order
+  constexpr int kVBytes = kT * kTile * S::kRowBytes;  // V of a step's tiles, row order
   constexpr int kBuf = kKBytes + kVBytes;
+  constexpr int kBufs = kT == 2 ? 3 : 2;  // LDS buffers: loads run kBufs - 1 steps ahead
   constexpr int kThreads = 64 * kW;
-  constexpr int kKLoads = kKBytes / 16 / kThreads;  // 16-byte loads per thread per pair
+  constexpr int kKLoads = kKBytes / 16 / kThreads;  // 16-byte loads per thread per step
   constexpr int kVLoads = kVBytes / 16 / kThreads;
   constexpr int kRowChunks = S::kRowBytes / 16;
   constexpr int kVTileChunks = kTile * kRowChunks;
   static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kVBytes,
-                "a tile pair splits evenly over the workgroup");
+                "a step's tiles split evenly over the workgroup");
   static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
-  // three LDS buffers as separate objects: the compiler then tracks which
+  // the LDS buffers as separate objects: the compiler then tracks which
   // buffer each cache -> LDS load writes and waits only for the right ones
   __shared__ __attribute__((aligned(16))) char lds0[kBuf];
   __shared__ __attribute__((aligned(16))) char lds1[kBuf];
-  __shared__ __attribute__((aligned(16))) char lds2[kBuf];
+  __shared__ __attribute__((aligned(16))) char lds2[kBufs > 2 ? kBuf : 16];
 
   // The lambdas below capture only locals: a lambda that referenced `a`
   // would take its address, and next to the cache -> LDS loads (which may
@@ -1409,43 +1414,43 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     return ok ? static_cast<size_t>(r) : 0;
   };
 
-  const int nsteps = (nblk + 1) / 2;  // tile pairs of the partition
-  // cache -> LDS for the tile pair of step s, straight into LDS buffer `dst`
+  const int nsteps = (nblk + kT - 1) / kT;  // steps of kT tiles
+  // cache -> LDS for the kT tiles of step s, straight into LDS buffer `dst`
   // (buffer loads with the LDS flag: lane l's 16 bytes land at M0 + 16 l)
   auto fetch = [&](int s, char* dst) __attribute__((always_inline)) {
-    int va, vb;
-    const size_t ra = tile_src(2 * s, va);
-    const size_t rb = tile_src(2 * s + 1, vb);
-    const __amdgpu_buffer_rsrc_t rka = tile_rsrc(k_cache + ra * S::kRowBytes, va * rs);
-    const __amdgpu_buffer_rsrc_t rkb = tile_rsrc(k_cache + rb * S::kRowBytes, vb * rs);
-    const __amdgpu_buffer_rsrc_t rva = tile_rsrc(v_cache + ra * S::kRowBytes, va * rs);
-    const __amdgpu_buffer_rsrc_t rvb = tile_rsrc(v_cache + rb * S::kRowBytes, vb * rs);
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
-      // fragment f = w + kW i of the pair: tile f / kNK, chunk group cg = f % kNK;
+      // fragment f = w + kW i of the step: tile f / kNK, chunk group cg = f % kNK;
       // lane (q4, ln) takes token ln's 16-byte chunk 4 cg + q4
       const int f = w + kW * i;
       const int cg = f % kNK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(f < kNK ? rka : rkb, lds_ptr(dst + f * 1024), 16,
-                                               ln * rs + (4 * cg + q4) * 16, 0, 0, 0);
+      int valid;
+      const size_t r0 = tile_src(kT * s + f / kNK, valid);
+      // (a named resource: passed as a temporary, the host pass drops the kernel's launch stub)
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_cache + r0 * S::kRowBytes, valid * rs);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dst + f * 1024), 16, ln * rs + (4 * cg + q4) * 16, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
-      const int cw = 64 * w + kThreads * i;  // the wave's first V chunk of the pair
+      const int cw = 64 * w + kThreads * i;  // the wave's first V chunk of the step
       const int u = cw / kVTileChunks;
       const int ch = cw - u * kVTileChunks + lane;
       const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(u == 0 ? rva : rvb, lds_ptr(dst + kKBytes + cw * 16), 16,
-                                               row * rs + col * 16, 0, 0, 0);
+      int valid;
+      const size_t r0 = tile_src(kT * s + u, valid);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_cache + r0 * S::kRowBytes, valid * rs);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dst + kKBytes + cw * 16), 16, row * rs + col * 16, 0, 0, 0);
     }
   };
   // every wave's loads into the next buffer have landed once each wave has
-  // drained its own (all but the kLoads just issued) and the barrier is passed
+  // drained its own (all but those of the steps further ahead) and the
+  // barrier is passed
   constexpr int kLoads = kKLoads + kVLoads;
-  static_assert(kLoads < 16, "vmcnt field");
-  auto sync_pair = [&]() __attribute__((always_inline)) {
+  constexpr int kNewer = (kBufs - 2) * kLoads;  // loads that may stay in flight
+  static_assert(kNewer < 16, "vmcnt field");
+  auto sync_step = [&]() __attribute__((always_inline)) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xF70 | kLoads);  // vmcnt <= kLoads (expcnt, lgkmcnt: no wait)
+    __builtin_amdgcn_s_waitcnt(0xF70 | kNewer);  // vmcnt <= kNewer (expcnt, lgkmcnt: no wait)
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
@@ -1461,94 +1466,54 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     l_run[rg] = 0.f;
   }
 
-  // QK^T of pair s (its K fragments at kl) for every row group; zero for a
-  // pair past the partition or past every row's position
-  auto scores = [&](const char* kl, int s, f32x4 (&sa)[kR], f32x4 (&sb)[kR]) __attribute__((always_inline)) {
+  // QK^T of step s (its K fragments at kl) for every row group and tile
+  auto scores = [&](const char* kl, f32x4 (&sc)[kR][kT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rg = 0; rg < kR; ++rg) sa[rg] = sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!wave_rows || s >= nsteps || (blk0 + 2 * s) * kTile >= n_w) return;  // wave-uniform
+    for (int rg = 0; rg < kR; ++rg)
+#pragma unroll
+      for (int u = 0; u < kT; ++u) sc[rg][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < kNK; ++cc) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(kl + cc * 1024 + lane * 16);
-      const u32x4 kb = *reinterpret_cast<const u32x4*>(kl + (kNK + cc) * 1024 + lane * 16);
+      u32x4 kf[kT];
 #pragma unroll
-      for (int rg = 0; rg < kR; ++rg) {
-        sa[rg] = mfma_qk16<T>(ka, qv[rg][cc], sa[rg]);
-        sb[rg] = mfma_qk16<T>(kb, qv[rg][cc], sb[rg]);
-      }
+      for (int u = 0; u < kT; ++u) kf[u] = *reinterpret_cast<const u32x4*>(kl + (u * kNK + cc) * 1024 + lane * 16);
+#pragma unroll
+      for (int rg = 0; rg < kR; ++rg)
+#pragma unroll
+        for (int u = 0; u < kT; ++u) sc[rg][u] = mfma_qk16<T>(kf[u], qv[rg][cc], sc[rg][u]);
     }
   };
-  // online-softmax step and PV product of pair s (its V rows at vl)
-  auto attend = [&](const char* vl, int s, const f32x4 (&sa)[kR], const f32x4 (&sb)[kR])
-                    __attribute__((always_inline)) {
-    const int key_a = (blk0 + 2 * s) * kTile, key_b = key_a + kTile;
-    if (!wave_rows || key_a >= n_w) return;  // wave-uniform: the pair lies past every row's position
-    int va, vb;
-    tile_src(2 * s, va);
-    tile_src(2 * s + 1, vb);
-    // V rows 4*q4 + i of both tiles, this lane's E elements, packed into the
-    // A operand of each output block mt (K index: tile a's rows, then tile b's)
-    unsigned v_a[4][S::kVDW], v_b[4][S::kVDW];
+  // online-softmax step and PV products of step s (its V rows at vl); the
+  // scores are raw (the scale c = qk_scale > 0 is applied inside the
+  // exponent: max(c s) = c max(s)) and masked keys score -inf
+  auto attend = [&](const char* vl, int s, f32x4 (&sc)[kR][kT]) __attribute__((always_inline)) {
+    const int key0 = (blk0 + kT * s) * kTile;
+    int valid[kT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* ra = vl + (4 * q4 + i) * S::kRowBytes + ln * S::kE * 2;
-      const char* rb = ra + kTile * S::kRowBytes;
-      if constexpr (S::kVDW == 4) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(ra);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(rb);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          v_a[i][d] = x[d];
-          v_b[i][d] = y[d];
-        }
-      } else {
-        static_assert(S::kVDW == 2, "16-bit rows of 64 or 128 elements");
-        const u32x2 x = *reinterpret_cast<const u32x2*>(ra);
-        const u32x2 y = *reinterpret_cast<const u32x2*>(rb);
-        v_a[i][0] = x[0];
-        v_a[i][1] = x[1];
-        v_b[i][0] = y[0];
-        v_b[i][1] = y[1];
-      }
-    }
-    u32x4 av[S::kE];
-#pragma unroll
-    for (int mt = 0; mt < S::kE; ++mt) {
-      const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
-      av[mt] = u32x4{__builtin_amdgcn_perm(v_a[1][mt >> 1], v_a[0][mt >> 1], sel),
-                     __builtin_amdgcn_perm(v_a[3][mt >> 1], v_a[2][mt >> 1], sel),
-                     __builtin_amdgcn_perm(v_b[1][mt >> 1], v_b[0][mt >> 1], sel),
-                     __builtin_amdgcn_perm(v_b[3][mt >> 1], v_b[2][mt >> 1], sel)};
-    }
-    // Raw scores; the scale c = qk_scale > 0 is applied inside the exponent
-    // (max(c s) = c max(s)). Masked keys score -inf.
-    float sc[kR][8], mx[kR];
+    for (int u = 0; u < kT; ++u) tile_src(kT * s + u, valid[u]);
+    float mx[kR];
     bool grow_any = false;
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[rg][i] = sa[rg][i];
-        sc[rg][4 + i] = sb[rg][i];
-      }
-      // rows past a tile's valid count were not fetched (they read as zero);
-      // keys past a row's position are masked (both tests are wave-uniform)
-      if (va < kTile || key_a + kTile > min_limit) {
+      for (int u = 0; u < kT; ++u) {
+        // rows past a tile's valid count were not fetched (they read as
+        // zero); keys past a row's position are masked (wave-uniform tests)
+        const int key = key0 + u * kTile;
+        if (valid[u] < kTile || key + kTile > min_limit) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[rg][i] = (4 * q4 + i < va && key_a + 4 * q4 + i < my_limit[rg]) ? sc[rg][i] : kNegInf;
+          for (int i = 0; i < 4; ++i)
+            sc[rg][u][i] = (4 * q4 + i < valid[u] && key + 4 * q4 + i < my_limit[rg]) ? sc[rg][u][i] : kNegInf;
+        }
       }
-      if (vb < kTile || key_b + kTile > min_limit) {
+      float m4 = kNegInf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[rg][4 + i] = (4 * q4 + i < vb && key_b + 4 * q4 + i < my_limit[rg]) ? sc[rg][4 + i] : kNegInf;
-      }
-      const float m8 = fmax_nan(fmax_nan(fmax_nan(sc[rg][0], sc[rg][1]), fmax_nan(sc[rg][2], sc[rg][3])),
-                                fmax_nan(fmax_nan(sc[rg][4], sc[rg][5]), fmax_nan(sc[rg][6], sc[rg][7])));
-      mx[rg] = quarter_max(m8) * c;  // -inf stays -inf (c > 0)
+      for (int u = 0; u < kT; ++u)
+        m4 = fmax_nan(m4, fmax_nan(fmax_nan(sc[rg][u][0], sc[rg][u][1]), fmax_nan(sc[rg][u][2], sc[rg][u][3])));
+      mx[rg] = quarter_max(m4) * c;  // -inf stays -inf (c > 0)
       grow_any |= mx[rg] > m_run[rg] + kRescaleSlack;
     }
-    // one wave-uniform rescale decision for all row groups of the pair
+    // one wave-uniform rescale decision for all row groups of the step
     if (__builtin_amdgcn_ballot_w64(grow_any)) {
 #pragma unroll
       for (int rg = 0; rg < kR; ++rg) {
@@ -1561,46 +1526,92 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         m_run[rg] = m_new;
       }
     }
+    // weights as 16-bit head + residual, per pair of tiles: the MFMA's K index
+    // runs over tile 2pp's rows 4*q4 .. 4*q4+3, then tile 2pp+1's
+    u32x4 pw_hi[kR][kT / 2], pw_lo[kR][kT / 2];
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg) {
       const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
-      float pr[8];
       float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rg][i], c, -m_use));
-        lsum += pr[i];
+      for (int pp = 0; pp < kT / 2; ++pp) {
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rg][2 * pp + i / 4][i % 4], c, -m_use));
+          lsum += pr[i];
+        }
+        unsigned hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split16_pair<T>(pr[2 * i], pr[2 * i + 1], hi[i], lo[i]);
+        pw_hi[rg][pp] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        pw_lo[rg][pp] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       }
       l_run[rg] += lsum;
-      unsigned hi[4], lo[4];
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) split16_pair<T>(pr[2 * i], pr[2 * i + 1], hi[i], lo[i]);
-      const u32x4 pw_hi = {hi[0], hi[1], hi[2], hi[3]}, pw_lo = {lo[0], lo[1], lo[2], lo[3]};
-  #pragma unroll
+    for (int pp = 0; pp < kT / 2; ++pp) {
+      // V rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's E elements,
+      // packed into the A operand of each output block mt
+      unsigned v_a[4][S::kVDW], v_b[4][S::kVDW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* ra = vl + (2 * pp * kTile + 4 * q4 + i) * S::kRowBytes + ln * S::kE * 2;
+        const char* rb = ra + kTile * S::kRowBytes;
+        if constexpr (S::kVDW == 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(ra);
+          const u32x4 y = *reinterpret_cast<const u32x4*>(rb);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            v_a[i][d] = x[d];
+            v_b[i][d] = y[d];
+          }
+        } else {
+          static_assert(S::kVDW == 2, "16-bit rows of 64 or 128 elements");
+          const u32x2 x = *reinterpret_cast<const u32x2*>(ra);
+          const u32x2 y = *reinterpret_cast<const u32x2*>(rb);
+          v_a[i][0] = x[0];
+          v_a[i][1] = x[1];
+          v_b[i][0] = y[0];
+          v_b[i][1] = y[1];
+        }
+      }
+#pragma unroll
       for (int mt = 0; mt < S::kE; ++mt) {
-        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
-        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo, acc[rg][mt]);
+        const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
+        const u32x4 av = {__builtin_amdgcn_perm(v_a[1][mt >> 1], v_a[0][mt >> 1], sel),
+                          __builtin_amdgcn_perm(v_a[3][mt >> 1], v_a[2][mt >> 1], sel),
+                          __builtin_amdgcn_perm(v_b[1][mt >> 1], v_b[0][mt >> 1], sel),
+                          __builtin_amdgcn_perm(v_b[3][mt >> 1], v_b[2][mt >> 1], sel)};
+#pragma unroll
+        for (int rg = 0; rg < kR; ++rg) {
+          acc[rg][mt] = mfma_qk16<T>(av, pw_hi[rg][pp], acc[rg][mt]);
+          acc[rg][mt] = mfma_qk16<T>(av, pw_lo[rg][pp], acc[rg][mt]);
+        }
       }
-      }
+    }
   };
 
-  // Three buffers, loads two pairs ahead: step s consumes buffer s % 3 while
-  // pairs s+1 and s+2 load; its barrier makes pair s+1 visible and frees
-  // buffer s % 3 for pair s+3. Past the partition end the loads fetch nothing.
-  fetch(0, lds0);
-  fetch(1, lds1);
-  sync_pair();
+  // kBufs buffers, loads kBufs - 1 steps ahead: step s consumes buffer
+  // s % kBufs while the next steps load; its barrier makes step s+1 visible
+  // and frees buffer s % kBufs. Past the partition end the loads fetch nothing.
+  char* const bufs[3] = {lds0, lds1, lds2};
+#pragma unroll
+  for (int u = 0; u < kBufs - 1; ++u) fetch(u, bufs[u]);
+  sync_step();
   auto step = [&](int s, const char* cur, char* ahead) __attribute__((always_inline)) {
-    fetch(s + 2, ahead);
-    f32x4 sa[kR], sb[kR];
-    scores(cur, s, sa, sb);
-    attend(cur + kKBytes, s, sa, sb);
-    sync_pair();
+    fetch(s + kBufs - 1, ahead);
+    if (wave_rows && (blk0 + kT * s) * kTile < n_w) {  // wave-uniform: some key of the step is visible
+      f32x4 sc[kR][kT];
+      scores(cur, sc);
+      attend(cur + kKBytes, s, sc);
+    }
+    sync_step();
   };
-  for (int s0 = 0; s0 < nsteps; s0 += 3) {
-    step(s0, lds0, lds2);
-    if (s0 + 1 < nsteps) step(s0 + 1, lds1, lds0);
-    if (s0 + 2 < nsteps) step(s0 + 2, lds2, lds1);
+  for (int s0 = 0; s0 < nsteps; s0 += kBufs) {
+#pragma unroll
+    for (int u = 0; u < kBufs; ++u)
+      if (u == 0 || s0 + u < nsteps) step(s0 + u, bufs[u], bufs[(u + kBufs - 1) % kBufs]);
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // no load into LDS outlives the workgroup
   if (!wave_rows) return;
@@ -1884,9 +1895,9 @@ pkv_status launch_prefill(const DecodeArgs& a, int32_t num_seqs, hipStream_t str
 template <typename T, int D>
 pkv_status launch_prefill_lds(const DecodeArgs& a, int32_t num_seqs, hipStream_t stream, bool nhd) {
   dim3 grid(a.num_parts, a.num_kv_heads * a.q_tiles, num_seqs);
-  constexpr int kW = prefill_waves(D), kR = PKV_PREFILL_LDS_ROWS;
-  if (nhd) hipLaunchKernelGGL((prefill_lds_kernel<T, D, true, kW, kR>), grid, dim3(64 * kW), 0, stream, a);
-  else hipLaunchKernelGGL((prefill_lds_kernel<T, D, false, kW, kR>), grid, dim3(64 * kW), 0, stream, a);
+  constexpr int kW = prefill_waves(D), kR = PKV_PREFILL_LDS_ROWS, kT = PKV_PREFILL_TILES;
+  if (nhd) hipLaunchKernelGGL((prefill_lds_kernel<T, D, true, kW, kR, kT>), grid, dim3(64 * kW), 0, stream, a);
+  else hipLaunchKernelGGL((prefill_lds_kernel<T, D, false, kW, kR, kT>), grid, dim3(64 * kW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
