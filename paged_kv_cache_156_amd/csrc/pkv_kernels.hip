@@ -1416,19 +1416,32 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 
   const int nsteps = (nblk + kT - 1) / kT;  // steps of kT tiles
   // cache -> LDS for the kT tiles of step s, straight into LDS buffer `dst`
-  // (buffer loads with the LDS flag: lane l's 16 bytes land at M0 + 16 l)
-  auto fetch = [&](int s, char* dst) __attribute__((always_inline)) {
+  // (buffer loads with the LDS flag: lane l's 16 bytes land at M0 + 16 l);
+  // each tile's valid row count goes to `valid` for the step's softmax
+  auto fetch = [&](int s, char* dst, int (&valid)[kT]) __attribute__((always_inline)) {
+    __amdgpu_buffer_rsrc_t rk[kT], rv[kT];
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      const size_t r0 = tile_src(kT * s + u, valid[u]);
+      rk[u] = tile_rsrc(k_cache + r0 * S::kRowBytes, valid[u] * rs);
+      rv[u] = tile_rsrc(v_cache + r0 * S::kRowBytes, valid[u] * rs);
+    }
+    // the tile of a wave's i-th load: t0, or t0 + 1 for the upper half of the
+    // waves where one tile's K (or V) is half of what the workgroup loads at once
+    constexpr bool kKHalf = kNK < kW, kVHalf = kVTileChunks < 64 * kW;
+    static_assert(kNK == kW || 2 * kNK == kW, "four waves, 64- or 128-element rows");
+    static_assert(kVTileChunks == 64 * kW || 2 * kVTileChunks == 64 * kW, "V chunks per tile");
+    auto pick = [&](const __amdgpu_buffer_rsrc_t (&r)[kT], int t0, bool half) __attribute__((always_inline)) {
+      return half && w >= kW / 2 ? r[t0 + 1] : r[t0];
+    };
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       // fragment f = w + kW i of the step: tile f / kNK, chunk group cg = f % kNK;
       // lane (q4, ln) takes token ln's 16-byte chunk 4 cg + q4
       const int f = w + kW * i;
       const int cg = f % kNK;
-      int valid;
-      const size_t r0 = tile_src(kT * s + f / kNK, valid);
-      // (a named resource: passed as a temporary, the host pass drops the kernel's launch stub)
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_cache + r0 * S::kRowBytes, valid * rs);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dst + f * 1024), 16, ln * rs + (4 * cg + q4) * 16, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t r = pick(rk, kW * i / kNK, kKHalf);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + f * 1024), 16, ln * rs + (4 * cg + q4) * 16, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
@@ -1436,10 +1449,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
       const int u = cw / kVTileChunks;
       const int ch = cw - u * kVTileChunks + lane;
       const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
-      int valid;
-      const size_t r0 = tile_src(kT * s + u, valid);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_cache + r0 * S::kRowBytes, valid * rs);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dst + kKBytes + cw * 16), 16, row * rs + col * 16, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t r = pick(rv, kThreads * i / kVTileChunks, kVHalf);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + kKBytes + cw * 16), 16, row * rs + col * 16, 0, 0, 0);
     }
   };
   // every wave's loads into the next buffer have landed once each wave has
@@ -1486,11 +1497,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   // online-softmax step and PV products of step s (its V rows at vl); the
   // scores are raw (the scale c = qk_scale > 0 is applied inside the
   // exponent: max(c s) = c max(s)) and masked keys score -inf
-  auto attend = [&](const char* vl, int s, f32x4 (&sc)[kR][kT]) __attribute__((always_inline)) {
+  auto attend = [&](const char* vl, int s, f32x4 (&sc)[kR][kT], const int (&valid)[kT])
+                    __attribute__((always_inline)) {
     const int key0 = (blk0 + kT * s) * kTile;
-    int valid[kT];
-#pragma unroll
-    for (int u = 0; u < kT; ++u) tile_src(kT * s + u, valid[u]);
     float mx[kR];
     bool grow_any = false;
 #pragma unroll
@@ -1498,12 +1507,13 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < kT; ++u) {
         // rows past a tile's valid count were not fetched (they read as
-        // zero); keys past a row's position are masked (wave-uniform tests)
+        // zero); keys past a row's position are masked: lane (q4, .) keeps
+        // its rows 4*q4 + i below both limits (the test to enter is wave-uniform)
         const int key = key0 + u * kTile;
         if (valid[u] < kTile || key + kTile > min_limit) {
+          const int lim = min(valid[u], my_limit[rg] - key) - 4 * q4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sc[rg][u][i] = (4 * q4 + i < valid[u] && key + 4 * q4 + i < my_limit[rg]) ? sc[rg][u][i] : kNegInf;
+          for (int i = 0; i < 4; ++i) sc[rg][u][i] = i < lim ? sc[rg][u][i] : kNegInf;
         }
       }
       float m4 = kNegInf;
@@ -1596,22 +1606,23 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   // s % kBufs while the next steps load; its barrier makes step s+1 visible
   // and frees buffer s % kBufs. Past the partition end the loads fetch nothing.
   char* const bufs[3] = {lds0, lds1, lds2};
+  int valid[kBufs][kT];  // valid rows of the tiles in each buffer
 #pragma unroll
-  for (int u = 0; u < kBufs - 1; ++u) fetch(u, bufs[u]);
+  for (int u = 0; u < kBufs - 1; ++u) fetch(u, bufs[u], valid[u]);
   sync_step();
-  auto step = [&](int s, const char* cur, char* ahead) __attribute__((always_inline)) {
-    fetch(s + kBufs - 1, ahead);
+  auto step = [&](int s, int cur, int ahead) __attribute__((always_inline)) {
+    fetch(s + kBufs - 1, bufs[ahead], valid[ahead]);
     if (wave_rows && (blk0 + kT * s) * kTile < n_w) {  // wave-uniform: some key of the step is visible
       f32x4 sc[kR][kT];
-      scores(cur, sc);
-      attend(cur + kKBytes, s, sc);
+      scores(bufs[cur], sc);
+      attend(bufs[cur] + kKBytes, s, sc, valid[cur]);
     }
     sync_step();
   };
   for (int s0 = 0; s0 < nsteps; s0 += kBufs) {
 #pragma unroll
     for (int u = 0; u < kBufs; ++u)
-      if (u == 0 || s0 + u < nsteps) step(s0 + u, bufs[u], bufs[(u + kBufs - 1) % kBufs]);
+      if (u == 0 || s0 + u < nsteps) step(s0 + u, u, (u + kBufs - 1) % kBufs);
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // no load into LDS outlives the workgroup
   if (!wave_rows) return;
