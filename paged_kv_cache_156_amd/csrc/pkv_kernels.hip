@@ -409,6 +409,39 @@ __device__ __forceinline__ void codes_to_16(const Fp8Regs<D>& r, BlockRegs<T, D>
     }
 }
 
+// K chunks of an 8-bit raw block -> the 16-bit A operands of the QK MFMAs
+template <int kQ, typename T, int D>
+__device__ __forceinline__ void codes_k_to_16(const Fp8Regs<D>& r, BlockRegs<T, D>& o) {
+#pragma unroll
+  for (int c = 0; c < Shape<T, D>::kNK; ++c) {  // chunk c = code bytes 8c..8c+7 of the lane's slice
+    const u32x2 a = codes4_to_16<kQ, T>(r.k[c >> 1][(c & 1) * 2]);
+    const u32x2 b = codes4_to_16<kQ, T>(r.k[c >> 1][(c & 1) * 2 + 1]);
+    o.k[c] = u32x4{a[0], a[1], b[0], b[1]};
+  }
+}
+
+// V of a pair of 8-bit raw blocks -> the A operand of each output block mt of
+// the 16x16x32 PV MFMA (dwords: rows (0,1) and (2,3) of tile a, then of tile
+// b, at element mt). The codes of two rows are interleaved byte by byte
+// first, so every converted pair is already (row 2i, row 2i + 1) at one
+// element: no 16-bit shuffles after the conversion.
+template <int kQ, typename T, int D>
+__device__ __forceinline__ void codes_v_operand(const Fp8Regs<D>& a, const Fp8Regs<D>& b, u32x4 (&av)[D / 16]) {
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w)  // code dword w of a row: elements 4w .. 4w+3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {   // dword q of the operand: tile q / 2, rows 2 (q % 2), 2 (q % 2) + 1
+      const Fp8Regs<D>& t = q < 2 ? a : b;
+      const unsigned c0 = t.v[2 * (q & 1)][w], c1 = t.v[2 * (q & 1) + 1][w];
+      const u32x2 lo = codes4_to_16<kQ, T>(__builtin_amdgcn_perm(c1, c0, 0x05010400u));  // elements 4w, 4w+1
+      const u32x2 hi = codes4_to_16<kQ, T>(__builtin_amdgcn_perm(c1, c0, 0x07030602u));  // elements 4w+2, 4w+3
+      av[4 * w][q] = lo[0];
+      av[4 * w + 1][q] = lo[1];
+      av[4 * w + 2][q] = hi[0];
+      av[4 * w + 3][q] = hi[1];
+    }
+}
+
 // Quantize values of one token row given the row's absolute maximum and the
 // format's largest code Q (448 for E4M3, 127 for INT8): scale = amax / Q,
 // inv = Q / amax (both fp32; amax == 0 -> 1, 1), and each code is the nearest
@@ -1054,27 +1087,28 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
     BlockRegs<T, D> ca, cb;
     BlockRegs<T, D>* pa;
     BlockRegs<T, D>* pb2;
+    // V operands over both tiles, shared by the row groups
+    u32x4 av[S::kE];
     if constexpr (kFp8) {
-      codes_to_16<kQ, T, D>(ra, ca);
-      codes_to_16<kQ, T, D>(rb, cb);
+      codes_k_to_16<kQ, T, D>(ra, ca);
+      codes_k_to_16<kQ, T, D>(rb, cb);
+      codes_v_operand<kQ, T, D>(ra, rb, av);
       pa = &ca;
       pb2 = &cb;
     } else {
       pa = &ra;
       pb2 = &rb;
+#pragma unroll
+      for (int mt = 0; mt < S::kE; ++mt) {
+        const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
+        av[mt] = u32x4{__builtin_amdgcn_perm(ra.v[1][mt >> 1], ra.v[0][mt >> 1], sel),
+                       __builtin_amdgcn_perm(ra.v[3][mt >> 1], ra.v[2][mt >> 1], sel),
+                       __builtin_amdgcn_perm(rb.v[1][mt >> 1], rb.v[0][mt >> 1], sel),
+                       __builtin_amdgcn_perm(rb.v[3][mt >> 1], rb.v[2][mt >> 1], sel)};
+      }
     }
     BlockRegs<T, D>& A = *pa;
     BlockRegs<T, D>& Bt = *pb2;
-    // V operands over both tiles, shared by the row groups
-    u32x4 av[S::kE];
-#pragma unroll
-    for (int mt = 0; mt < S::kE; ++mt) {
-      const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
-      av[mt] = u32x4{__builtin_amdgcn_perm(A.v[1][mt >> 1], A.v[0][mt >> 1], sel),
-                     __builtin_amdgcn_perm(A.v[3][mt >> 1], A.v[2][mt >> 1], sel),
-                     __builtin_amdgcn_perm(Bt.v[1][mt >> 1], Bt.v[0][mt >> 1], sel),
-                     __builtin_amdgcn_perm(Bt.v[3][mt >> 1], Bt.v[2][mt >> 1], sel)};
-    }
     const int key_a = (blk0 + ta) * kTile, key_b = (blk0 + tb) * kTile;
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg) {
