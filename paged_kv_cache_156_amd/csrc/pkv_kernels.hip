@@ -106,6 +106,8 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask) {
 }
 
 using lds_void = __attribute__((address_space(3))) void;
+using s16x4_t = short __attribute__((ext_vector_type(4)));
+using lds_s16x4 = __attribute__((address_space(3))) s16x4_t;
 __device__ __forceinline__ lds_void* lds_ptr(char* p) { return (lds_void*)(p); }
 
 // IEEE maximum (a NaN operand gives NaN): unlike fmaxf it needs no operand
@@ -1317,6 +1319,9 @@ constexpr int kXcds = 8;  // MI355X: eight accelerator complex dies
 #ifndef PKV_PREFILL_LDS_ROWS
 #define PKV_PREFILL_LDS_ROWS 2  // 16-row groups per wave
 #endif
+#ifndef PKV_PREFILL_TR
+#define PKV_PREFILL_TR 1  // head size 128: V operands by transposing LDS reads
+#endif
 #ifndef PKV_PREFILL_TILES
 #define PKV_PREFILL_TILES 4  // 16-row key tiles per softmax step (2 or 4)
 #endif
@@ -1332,16 +1337,24 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   static_assert(kT == 2 || kT == 4, "two or four tiles per step");
   constexpr int kNK = S::kNK;                         // K fragments per tile
   constexpr int kKBytes = kT * kNK * 1024;            // K of a step's tiles, fragment order
-  constexpr int kVBytes = kT * kTile * S::kRowBytes;  // V of a step's tiles, row order
+  // V: head size 128 keeps each tile as four 1 KiB blocks, block k holding rows
+  // k, 4+k, 8+k, 12+k, each block 32 bytes after the previous one ends, so the
+  // transposing reads of four rows 4*q4 + k at one column hit distinct banks;
+  // head size 64 keeps plain row order (read with 16-byte loads and shuffles)
+  constexpr bool kTrV = D == 128 && PKV_PREFILL_TR;
+  constexpr int kVBlock = 1024 + 32;
+  constexpr int kVTileBytes = kTrV ? 4 * kVBlock : kTile * S::kRowBytes;
+  constexpr int kVBytes = kT * kVTileBytes;  // V of a step's tiles
   constexpr int kBuf = kKBytes + kVBytes;
   constexpr int kBufs = kT == 2 ? 3 : 2;  // LDS buffers: loads run kBufs - 1 steps ahead
   constexpr int kThreads = 64 * kW;
   constexpr int kKLoads = kKBytes / 16 / kThreads;  // 16-byte loads per thread per step
-  constexpr int kVLoads = kVBytes / 16 / kThreads;
+  constexpr int kVLoads = kT * kTile * S::kRowBytes / 16 / kThreads;
   constexpr int kRowChunks = S::kRowBytes / 16;
   constexpr int kVTileChunks = kTile * kRowChunks;
-  static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kVBytes,
+  static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kT * kTile * S::kRowBytes,
                 "a step's tiles split evenly over the workgroup");
+  static_assert(!kTrV || kVLoads == kT, "one V block per wave per tile");
   static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
   // the LDS buffers as separate objects: the compiler then tracks which
   // buffer each cache -> LDS load writes and waits only for the right ones
@@ -1468,6 +1481,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     auto pick = [&](const __amdgpu_buffer_rsrc_t (&r)[kT], int t0, bool half) __attribute__((always_inline)) {
       return half && w >= kW / 2 ? r[t0 + 1] : r[t0];
     };
+    // Every resource reaches the LDS-load builtin as a named local: given a
+    // temporary or an array element, the host compilation pass drops the
+    // kernel's launch stub (the library then fails to load).
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       // fragment f = w + kW i of the step: tile f / kNK, chunk group cg = f % kNK;
@@ -1479,12 +1495,21 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
-      const int cw = 64 * w + kThreads * i;  // the wave's first V chunk of the step
-      const int u = cw / kVTileChunks;
-      const int ch = cw - u * kVTileChunks + lane;
-      const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
-      const __amdgpu_buffer_rsrc_t r = pick(rv, kThreads * i / kVTileChunks, kVHalf);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + kKBytes + cw * 16), 16, row * rs + col * 16, 0, 0, 0);
+      if constexpr (kTrV) {
+        // tile i, block w: lane l takes row 4 (l / 16) + w, 16-byte chunk l % 16
+        const int row = 4 * (lane >> 4) + w, col = lane & 15;
+        const __amdgpu_buffer_rsrc_t r = rv[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + kKBytes + i * kVTileBytes + w * kVBlock), 16,
+                                                 row * rs + col * 16, 0, 0, 0);
+      } else {
+        const int cw = 64 * w + kThreads * i;  // the wave's first V chunk of the step
+        const int u = cw / kVTileChunks;
+        const int ch = cw - u * kVTileChunks + lane;
+        const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
+        const __amdgpu_buffer_rsrc_t r = pick(rv, kThreads * i / kVTileChunks, kVHalf);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + kKBytes + cw * 16), 16, row * rs + col * 16, 0, 0,
+                                                 0);
+      }
     }
   };
   // every wave's loads into the next buffer have landed once each wave has
@@ -1595,6 +1620,29 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int pp = 0; pp < kT / 2; ++pp) {
+      if constexpr (kTrV) {
+        // Transposing reads (ds_read_b64_tr_b16): in each quarter-wave, lane
+        // s = 4k + a names 8 bytes of row 4*q4 + k at column 16 mt + 4a, and
+        // lane r receives the four rows' values at column 16 mt + r -- the A
+        // operand of output block mt (rows d = 16 mt + r) for this quarter's keys.
+        const int sk = ln >> 2, sa = ln & 3;
+        const char* base = vl + sk * kVBlock + q4 * S::kRowBytes + sa * 8;
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt) {
+          const auto x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(base + (2 * pp) * kVTileBytes + mt * 32));
+          const auto y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(base + (2 * pp + 1) * kVTileBytes + mt * 32));
+          const u32x2 xa = __builtin_bit_cast(u32x2, x), yb = __builtin_bit_cast(u32x2, y);
+          const u32x4 av = {xa[0], xa[1], yb[0], yb[1]};
+#pragma unroll
+          for (int rg = 0; rg < kR; ++rg) {
+            acc[rg][mt] = mfma_qk16<T>(av, pw_hi[rg][pp], acc[rg][mt]);
+            acc[rg][mt] = mfma_qk16<T>(av, pw_lo[rg][pp], acc[rg][mt]);
+          }
+        }
+        continue;
+      }
       // V rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's E elements,
       // packed into the A operand of each output block mt
       unsigned v_a[4][S::kVDW], v_b[4][S::kVDW];
@@ -1668,17 +1716,27 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     l_tot[rg] += xor_shuffle(l_tot[rg], 32);
     inv[rg] = l_tot[rg] > 0.f ? 1.0f / l_tot[rg] : 0.f;
   }
-  // this lane's 4 x E output values of row group rg (d = (4*q4 + i) * E + mt)
+  // this lane's 4 x E output values of row group rg: d = 16 mt + 4*q4 + i
+  // (transposed V reads), else d = (4*q4 + i) * E + mt
   auto write_out = [&](int rg, float scale_by) {
     if (!head_ok[rg]) return;
     char* orow = out + qidx[rg] * S::kRowBytes;
+    if constexpr (kTrV) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      unsigned wv[S::kVDW];
+      for (int mt = 0; mt < S::kE; ++mt) {
+        const u32x2 wv = {to_bits16<T>(acc[rg][mt][0] * scale_by) | (to_bits16<T>(acc[rg][mt][1] * scale_by) << 16),
+                          to_bits16<T>(acc[rg][mt][2] * scale_by) | (to_bits16<T>(acc[rg][mt][3] * scale_by) << 16)};
+        *reinterpret_cast<u32x2*>(orow + (16 * mt + 4 * q4) * 2) = wv;
+      }
+    } else {
 #pragma unroll
-      for (int mt = 0; mt < S::kE; mt += 2)
-        wv[mt >> 1] = to_bits16<T>(acc[rg][mt][i] * scale_by) | (to_bits16<T>(acc[rg][mt + 1][i] * scale_by) << 16);
-      store_dwords<S::kVDW>(orow + (4 * q4 + i) * S::kE * 2, wv);
+      for (int i = 0; i < 4; ++i) {
+        unsigned wv[S::kVDW];
+#pragma unroll
+        for (int mt = 0; mt < S::kE; mt += 2)
+          wv[mt >> 1] = to_bits16<T>(acc[rg][mt][i] * scale_by) | (to_bits16<T>(acc[rg][mt + 1][i] * scale_by) << 16);
+        store_dwords<S::kVDW>(orow + (4 * q4 + i) * S::kE * 2, wv);
+      }
     }
   };
   if (nparts == 1) {
