@@ -1084,95 +1084,97 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   // V rows and those weights, so neither operand moves between lanes.
   constexpr bool kPairs = k16 && (kPrefill ? PKV_PREFILL_PAIRS : PKV_DECODE_PAIRS);
   auto process_pair = [&](R& ra, int va, int ta, R& rb, int vb, int tb) {
-    patch_new(ra, va, ta);
-    patch_new(rb, vb, tb);
-    BlockRegs<T, D> ca, cb;
-    BlockRegs<T, D>* pa;
-    BlockRegs<T, D>* pb2;
-    // V operands over both tiles, shared by the row groups
-    u32x4 av[S::kE];
-    if constexpr (kFp8) {
-      codes_k_to_16<kQ, T, D>(ra, ca);
-      codes_k_to_16<kQ, T, D>(rb, cb);
-      codes_v_operand<kQ, T, D>(ra, rb, av);
-      pa = &ca;
-      pb2 = &cb;
-    } else {
-      pa = &ra;
-      pb2 = &rb;
+    if constexpr (kPairs) {  // (16-bit queries only: the fp32 build must not instantiate it)
+      patch_new(ra, va, ta);
+      patch_new(rb, vb, tb);
+      BlockRegs<T, D> ca, cb;
+      BlockRegs<T, D>* pa;
+      BlockRegs<T, D>* pb2;
+      // V operands over both tiles, shared by the row groups
+      u32x4 av[S::kE];
+      if constexpr (kFp8) {
+        codes_k_to_16<kQ, T, D>(ra, ca);
+        codes_k_to_16<kQ, T, D>(rb, cb);
+        codes_v_operand<kQ, T, D>(ra, rb, av);
+        pa = &ca;
+        pb2 = &cb;
+      } else {
+        pa = &ra;
+        pb2 = &rb;
 #pragma unroll
-      for (int mt = 0; mt < S::kE; ++mt) {
-        const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
-        av[mt] = u32x4{__builtin_amdgcn_perm(ra.v[1][mt >> 1], ra.v[0][mt >> 1], sel),
-                       __builtin_amdgcn_perm(ra.v[3][mt >> 1], ra.v[2][mt >> 1], sel),
-                       __builtin_amdgcn_perm(rb.v[1][mt >> 1], rb.v[0][mt >> 1], sel),
-                       __builtin_amdgcn_perm(rb.v[3][mt >> 1], rb.v[2][mt >> 1], sel)};
-      }
-    }
-    BlockRegs<T, D>& A = *pa;
-    BlockRegs<T, D>& Bt = *pb2;
-    const int key_a = (blk0 + ta) * kTile, key_b = (blk0 + tb) * kTile;
-#pragma unroll
-    for (int rg = 0; rg < kR; ++rg) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < S::kNK; ++c) {
-        sa = mfma_qk16<T>(A.k[c], qv[rg][c], sa);
-        sb = mfma_qk16<T>(Bt.k[c], qv[rg][c], sb);
-      }
-      float sc[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (kFp8) {
-          sc[i] = sa[i] * ra.ks[i] * a.qk_scale;
-          sc[4 + i] = sb[i] * rb.ks[i] * a.qk_scale;
-        } else {
-          sc[i] = sa[i] * a.qk_scale;
-          sc[4 + i] = sb[i] * a.qk_scale;
+        for (int mt = 0; mt < S::kE; ++mt) {
+          const unsigned sel = (mt & 1) ? 0x07060302u : 0x05040100u;
+          av[mt] = u32x4{__builtin_amdgcn_perm(ra.v[1][mt >> 1], ra.v[0][mt >> 1], sel),
+                         __builtin_amdgcn_perm(ra.v[3][mt >> 1], ra.v[2][mt >> 1], sel),
+                         __builtin_amdgcn_perm(rb.v[1][mt >> 1], rb.v[0][mt >> 1], sel),
+                         __builtin_amdgcn_perm(rb.v[3][mt >> 1], rb.v[2][mt >> 1], sel)};
         }
       }
-      // rows past a tile's valid count were not fetched; keys past a row's
-      // position are masked (both tests are wave-uniform to enter)
-      if (va < kTile || (kPrefill && key_a + kTile > min_limit)) {
+      BlockRegs<T, D>& A = *pa;
+      BlockRegs<T, D>& Bt = *pb2;
+      const int key_a = (blk0 + ta) * kTile, key_b = (blk0 + tb) * kTile;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[i] = (4 * q4 + i < va && (!kPrefill || key_a + 4 * q4 + i < my_limit[rg])) ? sc[i] : kNegInf;
-      }
-      if (vb < kTile || (kPrefill && key_b + kTile > min_limit)) {
+      for (int rg = 0; rg < kR; ++rg) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[4 + i] = (4 * q4 + i < vb && (!kPrefill || key_b + 4 * q4 + i < my_limit[rg])) ? sc[4 + i] : kNegInf;
-      }
-      const float mx = row_max4(fmax_nan(fmax_nan(fmax_nan(sc[0], sc[1]), fmax_nan(sc[2], sc[3])),
-                                         fmax_nan(fmax_nan(sc[4], sc[5]), fmax_nan(sc[6], sc[7]))));
-      const bool grow = mx > m_run[rg] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
-        const float m_new = grow ? mx : m_run[rg];
-        const float alpha = m_run[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+        for (int c = 0; c < S::kNK; ++c) {
+          sa = mfma_qk16<T>(A.k[c], qv[rg][c], sa);
+          sb = mfma_qk16<T>(Bt.k[c], qv[rg][c], sb);
+        }
+        float sc[8];
 #pragma unroll
-        for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= alpha;
-        l_run[rg] *= alpha;
-        m_run[rg] = m_new;
-      }
-      const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
-      float pv[8];
-      float lsum = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (kFp8) {
+            sc[i] = sa[i] * ra.ks[i] * a.qk_scale;
+            sc[4 + i] = sb[i] * rb.ks[i] * a.qk_scale;
+          } else {
+            sc[i] = sa[i] * a.qk_scale;
+            sc[4 + i] = sb[i] * a.qk_scale;
+          }
+        }
+        // rows past a tile's valid count were not fetched; keys past a row's
+        // position are masked (both tests are wave-uniform to enter)
+        if (va < kTile || (kPrefill && key_a + kTile > min_limit)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(sc[i] - m_use);
-        lsum += pr;
-        pv[i] = pr;
-        if constexpr (kFp8) pv[i] *= i < 4 ? ra.vs[i] : rb.vs[i - 4];
-      }
-      l_run[rg] += lsum;
-      unsigned hi[4], lo[4];
+          for (int i = 0; i < 4; ++i)
+            sc[i] = (4 * q4 + i < va && (!kPrefill || key_a + 4 * q4 + i < my_limit[rg])) ? sc[i] : kNegInf;
+        }
+        if (vb < kTile || (kPrefill && key_b + kTile > min_limit)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) split16_pair<T>(pv[2 * i], pv[2 * i + 1], hi[i], lo[i]);
-      const u32x4 pw_hi = {hi[0], hi[1], hi[2], hi[3]}, pw_lo = {lo[0], lo[1], lo[2], lo[3]};
+          for (int i = 0; i < 4; ++i)
+            sc[4 + i] = (4 * q4 + i < vb && (!kPrefill || key_b + 4 * q4 + i < my_limit[rg])) ? sc[4 + i] : kNegInf;
+        }
+        const float mx = row_max4(fmax_nan(fmax_nan(fmax_nan(sc[0], sc[1]), fmax_nan(sc[2], sc[3])),
+                                           fmax_nan(fmax_nan(sc[4], sc[5]), fmax_nan(sc[6], sc[7]))));
+        const bool grow = mx > m_run[rg] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+          const float m_new = grow ? mx : m_run[rg];
+          const float alpha = m_run[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
 #pragma unroll
-      for (int mt = 0; mt < S::kE; ++mt) {
-        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
-        acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo, acc[rg][mt]);
+          for (int mt = 0; mt < S::kE; ++mt) acc[rg][mt] *= alpha;
+          l_run[rg] *= alpha;
+          m_run[rg] = m_new;
+        }
+        const float m_use = m_run[rg] == kNegInf ? 0.f : m_run[rg];
+        float pv[8];
+        float lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(sc[i] - m_use);
+          lsum += pr;
+          pv[i] = pr;
+          if constexpr (kFp8) pv[i] *= i < 4 ? ra.vs[i] : rb.vs[i - 4];
+        }
+        l_run[rg] += lsum;
+        unsigned hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split16_pair<T>(pv[2 * i], pv[2 * i + 1], hi[i], lo[i]);
+        const u32x4 pw_hi = {hi[0], hi[1], hi[2], hi[3]}, pw_lo = {lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt) {
+          acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi, acc[rg][mt]);
+          acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo, acc[rg][mt]);
+        }
       }
     }
   };
@@ -2481,8 +2483,9 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
     return 0;
   // enough for every plan (the launch's dtype and cache format decide which)
   size_t need = 0;
-  for (const PrefillPlan& plan : {prefill_plan(PKV_BF16, 0, head_dim, 1.f), prefill_plan(PKV_BF16, kQFp8, head_dim, 1.f),
-                                  prefill_plan(PKV_F32, 0, head_dim, 1.f)}) {
+  const PrefillPlan plans[] = {prefill_plan(PKV_BF16, 0, head_dim, 1.f), prefill_plan(PKV_BF16, kQFp8, head_dim, 1.f),
+                               prefill_plan(PKV_F32, 0, head_dim, 1.f)};
+  for (const PrefillPlan& plan : plans) {
     const size_t bytes = prefill_split(plan, num_seqs, num_heads, num_kv_heads, head_dim, max_q_len,
                                        max_blocks_per_seq, block_size, partition_blocks).ws_bytes;
     need = bytes > need ? bytes : need;

@@ -97,7 +97,10 @@ uint64_t mix64(uint64_t z) {
 // accepted after comparing the tokens and the parent exactly.
 uint64_t chain_key(uint64_t prev, const int32_t* toks, int32_t n) {
   uint64_t h = mix64(prev ^ 0x6A09E667F3BCC909ull);
-  for (int32_t t = 0; t < n; ++t) h = mix64(h ^ (static_cast<uint64_t>(static_cast<uint32_t>(toks[t])) + 0x9E3779B97F4A7C15ull));
+  for (int32_t t = 0; t < n; ++t) {
+    const uint64_t tok = static_cast<uint32_t>(toks[t]);
+    h = mix64(h ^ (tok + 0x9E3779B97F4A7C15ull));
+  }
   return h;
 }
 uint64_t root_key(uint64_t ns) { return mix64(ns + 0x3C6EF372FE94F82Bull); }
