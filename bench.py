@@ -204,12 +204,20 @@ def run_prefill(args):
     Hq, Hkv, D, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     lens = np.full(B, P + C, np.int32)
     asg, slots, _ = pool_assignment(cfg, lens, pkv, wl)
-    wkd = wl.make_device_workload(cfg, dev, layers=1, context_lens=lens, assignment=asg)
-    kc, vc = wkd.k_cache[0], wkd.v_cache[0]
-    if args.layout == "NHD":
-        kc, vc = kc.transpose(1, 2).contiguous(), vc.transpose(1, 2).contiguous()
-    # the last position too: every chunk token's K/V is in the cache
-    pkv.kv_append(wkd.k_new[0], wkd.v_new[0], torch.from_numpy(slots).to(dev), kc, vc, layout=args.layout)
+    q8 = args.kv != "native"
+    fmt = "int8" if args.kv == "int8" else "e4m3"
+    nhd = (lambda x: x.transpose(1, 2).contiguous()) if args.layout == "NHD" else (lambda x: x)
+    slots_d = torch.from_numpy(slots).to(dev)
+    if q8:  # 8-bit codes + per-row scales (the values are random codes)
+        wkd = wl.make_device_workload_fp8(cfg, dev, layers=1, context_lens=lens, assignment=asg)
+        kc, vc = nhd(wkd.k_codes[0]), nhd(wkd.v_codes[0])
+        ks, vs = nhd(wkd.k_scales[0]), nhd(wkd.v_scales[0])
+        pkv.kv_append_fp8(wkd.k_new[0], wkd.v_new[0], slots_d, kc, vc, ks, vs, layout=args.layout, fmt=fmt)
+    else:
+        wkd = wl.make_device_workload(cfg, dev, layers=1, context_lens=lens, assignment=asg)
+        kc, vc = nhd(wkd.k_cache[0]), nhd(wkd.v_cache[0])
+        # the last position too: every chunk token's K/V is in the cache
+        pkv.kv_append(wkd.k_new[0], wkd.v_new[0], slots_d, kc, vc, layout=args.layout)
     g = torch.Generator(device=dev)
     g.manual_seed(cfg.seed)
     q = torch.randn((B * C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
@@ -219,8 +227,12 @@ def run_prefill(args):
     ws = pkv.alloc_prefill_workspace(q_start, Hq, kc, wkd.block_tables, C, pb, layout=args.layout)
 
     def launch():
-        pkv.prefill_attention(q, kc, vc, wkd.block_tables, q_start, C, wkd.context_lens_dev, cfg.scale, out, ws, pb,
-                              layout=args.layout)
+        if q8:
+            pkv.prefill_attention_fp8(q, kc, vc, ks, vs, wkd.block_tables, q_start, C, wkd.context_lens_dev, cfg.scale,
+                                      out, ws, pb, layout=args.layout, fmt=fmt)
+        else:
+            pkv.prefill_attention(q, kc, vc, wkd.block_tables, q_start, C, wkd.context_lens_dev, cfg.scale, out, ws,
+                                  pb, layout=args.layout)
 
     for _ in range(args.warmup):
         launch()
@@ -238,7 +250,7 @@ def run_prefill(args):
     flops = 4 * Hq * D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
     cpu = None
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and not q8:
         import oracle
         import time as _t
         # one sequence's chunk, the first rows only, on the host
@@ -266,11 +278,12 @@ def run_prefill(args):
         "metric": "chunked-prefill paged attention TFLOP/s (QK^T + PV over the causal triangle)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": f"{fmt} K/V + f32 row scales, bf16 q/out" if q8 else "bf16", "data": "synthetic",
         "config": {"workload": f"prefill: {B} sequences x {C}-token chunks after {P} cached tokens, 64 query / 8 KV "
                                f"heads, head_dim 128, {args.layout} blocks of {bs}", "seqs": B, "chunk": C,
-                   "context": P, "partition_blocks": pb},
-        "roofline": {"bound": "mfma", "kernel": "prefill_lds_kernel", "achieved": round(tflops, 2),
+                   "context": P, "partition_blocks": pb, "kv": args.kv},
+        "roofline": {"bound": "mfma", "kernel": "decode_partition_kernel<prefill>" if q8 else "prefill_lds_kernel",
+                     "achieved": round(tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2), "kernel_sha": kernel_sha()},
         "cpu_baseline": cpu,
