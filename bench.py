@@ -282,7 +282,7 @@ def run_prefill(args):
         "config": {"workload": f"prefill: {B} sequences x {C}-token chunks after {P} cached tokens, 64 query / 8 KV "
                                f"heads, head_dim 128, {args.layout} blocks of {bs}", "seqs": B, "chunk": C,
                    "context": P, "partition_blocks": pb, "kv": args.kv},
-        "roofline": {"bound": "mfma", "kernel": "decode_partition_kernel<prefill>" if q8 else "prefill_lds_kernel",
+        "roofline": {"bound": "mfma", "kernel": "prefill_lds_kernel",
                      "achieved": round(tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2), "kernel_sha": kernel_sha()},

@@ -347,8 +347,8 @@ pkv_status pkv_prefill_attention_int8(const void* q, const void* k_cache, const 
  * Every other argument as pkv_paged_decode_attention. Work unit: a group of
  * (query token, query head) rows of one KV head and one context partition --
  * 128 rows in a four-wave workgroup that shares each K/V tile through LDS for
- * 16-bit caches and scale > 0, 64 (16-bit) or 32 (fp32) rows in one wave
- * otherwise; split contexts are merged in the kernel by the partition that
+ * 16-bit caches (8-bit caches: head size 128) and scale > 0, 64 (16-bit
+ * queries) or 32 (fp32) rows in one wave otherwise; split contexts are merged in the kernel by the partition that
  * finishes last. The workspace size covers every variant.
  * Errors as pkv_paged_decode_attention.
  */

@@ -1332,30 +1332,40 @@ constexpr int kXcds = 8;  // MI355X: eight accelerator complex dies
 #endif
 constexpr int prefill_waves(int head_dim) { return head_dim == 64 ? 4 : PKV_PREFILL_WAVES; }
 
-template <typename T, int D, bool kNHD, int kW, int kR, int kT>
+// kQ = 0: the caches hold T; kQFp8 / kQInt8: 8-bit codes (head size 128)
+// with one fp32 scale per token row, staged in LDS as codes and converted to
+// T exactly by each wave; the K scale multiplies the scores, the V scale the
+// softmax weights.
+template <typename T, int D, bool kNHD, int kW, int kR, int kT, int kQ>
 __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
-  static_assert(sizeof(T) == 2, "the LDS prefill reads 16-bit caches");
+  static_assert(sizeof(T) == 2, "16-bit queries and MFMA operands");
   static_assert(kT == 2 || kT == 4, "two or four tiles per step");
-  constexpr int kNK = S::kNK;                         // K fragments per tile
+  constexpr bool kCodes = kQ != 0;
+  static_assert(!kCodes || D == 128, "8-bit caches: head size 128");
+  constexpr int kRowB = kCodes ? D : S::kRowBytes;    // bytes of a cache row
+  constexpr int kNK = kRowB / 64;                     // K fragments (16 bytes per lane) per tile
   constexpr int kKBytes = kT * kNK * 1024;            // K of a step's tiles, fragment order
   // V: head size 128 keeps each tile as four 1 KiB blocks, block k holding rows
   // k, 4+k, 8+k, 12+k, each block 32 bytes after the previous one ends, so the
   // transposing reads of four rows 4*q4 + k at one column hit distinct banks;
   // head size 64 keeps plain row order (read with 16-byte loads and shuffles)
-  constexpr bool kTrV = D == 128 && PKV_PREFILL_TR;
+  constexpr bool kTrV = !kCodes && D == 128 && PKV_PREFILL_TR;
   constexpr int kVBlock = 1024 + 32;
-  constexpr int kVTileBytes = kTrV ? 4 * kVBlock : kTile * S::kRowBytes;
+  constexpr int kVTileBytes = kTrV ? 4 * kVBlock : kTile * kRowB;
   constexpr int kVBytes = kT * kVTileBytes;  // V of a step's tiles
-  constexpr int kBuf = kKBytes + kVBytes;
+  constexpr int kSBytes = kCodes ? 2 * kT * kTile * 4 : 0;  // 8-bit: K, then V row scales of the tiles
+  constexpr int kBuf = kKBytes + kVBytes + kSBytes;
   constexpr int kBufs = kT == 2 ? 3 : 2;  // LDS buffers: loads run kBufs - 1 steps ahead
   constexpr int kThreads = 64 * kW;
   constexpr int kKLoads = kKBytes / 16 / kThreads;  // 16-byte loads per thread per step
-  constexpr int kVLoads = kT * kTile * S::kRowBytes / 16 / kThreads;
-  constexpr int kRowChunks = S::kRowBytes / 16;
+  constexpr int kVLoads = kT * kTile * kRowB / 16 / kThreads;
+  constexpr int kSLoads = kCodes ? 2 * kT / kW : 0;  // 8-bit: scale rows per wave per step
+  constexpr int kRowChunks = kRowB / 16;
   constexpr int kVTileChunks = kTile * kRowChunks;
-  static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kT * kTile * S::kRowBytes,
+  static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kT * kTile * kRowB,
                 "a step's tiles split evenly over the workgroup");
+  static_assert(!kCodes || kSLoads * kW == 2 * kT, "scale rows split evenly over the waves");
   static_assert(!kTrV || kVLoads == kT, "one V block per wave per tile");
   static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
   // the LDS buffers as separate objects: the compiler then tracks which
@@ -1370,6 +1380,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   // copied to scratch and reloaded per lane.
   const char* const k_cache = a.k_cache;
   const char* const v_cache = a.v_cache;
+  const char* const k_scales = a.k_scales;
+  const char* const v_scales = a.v_scales;
   const int32_t* const tables = a.block_tables;
   char* const out = a.out;
   const int num_blocks = a.num_blocks;
@@ -1421,7 +1433,10 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   int my_limit[kR];
   bool head_ok[kR];
   size_t qidx[kR];
-  u32x4 qv[kR][kNK];  // Q as the B operand, same chunk permutation as K
+  // Q as the B operand of chunk cc, in the d order of K: 16-bit caches keep
+  // 16-byte chunk 4 cc + q4 of each row in lane (q4, .); 8-bit caches give
+  // lane (q4, .) a row's codes q4 D/4 .. q4 D/4 + D/4 - 1, 8 per chunk
+  u32x4 qv[kR][S::kNK];
 #pragma unroll
   for (int rg = 0; rg < kR; ++rg) {
     const int r = r0 + rg * kTile + ln;
@@ -1432,8 +1447,10 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     qidx[rg] = (static_cast<size_t>(q_tok0) + tok) * a.num_heads + j * a.group + hin;
     const char* qrow = a.q + qidx[rg] * S::kRowBytes;
 #pragma unroll
-    for (int cc = 0; cc < kNK; ++cc)
-      qv[rg][cc] = head_ok[rg] ? *reinterpret_cast<const u32x4*>(qrow + (4 * cc + q4) * 16) : u32x4{0, 0, 0, 0};
+    for (int cc = 0; cc < S::kNK; ++cc) {
+      const int off = kCodes ? q4 * (D / 2) + 16 * cc : (4 * cc + q4) * 16;
+      qv[rg][cc] = head_ok[rg] ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0, 0, 0, 0};
+    }
   }
   const float c = a.qk_scale;  // > 0: the host routes other scales to the one-wave kernel
 
@@ -1452,7 +1469,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   int my_r0 = -1, my_r02 = -1;
   if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
   if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
-  const int rs = S::kRowBytes * (kNHD ? a.num_kv_heads : 1);  // bytes between a head's consecutive token rows
+  const int rs = kRowB * (kNHD ? a.num_kv_heads : 1);  // bytes between a head's consecutive token rows
+  const int ss = kNHD ? 4 * a.num_kv_heads : 4;        // 8-bit: bytes between their scales
   // first cache row of the partition's tile t and its rows to fetch: 0 past
   // the partition end or for an id outside the pool (nothing is read then)
   auto tile_src = [&](int t, int& valid) -> size_t {
@@ -1472,8 +1490,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
       const size_t r0 = tile_src(kT * s + u, valid[u]);
-      rk[u] = tile_rsrc(k_cache + r0 * S::kRowBytes, valid[u] * rs);
-      rv[u] = tile_rsrc(v_cache + r0 * S::kRowBytes, valid[u] * rs);
+      rk[u] = tile_rsrc(k_cache + r0 * kRowB, valid[u] * rs);
+      rv[u] = tile_rsrc(v_cache + r0 * kRowB, valid[u] * rs);
     }
     // the tile of a wave's i-th load: t0, or t0 + 1 for the upper half of the
     // waves where one tile's K (or V) is half of what the workgroup loads at once
@@ -1489,11 +1507,13 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       // fragment f = w + kW i of the step: tile f / kNK, chunk group cg = f % kNK;
-      // lane (q4, ln) takes token ln's 16-byte chunk 4 cg + q4
+      // lane (q4, ln) takes token ln's 16-byte chunk 4 cg + q4 (8-bit: the
+      // chunk at byte q4 D/4 + 16 cg)
       const int f = w + kW * i;
       const int cg = f % kNK;
+      const int col = kCodes ? q4 * (D / 4) + 16 * cg : (4 * cg + q4) * 16;
       const __amdgpu_buffer_rsrc_t r = pick(rk, kW * i / kNK, kKHalf);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + f * 1024), 16, ln * rs + (4 * cg + q4) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + f * 1024), 16, ln * rs + col, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
@@ -1513,11 +1533,27 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
                                                  0);
       }
     }
+    if constexpr (kCodes) {
+      // scale row j = w + kW i of the step: K (j even) or V scales of tile
+      // j / 2, 4 bytes per lane from the first 16 lanes (the rows past the
+      // tile's valid count read as zero)
+#pragma unroll
+      for (int i = 0; i < kSLoads; ++i) {
+        const int jj = w + kW * i, tile = jj >> 1;
+        int vv;
+        const size_t r0 = tile_src(kT * s + tile, vv);
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(((jj & 1) ? v_scales : k_scales) + r0 * 4, vv * ss);
+        if (lane < kTile)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r, lds_ptr(dst + kKBytes + kVBytes + (jj & 1) * (kT * kTile * 4) + tile * (kTile * 4)), 4, lane * ss,
+              0, 0, 0);
+      }
+    }
   };
   // every wave's loads into the next buffer have landed once each wave has
   // drained its own (all but those of the steps further ahead) and the
   // barrier is passed
-  constexpr int kLoads = kKLoads + kVLoads;
+  constexpr int kLoads = kKLoads + kVLoads + kSLoads;
   constexpr int kNewer = (kBufs - 2) * kLoads;  // loads that may stay in flight
   static_assert(kNewer < 16, "vmcnt field");
   auto sync_step = [&]() __attribute__((always_inline)) {
@@ -1546,13 +1582,45 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
       for (int u = 0; u < kT; ++u) sc[rg][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < kNK; ++cc) {
-      u32x4 kf[kT];
+      if constexpr (kCodes) {
+        // 16 codes per lane: chunks 2 cc (bytes 0..7) and 2 cc + 1 of the MFMA
+        u32x4 k0[kT], k1[kT];
 #pragma unroll
-      for (int u = 0; u < kT; ++u) kf[u] = *reinterpret_cast<const u32x4*>(kl + (u * kNK + cc) * 1024 + lane * 16);
+        for (int u = 0; u < kT; ++u) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(kl + (u * kNK + cc) * 1024 + lane * 16);
+          const u32x2 x0 = codes4_to_16<kQ, T>(raw[0]), x1 = codes4_to_16<kQ, T>(raw[1]);
+          const u32x2 x2 = codes4_to_16<kQ, T>(raw[2]), x3 = codes4_to_16<kQ, T>(raw[3]);
+          k0[u] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+          k1[u] = u32x4{x2[0], x2[1], x3[0], x3[1]};
+        }
 #pragma unroll
-      for (int rg = 0; rg < kR; ++rg)
+        for (int rg = 0; rg < kR; ++rg)
 #pragma unroll
-        for (int u = 0; u < kT; ++u) sc[rg][u] = mfma_qk16<T>(kf[u], qv[rg][cc], sc[rg][u]);
+          for (int u = 0; u < kT; ++u) sc[rg][u] = mfma_qk16<T>(k0[u], qv[rg][2 * cc], sc[rg][u]);
+#pragma unroll
+        for (int rg = 0; rg < kR; ++rg)
+#pragma unroll
+          for (int u = 0; u < kT; ++u) sc[rg][u] = mfma_qk16<T>(k1[u], qv[rg][2 * cc + 1], sc[rg][u]);
+      } else {
+        u32x4 kf[kT];
+#pragma unroll
+        for (int u = 0; u < kT; ++u) kf[u] = *reinterpret_cast<const u32x4*>(kl + (u * kNK + cc) * 1024 + lane * 16);
+#pragma unroll
+        for (int rg = 0; rg < kR; ++rg)
+#pragma unroll
+          for (int u = 0; u < kT; ++u) sc[rg][u] = mfma_qk16<T>(kf[u], qv[rg][cc], sc[rg][u]);
+      }
+    }
+    if constexpr (kCodes) {  // the K scales of this lane's keys 4*q4 + i
+      const char* sl = kl + kKBytes + kVBytes;
+#pragma unroll
+      for (int u = 0; u < kT; ++u) {
+        const f32x4 ksv = *reinterpret_cast<const f32x4*>(sl + u * (kTile * 4) + q4 * 16);
+#pragma unroll
+        for (int rg = 0; rg < kR; ++rg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[rg][u][i] *= ksv[i];
+      }
     }
   };
   // online-softmax step and PV products of step s (its V rows at vl); the
@@ -1612,6 +1680,16 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
           pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rg][2 * pp + i / 4][i % 4], c, -m_use));
           lsum += pr[i];
         }
+        if constexpr (kCodes) {  // the V scale rides on the weight
+          const char* vsl = vl + kVBytes + kT * kTile * 4;
+          const f32x4 va = *reinterpret_cast<const f32x4*>(vsl + (2 * pp) * (kTile * 4) + q4 * 16);
+          const f32x4 vb = *reinterpret_cast<const f32x4*>(vsl + (2 * pp + 1) * (kTile * 4) + q4 * 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pr[i] *= va[i];
+            pr[4 + i] *= vb[i];
+          }
+        }
         unsigned hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) split16_pair<T>(pr[2 * i], pr[2 * i + 1], hi[i], lo[i]);
@@ -1643,6 +1721,31 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
             acc[rg][mt] = mfma_qk16<T>(av, pw_lo[rg][pp], acc[rg][mt]);
           }
         }
+        continue;
+      }
+      if constexpr (kCodes) {
+        // codes of rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's D/16
+        // elements, converted straight into the A operand of each block mt
+        Fp8Regs<D> ta, tb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const char* ra = vl + (2 * pp * kTile + 4 * q4 + i) * kRowB + ln * (D / 16);
+          const u32x2 x = *reinterpret_cast<const u32x2*>(ra);
+          const u32x2 y = *reinterpret_cast<const u32x2*>(ra + kTile * kRowB);
+          ta.v[i][0] = x[0];
+          ta.v[i][1] = x[1];
+          tb.v[i][0] = y[0];
+          tb.v[i][1] = y[1];
+        }
+        u32x4 av[S::kE];
+        codes_v_operand<kQ, T, D>(ta, tb, av);
+#pragma unroll
+        for (int mt = 0; mt < S::kE; ++mt)
+#pragma unroll
+          for (int rg = 0; rg < kR; ++rg) {
+            acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi[rg][pp], acc[rg][mt]);
+            acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo[rg][pp], acc[rg][mt]);
+          }
         continue;
       }
       // V rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's E elements,
@@ -1997,12 +2100,12 @@ pkv_status launch_prefill(const DecodeArgs& a, int32_t num_seqs, hipStream_t str
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-template <typename T, int D>
+template <typename T, int D, int kQ = 0>
 pkv_status launch_prefill_lds(const DecodeArgs& a, int32_t num_seqs, hipStream_t stream, bool nhd) {
   dim3 grid(a.num_parts, a.num_kv_heads * a.q_tiles, num_seqs);
   constexpr int kW = prefill_waves(D), kR = PKV_PREFILL_LDS_ROWS, kT = PKV_PREFILL_TILES;
-  if (nhd) hipLaunchKernelGGL((prefill_lds_kernel<T, D, true, kW, kR, kT>), grid, dim3(64 * kW), 0, stream, a);
-  else hipLaunchKernelGGL((prefill_lds_kernel<T, D, false, kW, kR, kT>), grid, dim3(64 * kW), 0, stream, a);
+  if (nhd) hipLaunchKernelGGL((prefill_lds_kernel<T, D, true, kW, kR, kT, kQ>), grid, dim3(64 * kW), 0, stream, a);
+  else hipLaunchKernelGGL((prefill_lds_kernel<T, D, false, kW, kR, kT, kQ>), grid, dim3(64 * kW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
@@ -2055,11 +2158,11 @@ StepLayout step_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   const int64_t groups = ceil_div64(num_heads / num_kv_heads, 16);
   return merge_layout(static_cast<int64_t>(num_seqs) * num_kv_heads * groups, head_dim, parts);
 }
-// How a prefill launch splits its rows. The LDS kernel serves 16-bit caches
-// and positive finite scales: a work unit is a workgroup of
-// prefill_waves(head_dim) waves with PKV_PREFILL_LDS_ROWS row groups each.
-// 8-bit and fp32 caches (and other scales) take the one-wave tile kernel
-// with prefill_row_groups(dtype) row groups per unit.
+// How a prefill launch splits its rows. The LDS kernel serves 16-bit caches,
+// 8-bit caches of head size 128, and positive finite scales: a work unit is a
+// workgroup of prefill_waves(head_dim) waves with PKV_PREFILL_LDS_ROWS row
+// groups each. fp32 caches, 8-bit caches of head size 64 (and other scales)
+// take the one-wave tile kernel with prefill_row_groups(dtype) row groups per unit.
 struct PrefillPlan {
   bool lds;
   int32_t rows_per_unit;   // (token, head) rows of one KV head per work unit
@@ -2068,7 +2171,7 @@ struct PrefillPlan {
 };
 PrefillPlan prefill_plan(pkv_dtype dtype, int codes, int32_t head_dim, float scale) {
   const float c = scale * kLog2e;  // the LDS kernel applies c > 0 inside the exponent
-  if (PKV_PREFILL_LDS && codes == 0 && dtype != PKV_F32 && c > 0.f && c <= 3.0e38f) {
+  if (PKV_PREFILL_LDS && (codes == 0 || head_dim == 128) && dtype != PKV_F32 && c > 0.f && c <= 3.0e38f) {
     const int32_t groups = prefill_waves(head_dim) * PKV_PREFILL_LDS_ROWS;
     return {true, groups * kTile, groups, kMaxPartitionBlocks};
   }
@@ -2258,6 +2361,14 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool nhd = layout == PKV_NHD;
+  if (fp8 && plan.lds) {  // head size 128
+    const bool i8 = codes == kQInt8;
+    if (dtype == PKV_BF16)
+      return i8 ? launch_prefill_lds<__bf16, 128, kQInt8>(a, num_seqs, s, nhd)
+                : launch_prefill_lds<__bf16, 128, kQFp8>(a, num_seqs, s, nhd);
+    return i8 ? launch_prefill_lds<_Float16, 128, kQInt8>(a, num_seqs, s, nhd)
+              : launch_prefill_lds<_Float16, 128, kQFp8>(a, num_seqs, s, nhd);
+  }
   if (fp8) return dispatch_codes<PrefillLauncher>(dtype, head_dim, codes, a, num_seqs, s, nhd);
   if (plan.lds) {
     if (dtype == PKV_BF16)
@@ -2481,10 +2592,10 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_q_len <= 0 ||
       max_blocks_per_seq <= 0 || num_heads % num_kv_heads != 0 || !valid_block_size(block_size))
     return 0;
-  // enough for every plan (the launch's dtype and cache format decide which)
+  // enough for every plan (the launch's dtype, cache format and scale decide which)
   size_t need = 0;
   const PrefillPlan plans[] = {prefill_plan(PKV_BF16, 0, head_dim, 1.f), prefill_plan(PKV_BF16, kQFp8, head_dim, 1.f),
-                               prefill_plan(PKV_F32, 0, head_dim, 1.f)};
+                               prefill_plan(PKV_BF16, 0, head_dim, -1.f), prefill_plan(PKV_F32, 0, head_dim, 1.f)};
   for (const PrefillPlan& plan : plans) {
     const size_t bytes = prefill_split(plan, num_seqs, num_heads, num_kv_heads, head_dim, max_q_len,
                                        max_blocks_per_seq, block_size, partition_blocks).ws_bytes;
