@@ -2,6 +2,7 @@
 chunks of several sequences at different offsets into their cached context,
 GQA / MHA / MQA head shapes, 16-bit, fp32 and FP8 caches, both block layouts,
 block sizes 16 and 64, several partition sizes."""
+import dataclasses
 import sys
 
 import numpy as np
@@ -79,32 +80,37 @@ def test_prefill_parity(torch_dev, layout, bs, dtype, shape):
 
 @pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
-def test_prefill_fp8_parity(torch_dev, layout, fmt):
+@pytest.mark.parametrize("dtype,shape,bs", [("bf16", (32, 8, 128), 16), ("f16", (16, 2, 128), 64),
+                                            ("bf16", (8, 8, 64), 16)], ids=lambda x: str(x))
+def test_prefill_fp8_parity(torch_dev, layout, fmt, dtype, shape, bs):
+    """8-bit caches: head size 128 takes the LDS kernel (bf16 and fp16
+    queries), head size 64 the one-wave kernel."""
     torch, dev = torch_dev
-    Hq, Hkv, D, bs, dtype = 32, 8, 128, 16, "bf16"
+    Hq, Hkv, D = shape
     lens, q_start, max_q = chunk_layout()
     cfg = wl.DecodeConfig("prefill8", 0, 1, len(lens), Hq, Hkv, D, bs, dtype, context_lens=tuple(lens))
-    wk = wl.make_host_workload_fp8(cfg, seed=7100)
+    wk = wl.make_host_workload_fp8(cfg, seed=7100 + Hq + D + bs)
     kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
     oracle.kv_append_fp8(kc, vc, ks, vs, wk.k_new, wk.v_new, oracle.slot_mapping(wk.block_tables, lens - 1, bs), bs,
                          dtype, fmt=fmt)
     to = lambda x: wl.to_layout(x, layout)
     to_s = lambda x: to(x[..., None])[..., 0].copy()
     kc, vc, ks, vs = to(kc), to(vc), to_s(ks), to_s(vs)
-    q = wl.draw_values(np.random.default_rng(2), (int(q_start[-1]), Hq, D), dtype)
+    q = wl.draw_values(np.random.default_rng(2 + D), (int(q_start[-1]), Hq, D), dtype)
     ref = oracle.prefill_attention_fp8(q, kc, vc, ks, vs, wk.block_tables, q_start, lens, cfg.scale, Hkv, bs, dtype,
                                        layout, fmt=fmt)
     dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     qd = wl.raw_to_torch(q, dtype, dev)
     t, ld, qs = dv(wk.block_tables.astype(np.int32)), dv(lens), dv(q_start)
     for pb in (0, 2):
-        note(f"prefill {fmt} {layout} pb={pb}")
+        note(f"prefill {fmt} {layout} {dtype} {shape} bs={bs} pb={pb}")
         ws = pkv.alloc_prefill_workspace(qs, Hq, dv(kc), t, max_q, pb, layout=layout)
         out = torch.full_like(qd, float("nan"))
         pkv.prefill_attention_fp8(qd, dv(kc), dv(vc), dv(ks), dv(vs), t, qs, max_q, ld, cfg.scale, out, ws, pb,
                                   layout=layout, fmt=fmt)
         torch.cuda.synchronize()
-        check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype, f"prefill {fmt} {layout} pb={pb}")
+        check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype,
+                    f"prefill {fmt} {layout} {dtype} bs={bs} pb={pb}")
 
 
 def test_prefill_full_prompt_equals_decode_steps(torch_dev):
@@ -156,3 +162,60 @@ def test_prefill_any_scale(torch_dev, scale):
     pkv.prefill_attention(qd, kcd, vcd, t, qs, max_q, torch.from_numpy(lens).to(dev), scale, out, ws, 0)
     torch.cuda.synchronize()
     check_close(oracle.upcast(wl.torch_to_raw(out, dtype), dtype), ref, dtype, f"prefill scale {scale}")
+
+
+@pytest.mark.parametrize("kv", ["native", "e4m3", "int8"])
+def test_prefill_full_size_sampled(torch_dev, kv):
+    """The timed prefill workload: 4 sequences x 512-token chunks after 4096
+    cached tokens, Llama-3-70B attention heads (64 query / 8 KV, head size
+    128), bf16 queries, 16-token HND blocks, automatic partitions; sampled
+    (sequence, token) rows, every query head, against the reference of
+    attention at that token's position."""
+    torch, dev = torch_dev
+    B, C, P = 4, 512, 4096
+    cfg = dataclasses.replace(wl.CONFIG_BY_NAME["llama3_70b"], name="prefill_70b", num_seqs=B,
+                              context_lens=(P + C,) * B)
+    Hq, Hkv, D, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    lens = np.full(B, P + C, np.int32)
+    note(f"prefill full size {kv}")
+    q8 = kv != "native"
+    if q8:
+        wkd = wl.make_device_workload_fp8(cfg, dev, layers=1, context_lens=lens)
+        kc, vc, ks, vs = wkd.k_codes[0], wkd.v_codes[0], wkd.k_scales[0], wkd.v_scales[0]
+    else:
+        wkd = wl.make_device_workload(cfg, dev, layers=1, context_lens=lens)
+        kc, vc = wkd.k_cache[0], wkd.v_cache[0]
+    slots = torch.from_numpy(pkv.slot_mapping_from_tables(wkd.assignment.table(), lens - 1, bs)).to(dev)
+    if q8:
+        pkv.kv_append_fp8(wkd.k_new[0], wkd.v_new[0], slots, kc, vc, ks, vs, fmt=kv)
+    else:
+        pkv.kv_append(wkd.k_new[0], wkd.v_new[0], slots, kc, vc)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    q = torch.randn((B * C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    q_start = torch.arange(0, B * C + 1, C, dtype=torch.int32, device=dev)
+    out = torch.full_like(q, float("nan"))
+    ws = pkv.alloc_prefill_workspace(q_start, Hq, kc, wkd.block_tables, C, 0)
+    if q8:
+        pkv.prefill_attention_fp8(q, kc, vc, ks, vs, wkd.block_tables, q_start, C, wkd.context_lens_dev, cfg.scale,
+                                  out, ws, 0, fmt=kv)
+    else:
+        pkv.prefill_attention(q, kc, vc, wkd.block_tables, q_start, C, wkd.context_lens_dev, cfg.scale, out, ws, 0)
+    torch.cuda.synchronize()
+    o = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
+    assert np.isfinite(o).all()
+    toks = (0, 1, 255, 256, 511)
+    for b in (0, B - 1):
+        # the sequence's blocks (the appended row included) as a private table
+        idx = torch.from_numpy(wkd.assignment.blocks[b].astype(np.int64)).to(dev)
+        table = np.tile(np.arange(len(idx), dtype=np.int32), (len(toks), 1))
+        n = [P + i + 1 for i in toks]
+        qs = wl.torch_to_raw(q[[b * C + i for i in toks]], "bf16")
+        if q8:
+            hc = [x.index_select(0, idx).cpu().numpy() for x in (kc, vc, ks, vs)]
+            ref = oracle.decode_attention_fp8(qs, *hc, table, n, cfg.scale, Hkv, bs, "bf16", fmt=kv)
+        else:
+            hk, hv = wl.torch_to_raw(kc.index_select(0, idx), "bf16"), wl.torch_to_raw(vc.index_select(0, idx), "bf16")
+            ref = oracle.decode_attention(qs, hk, hv, table, n, cfg.scale, Hkv, bs, "bf16")
+        for r, i in enumerate(toks):
+            check_close(o[b * C + i], ref[r], "bf16", f"prefill {kv} seq {b} token {i}")
