@@ -1333,27 +1333,37 @@ constexpr int kXcds = 8;  // MI355X: eight accelerator complex dies
 constexpr int prefill_waves(int head_dim) { return head_dim == 64 ? 4 : PKV_PREFILL_WAVES; }
 
 // kQ = 0: the caches hold T; kQFp8 / kQInt8: 8-bit codes (head size 128)
-// with one fp32 scale per token row, staged in LDS as codes and converted to
-// T exactly by each wave; the K scale multiplies the scores, the V scale the
-// softmax weights.
+// with one fp32 scale per token row, staged in LDS as codes and converted
+// exactly to T; the K scale multiplies the scores, the V scale the softmax
+// weights. E4M3 codes (one packed convert per two) are converted by each wave
+// as it reads them; INT8 codes (three instructions per two) once per step by
+// the workgroup, a share per thread, into a second LDS area laid out as the
+// 16-bit caches are.
 template <typename T, int D, bool kNHD, int kW, int kR, int kT, int kQ>
 __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   using S = Shape<T, D>;
   static_assert(sizeof(T) == 2, "16-bit queries and MFMA operands");
   static_assert(kT == 2 || kT == 4, "two or four tiles per step");
   constexpr bool kCodes = kQ != 0;
+  constexpr bool kConvShared = kQ == kQInt8;          // converted once per step into ldsx
+  constexpr bool kConvWave = kCodes && !kConvShared;  // converted by each wave from the codes
   static_assert(!kCodes || D == 128, "8-bit caches: head size 128");
   constexpr int kRowB = kCodes ? D : S::kRowBytes;    // bytes of a cache row
-  constexpr int kNK = kRowB / 64;                     // K fragments (16 bytes per lane) per tile
+  constexpr int kNK = kRowB / 64;                     // K fragments (16 bytes per lane) per tile, as loaded
   constexpr int kKBytes = kT * kNK * 1024;            // K of a step's tiles, fragment order
-  // V: head size 128 keeps each tile as four 1 KiB blocks, block k holding rows
-  // k, 4+k, 8+k, 12+k, each block 32 bytes after the previous one ends, so the
-  // transposing reads of four rows 4*q4 + k at one column hit distinct banks;
-  // head size 64 keeps plain row order (read with 16-byte loads and shuffles)
-  constexpr bool kTrV = !kCodes && D == 128 && PKV_PREFILL_TR;
+  // 16-bit V as the MFMAs read it: head size 128 keeps each tile as four 1 KiB
+  // blocks, block k holding rows k, 4+k, 8+k, 12+k, each block 32 bytes after
+  // the previous one ends, so the transposing reads of four rows 4*q4 + k at
+  // one column hit distinct banks; head size 64 keeps plain row order (read
+  // with 16-byte loads and shuffles). 8-bit codes are loaded in row order.
+  constexpr bool kTrV = D == 128 && PKV_PREFILL_TR && !kConvWave;
+  constexpr bool kTrLoad = kTrV && !kCodes;  // the loads place V in the block layout
   constexpr int kVBlock = 1024 + 32;
-  constexpr int kVTileBytes = kTrV ? 4 * kVBlock : kTile * kRowB;
-  constexpr int kVBytes = kT * kVTileBytes;  // V of a step's tiles
+  constexpr int kVTileX = kTrV ? 4 * kVBlock : kTile * S::kRowBytes;
+  constexpr int kVTileBytes = kCodes ? kTile * kRowB : kVTileX;
+  constexpr int kVBytes = kT * kVTileBytes;  // V of a step's tiles, as loaded
+  constexpr int kKBytesX = kT * S::kNK * 1024;  // INT8: the converted K (16-bit fragments), then V
+  constexpr int kXBytes = kConvShared ? kKBytesX + kT * kVTileX : 16;
   constexpr int kSBytes = kCodes ? 2 * kT * kTile * 4 : 0;  // 8-bit: K, then V row scales of the tiles
   constexpr int kBuf = kKBytes + kVBytes + kSBytes;
   constexpr int kBufs = kT == 2 ? 3 : 2;  // LDS buffers: loads run kBufs - 1 steps ahead
@@ -1366,13 +1376,14 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   static_assert(kKLoads * 16 * kThreads == kKBytes && kVLoads * 16 * kThreads == kT * kTile * kRowB,
                 "a step's tiles split evenly over the workgroup");
   static_assert(!kCodes || kSLoads * kW == 2 * kT, "scale rows split evenly over the waves");
-  static_assert(!kTrV || kVLoads == kT, "one V block per wave per tile");
+  static_assert(!kTrLoad || kVLoads == kT, "one V block per wave per tile");
   static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
   // the LDS buffers as separate objects: the compiler then tracks which
   // buffer each cache -> LDS load writes and waits only for the right ones
   __shared__ __attribute__((aligned(16))) char lds0[kBuf];
   __shared__ __attribute__((aligned(16))) char lds1[kBuf];
   __shared__ __attribute__((aligned(16))) char lds2[kBufs > 2 ? kBuf : 16];
+  __shared__ __attribute__((aligned(16))) char ldsx[kXBytes];
 
   // The lambdas below capture only locals: a lambda that referenced `a`
   // would take its address, and next to the cache -> LDS loads (which may
@@ -1517,7 +1528,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
-      if constexpr (kTrV) {
+      if constexpr (kTrLoad) {
         // tile i, block w: lane l takes row 4 (l / 16) + w, 16-byte chunk l % 16
         const int row = 4 * (lane >> 4) + w, col = lane & 15;
         const __amdgpu_buffer_rsrc_t r = rv[i];
@@ -1574,16 +1585,17 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     l_run[rg] = 0.f;
   }
 
-  // QK^T of step s (its K fragments at kl) for every row group and tile
-  auto scores = [&](const char* kl, f32x4 (&sc)[kR][kT]) __attribute__((always_inline)) {
+  // QK^T of step s (its 16-bit K fragments at kl) for every row group and
+  // tile; 8-bit: times the keys' K scales (at sl)
+  auto scores = [&](const char* kl, const char* sl, f32x4 (&sc)[kR][kT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg)
 #pragma unroll
       for (int u = 0; u < kT; ++u) sc[rg][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kConvWave) {
 #pragma unroll
-    for (int cc = 0; cc < kNK; ++cc) {
-      if constexpr (kCodes) {
-        // 16 codes per lane: chunks 2 cc (bytes 0..7) and 2 cc + 1 of the MFMA
+      for (int cc = 0; cc < kNK; ++cc) {
+        // 16 codes per lane: 16-bit chunks 2 cc (bytes 0..7) and 2 cc + 1
         u32x4 k0[kT], k1[kT];
 #pragma unroll
         for (int u = 0; u < kT; ++u) {
@@ -1601,10 +1613,14 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         for (int rg = 0; rg < kR; ++rg)
 #pragma unroll
           for (int u = 0; u < kT; ++u) sc[rg][u] = mfma_qk16<T>(k1[u], qv[rg][2 * cc + 1], sc[rg][u]);
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < S::kNK; ++cc) {
         u32x4 kf[kT];
 #pragma unroll
-        for (int u = 0; u < kT; ++u) kf[u] = *reinterpret_cast<const u32x4*>(kl + (u * kNK + cc) * 1024 + lane * 16);
+        for (int u = 0; u < kT; ++u)
+          kf[u] = *reinterpret_cast<const u32x4*>(kl + (u * S::kNK + cc) * 1024 + lane * 16);
 #pragma unroll
         for (int rg = 0; rg < kR; ++rg)
 #pragma unroll
@@ -1612,7 +1628,6 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
       }
     }
     if constexpr (kCodes) {  // the K scales of this lane's keys 4*q4 + i
-      const char* sl = kl + kKBytes + kVBytes;
 #pragma unroll
       for (int u = 0; u < kT; ++u) {
         const f32x4 ksv = *reinterpret_cast<const f32x4*>(sl + u * (kTile * 4) + q4 * 16);
@@ -1626,7 +1641,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   // online-softmax step and PV products of step s (its V rows at vl); the
   // scores are raw (the scale c = qk_scale > 0 is applied inside the
   // exponent: max(c s) = c max(s)) and masked keys score -inf
-  auto attend = [&](const char* vl, int s, f32x4 (&sc)[kR][kT], const int (&valid)[kT])
+  auto attend = [&](const char* vl, int s, f32x4 (&sc)[kR][kT], const int (&valid)[kT], const char* sl)
                     __attribute__((always_inline)) {
     const int key0 = (blk0 + kT * s) * kTile;
     float mx[kR];
@@ -1681,7 +1696,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
           lsum += pr[i];
         }
         if constexpr (kCodes) {  // the V scale rides on the weight
-          const char* vsl = vl + kVBytes + kT * kTile * 4;
+          const char* vsl = sl + kT * kTile * 4;
           const f32x4 va = *reinterpret_cast<const f32x4*>(vsl + (2 * pp) * (kTile * 4) + q4 * 16);
           const f32x4 vb = *reinterpret_cast<const f32x4*>(vsl + (2 * pp + 1) * (kTile * 4) + q4 * 16);
 #pragma unroll
@@ -1710,9 +1725,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
         for (int mt = 0; mt < S::kE; ++mt) {
           const auto x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(base + (2 * pp) * kVTileBytes + mt * 32));
+              (lds_s16x4*)(base + (2 * pp) * kVTileX + mt * 32));
           const auto y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(base + (2 * pp + 1) * kVTileBytes + mt * 32));
+              (lds_s16x4*)(base + (2 * pp + 1) * kVTileX + mt * 32));
           const u32x2 xa = __builtin_bit_cast(u32x2, x), yb = __builtin_bit_cast(u32x2, y);
           const u32x4 av = {xa[0], xa[1], yb[0], yb[1]};
 #pragma unroll
@@ -1723,7 +1738,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         }
         continue;
       }
-      if constexpr (kCodes) {
+      if constexpr (kConvWave) {
         // codes of rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's D/16
         // elements, converted straight into the A operand of each block mt
         Fp8Regs<D> ta, tb;
@@ -1789,6 +1804,50 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     }
   };
 
+  // INT8: the codes of a step (buffer cb) -> T in ldsx, 16 codes per thread
+  // and pass: K fragment f, lane l -> 16-bit fragments 2 (f % kNK) and
+  // 2 (f % kNK) + 1 of its tile, lane l (bytes 0..7, then 8..15); V row r,
+  // codes 16 c .. 16 c + 15 -> elements 16 c .. 16 c + 15 of row r in the
+  // block layout. Every byte the MFMAs read is rewritten each step.
+  auto convert = [&](const char* cb) __attribute__((always_inline)) {
+    constexpr int kKChunks = kT * kNK * 64, kVChunks = kT * kVTileChunks;
+    static_assert(kKChunks % kThreads == 0 && kVChunks % kThreads == 0, "conversion passes");
+#pragma unroll
+    for (int i = 0; i < kKChunks / kThreads; ++i) {
+      const int g = tid + kThreads * i;
+      const int f = g >> 6, l = g & 63;
+      const int u = f / kNK, cg = f - u * kNK;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(cb + g * 16);
+      const u32x2 x0 = codes4_to_16<kQ, T>(raw[0]), x1 = codes4_to_16<kQ, T>(raw[1]);
+      const u32x2 x2 = codes4_to_16<kQ, T>(raw[2]), x3 = codes4_to_16<kQ, T>(raw[3]);
+      char* dk = ldsx + ((u * S::kNK + 2 * cg) * 64 + l) * 16;
+      *reinterpret_cast<u32x4*>(dk) = u32x4{x0[0], x0[1], x1[0], x1[1]};
+      *reinterpret_cast<u32x4*>(dk + 1024) = u32x4{x2[0], x2[1], x3[0], x3[1]};
+    }
+#pragma unroll
+    for (int i = 0; i < kVChunks / kThreads; ++i) {
+      const int g = tid + kThreads * i;
+      const int u = g / kVTileChunks, ch = g - u * kVTileChunks;
+      const int row = ch / kRowChunks, col = ch - row * kRowChunks;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(cb + kKBytes + g * 16);
+      const u32x2 x0 = codes4_to_16<kQ, T>(raw[0]), x1 = codes4_to_16<kQ, T>(raw[1]);
+      const u32x2 x2 = codes4_to_16<kQ, T>(raw[2]), x3 = codes4_to_16<kQ, T>(raw[3]);
+      const int at = kTrV ? (row & 3) * kVBlock + (row >> 2) * S::kRowBytes : row * S::kRowBytes;
+      char* dv = ldsx + kKBytesX + u * kVTileX + at + col * 32;
+      *reinterpret_cast<u32x4*>(dv) = u32x4{x0[0], x0[1], x1[0], x1[1]};
+      *reinterpret_cast<u32x4*>(dv + 16) = u32x4{x2[0], x2[1], x3[0], x3[1]};
+    }
+  };
+  // every wave's conversion writes have landed once each wave has drained its
+  // own LDS operations and the barrier is passed (the cache loads in flight
+  // are not waited for)
+  auto sync_lds = [&]() __attribute__((always_inline)) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0 (vmcnt, expcnt: no wait)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
   // kBufs buffers, loads kBufs - 1 steps ahead: step s consumes buffer
   // s % kBufs while the next steps load; its barrier makes step s+1 visible
   // and frees buffer s % kBufs. Past the partition end the loads fetch nothing.
@@ -1799,10 +1858,16 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   sync_step();
   auto step = [&](int s, int cur, int ahead) __attribute__((always_inline)) {
     fetch(s + kBufs - 1, bufs[ahead], valid[ahead]);
+    if constexpr (kConvShared) {  // every wave takes part, with rows or not
+      convert(bufs[cur]);
+      sync_lds();
+    }
     if (wave_rows && (blk0 + kT * s) * kTile < n_w) {  // wave-uniform: some key of the step is visible
       f32x4 sc[kR][kT];
-      scores(bufs[cur], sc);
-      attend(bufs[cur] + kKBytes, s, sc, valid[cur]);
+      const char* xb = kConvShared ? ldsx : bufs[cur];
+      const char* sl = bufs[cur] + kKBytes + kVBytes;  // 8-bit: the row scales
+      scores(xb, sl, sc);
+      attend(xb + (kConvShared ? kKBytesX : kKBytes), s, sc, valid[cur], sl);
     }
     sync_step();
   };
