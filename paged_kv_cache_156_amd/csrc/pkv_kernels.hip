@@ -1352,10 +1352,11 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   constexpr int kNK = kRowB / 64;                     // K fragments (16 bytes per lane) per tile, as loaded
   constexpr int kKBytes = kT * kNK * 1024;            // K of a step's tiles, fragment order
   // 16-bit V as the MFMAs read it: head size 128 keeps each tile as four 1 KiB
-  // blocks, block k holding rows k, 4+k, 8+k, 12+k, each block 32 bytes after
-  // the previous one ends, so the transposing reads of four rows 4*q4 + k at
-  // one column hit distinct banks; head size 64 keeps plain row order (read
-  // with 16-byte loads and shuffles). 8-bit codes are loaded in row order.
+  // blocks, block k holding rows k, 4+k, 8+k, 12+k (rows 4+k and 12+k with
+  // their 128-byte halves swapped), each block 32 bytes after the previous one
+  // ends, so the transposing reads of four rows 4*q4 + k at one column hit
+  // distinct banks; head size 64 keeps plain row order (read with 16-byte
+  // loads and shuffles). 8-bit codes are loaded in row order.
   constexpr bool kTrV = D == 128 && PKV_PREFILL_TR && !kConvWave;
   constexpr bool kTrLoad = kTrV && !kCodes;  // the loads place V in the block layout
   constexpr int kVBlock = 1024 + 32;
@@ -1529,8 +1530,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
       if constexpr (kTrLoad) {
-        // tile i, block w: lane l takes row 4 (l / 16) + w, 16-byte chunk l % 16
-        const int row = 4 * (lane >> 4) + w, col = lane & 15;
+        // tile i, block w: lane l fills row 4 (l / 16) + w, 16-byte chunk l % 16
+        // of the block, taking the row's chunk (l % 16) ^ 8 for odd l / 16
+        const int row = 4 * (lane >> 4) + w, col = (lane & 15) ^ (((lane >> 4) & 1) << 3);
         const __amdgpu_buffer_rsrc_t r = rv[i];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + kKBytes + i * kVTileBytes + w * kVBlock), 16,
                                                  row * rs + col * 16, 0, 0, 0);
@@ -1720,14 +1722,19 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         // s = 4k + a names 8 bytes of row 4*q4 + k at column 16 mt + 4a, and
         // lane r receives the four rows' values at column 16 mt + r -- the A
         // operand of output block mt (rows d = 16 mt + r) for this quarter's keys.
+        // Odd q4 rows hold their two 128-byte halves swapped (column block mt
+        // at mt ^ 4), so the two quarter-waves of each half-wave read
+        // different 128-byte bank ranges.
         const int sk = ln >> 2, sa = ln & 3;
+        const int swz = (q4 & 1) * 128;
         const char* base = vl + sk * kVBlock + q4 * S::kRowBytes + sa * 8;
+        const char* base_lo = base + swz;  // column blocks 0..3
+        const char* base_hi = base - swz;  // column blocks 4..7
 #pragma unroll
         for (int mt = 0; mt < S::kE; ++mt) {
-          const auto x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(base + (2 * pp) * kVTileX + mt * 32));
-          const auto y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(base + (2 * pp + 1) * kVTileX + mt * 32));
+          const char* bm = (mt < 4 ? base_lo : base_hi) + mt * 32;
+          const auto x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bm + (2 * pp) * kVTileX));
+          const auto y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bm + (2 * pp + 1) * kVTileX));
           const u32x2 xa = __builtin_bit_cast(u32x2, x), yb = __builtin_bit_cast(u32x2, y);
           const u32x4 av = {xa[0], xa[1], yb[0], yb[1]};
 #pragma unroll
@@ -1832,8 +1839,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(cb + kKBytes + g * 16);
       const u32x2 x0 = codes4_to_16<kQ, T>(raw[0]), x1 = codes4_to_16<kQ, T>(raw[1]);
       const u32x2 x2 = codes4_to_16<kQ, T>(raw[2]), x3 = codes4_to_16<kQ, T>(raw[3]);
-      const int at = kTrV ? (row & 3) * kVBlock + (row >> 2) * S::kRowBytes : row * S::kRowBytes;
-      char* dv = ldsx + kKBytesX + u * kVTileX + at + col * 32;
+      const int at = kTrV ? (row & 3) * kVBlock + (row >> 2) * S::kRowBytes + ((col * 32) ^ (((row >> 2) & 1) * 128))
+                          : row * S::kRowBytes + col * 32;
+      char* dv = ldsx + kKBytesX + u * kVTileX + at;
       *reinterpret_cast<u32x4*>(dv) = u32x4{x0[0], x0[1], x1[0], x1[1]};
       *reinterpret_cast<u32x4*>(dv + 16) = u32x4{x2[0], x2[1], x3[0], x3[1]};
     }
