@@ -1295,19 +1295,21 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 }
 
 // ---------------------------------------------------------------------------
-// chunked prefill over 16-bit caches: K/V tiles shared through LDS
+// chunked prefill: K/V tiles shared through LDS (16-bit caches; 8-bit caches
+// of head size 128)
 // ---------------------------------------------------------------------------
 // Prefill multiplies many query rows against the same keys, so it is bound by
 // MFMA work and by the traffic that feeds the MFMAs, not by HBM bytes (page
 // "KV Cache and Inference Optimization": prefill is compute-bound, decode
 // memory-bound). A workgroup of kW waves, each holding kR groups of 16
 // (token, head) rows of one KV head's chunk, walks the partition's key tiles
-// two at a time. The workgroup copies a pair of tiles from the cache into LDS
-// -- K in MFMA fragment order (fragment f, lane l at byte 1024 f + 16 l), V in
-// row order -- double-buffered with one barrier per pair, and every wave runs
-// its QK and PV MFMAs from there: a tile is fetched once per workgroup instead
-// of once per wave. The register layouts, the online softmax and the 16-bit
-// head + residual weights are those of the decode kernel's tile pairs.
+// kT at a time (one softmax step per kT tiles). The workgroup copies a step's
+// tiles from the cache into LDS -- K in MFMA fragment order (fragment f, lane
+// l at byte 1024 f + 16 l), V in the layout its MFMA operand reads want --
+// with loads one step ahead and one barrier per step, and every wave runs its
+// QK and PV MFMAs from there: a tile is fetched once per workgroup instead of
+// once per wave. The register layouts, the online softmax and the 16-bit head
+// + residual weights are those of the decode kernel's tile pairs.
 //
 // Workgroups are numbered so that consecutive numbers land on one XCD
 // (workgroups are dealt to the XCDs round-robin by linear id) and the query
