@@ -719,8 +719,11 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   const int p = PKV_XCD_ROTATE ? static_cast<int>((blockIdx.x + blockIdx.y + gridDim.y * blockIdx.z) % gridDim.x)
                                : static_cast<int>(blockIdx.x);
   const int units_per_head = kPrefill ? a.q_tiles : a.head_groups;  // work units per (sequence, KV head)
-  const int jg = blockIdx.y / units_per_head;       // KV head, or group of blockDim / 64 heads
-  const int ui = blockIdx.y - jg * units_per_head;  // head group (decode) or query tile (prefill)
+  const int jg = blockIdx.y / units_per_head;  // KV head, or group of blockDim / 64 heads
+  // head group (decode) or query tile (prefill; in descending order: later
+  // tiles see more keys, and the longest workgroups start first)
+  const int ui = kPrefill ? units_per_head - 1 - static_cast<int>(blockIdx.y - jg * units_per_head)
+                          : static_cast<int>(blockIdx.y - jg * units_per_head);
   const int j = kMaxW == 1 ? jg
                            : jg * static_cast<int>(blockDim.x >> 6) +
                                  __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -1412,7 +1415,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const unsigned xcd = lin % kXcds, per = nwg / kXcds, extra = nwg % kXcds;
   unsigned id = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + lin / kXcds;
-  const int ui = static_cast<int>(id % static_cast<unsigned>(a.q_tiles));
+  // query tiles in descending order: the later tiles of a chunk see more keys
+  // (causal), and starting the longest workgroups first shortens the tail
+  const int ui = a.q_tiles - 1 - static_cast<int>(id % static_cast<unsigned>(a.q_tiles));
   id /= static_cast<unsigned>(a.q_tiles);
   const int p = static_cast<int>(id % gridDim.x);
   id /= gridDim.x;
