@@ -189,3 +189,46 @@ def test_int8_attention_reference_is_the_dequantized_attention():
             s_ = K @ qf[b, h] * 0.125
             w = np.exp(s_ - s_.max())
             assert np.max(np.abs(got[b, h] - (w / w.sum()) @ V)) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+def test_prefill_8bit_reference_is_causal_attention_over_dequantized_rows(fmt):
+    """Chunked prefill over 8-bit caches: token i of a chunk of q_len tokens
+    in a sequence of n attends to the dequantized rows 0 .. n - q_len + i
+    (E4M3 decoded by torch's float8 type, INT8 by a plain integer cast),
+    brute force; NHD copies of the caches give the same result."""
+    from oracle import prefill as pf
+    rng = np.random.default_rng(21)
+    NB, Hkv, bs, D, Hq = 7, 2, 16, 64, 6
+    kc = rng.integers(0, 256, (NB, Hkv, bs, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (NB, Hkv, bs, D), dtype=np.uint8)
+    if fmt == "e4m3":  # no NaN codes (S.1111.111) in valid rows
+        kc[(kc & 0x7F) == 0x7F] = 0x3C
+        vc[(vc & 0x7F) == 0x7F] = 0x3C
+        deq = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    else:
+        deq = lambda c: c.view(np.int8).astype(np.float64)
+    ks = rng.uniform(0.01, 0.2, (NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.01, 0.2, (NB, Hkv, bs)).astype(np.float32)
+    table = np.array([[3, 1, 0], [5, 2, 6]], np.int32)
+    lens, q_len = [37, 20], [5, 20]
+    q_start = np.array([0, 5, 25], np.int32)
+    qv = wl.draw_values(rng, (25, Hq, D), "bf16")
+    got = pf.prefill_attention_fp8(qv, kc, vc, ks, vs, table, q_start, lens, 0.125, Hkv, bs, "bf16", fmt=fmt)
+    kd, vd = deq(kc) * ks[..., None], deq(vc) * vs[..., None]
+    qf = da.upcast(qv, "bf16")
+    for b, n in enumerate(lens):
+        for i in range(q_len[b]):
+            m = n - q_len[b] + i + 1
+            rows = [(table[b][t // bs], t % bs) for t in range(m)]
+            for h in range(Hq):
+                j = h // (Hq // Hkv)
+                K = np.stack([kd[p, j, o] for p, o in rows])
+                V = np.stack([vd[p, j, o] for p, o in rows])
+                s_ = K @ qf[q_start[b] + i, h] * 0.125
+                w = np.exp(s_ - s_.max())
+                assert np.max(np.abs(got[q_start[b] + i, h] - (w / w.sum()) @ V)) < 1e-12
+    nhd = lambda x: np.ascontiguousarray(np.swapaxes(x, 1, 2))
+    got_n = pf.prefill_attention_fp8(qv, nhd(kc), nhd(vc), nhd(ks), nhd(vs), table, q_start, lens, 0.125, Hkv, bs,
+                                     "bf16", layout="NHD", fmt=fmt)
+    assert np.array_equal(got, got_n)
