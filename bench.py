@@ -155,6 +155,20 @@ def run_copy_blocks(args):
     ms = t0.elapsed_time(t1) / args.steps
     assert torch.equal(kc[pairs[:, 1].long()], kc[pairs[:, 0].long()])
     gbs = bytes_launch / (ms * 1e-3) / 1e9
+    # reference: one contiguous device copy of the same bytes (torch's copy
+    # kernel), the read + write rate the scattered block copies compare with
+    src = torch.empty(bytes_launch // 4, dtype=torch.uint16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ref_gbs = bytes_launch / (c0.elapsed_time(c1) / args.steps * 1e-3) / 1e9
+    del src, dst
     cpu = None
     if args.cpu_budget > 0:
         import oracle
@@ -179,6 +193,7 @@ def run_copy_blocks(args):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "alg_bytes_per_launch": bytes_launch, "avg_launch_us": round(ms * 1e3, 2),
                      "kernel_sha": kernel_sha()},
+        "contiguous_copy_gbps": round(ref_gbs, 2),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
