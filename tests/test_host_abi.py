@@ -219,3 +219,60 @@ def test_workspace_and_partition_choice():
     parts = -(-256 // pb)
     rows = 32 * 64 * parts
     assert pkv.decode_workspace_bytes(32, 64, 8, 128, 256, 0) >= rows * 129 * 4
+
+
+def test_step_8bit_prefill_and_copy_reject_bad_arguments_without_gpu():
+    """The fused step, the 8-bit calls, prefill and copy_blocks also check
+    their arguments before any HIP call (so these run on the CPU)."""
+    lib = pkv.load()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call fails validation or does nothing
+
+    def step(fn=lib.pkv_decode_step, codes=False, **kw):
+        a = dict(q=fake, kn=fake, vn=fake, k=fake, v=fake, ks=fake, vs=fake, t=fake, mb=4, lens=fake, B=2, Hq=4,
+                 Hkv=2, D=64, bs=16, lay=0, NB=8, scale=0.125, out=fake, dt=2, ws=None, wsb=0, pb=0)
+        a.update(kw)
+        head = [a["q"], a["kn"], a["vn"], a["k"], a["v"]] + ([a["ks"], a["vs"]] if codes else [])
+        return fn(*head, a["t"], a["mb"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"],
+                  a["scale"], a["out"], a["dt"], a["ws"], a["wsb"], a["pb"], None)
+
+    assert step(B=0) == pkv.PKV_OK
+    assert step(kn=None) == pkv.PKV_EINVAL
+    assert step(Hq=6, Hkv=4) == pkv.PKV_EINVAL
+    assert step(D=96) == pkv.PKV_EUNSUPPORTED
+    assert step(pb=1) == pkv.PKV_ESMALL  # 4 blocks in partitions of 1: a workspace is needed
+    for fn in (lib.pkv_decode_step_fp8, lib.pkv_decode_step_int8):
+        assert step(fn, True, ks=None) == pkv.PKV_EINVAL
+        assert step(fn, True, dt=0) == pkv.PKV_EUNSUPPORTED  # fp32 queries over 8-bit caches
+        assert step(fn, True, pb=1) == pkv.PKV_ESMALL
+    for fn in (lib.pkv_kv_append_fp8, lib.pkv_kv_append_int8):
+        assert fn(fake, fake, fake, 0, fake, fake, fake, fake, 4, 2, 64, 16, 0, 2, None) == pkv.PKV_OK  # no-op
+        assert fn(fake, fake, fake, 1, fake, fake, None, fake, 4, 2, 64, 16, 0, 2, None) == pkv.PKV_EINVAL
+        assert fn(fake, fake, fake, 1, fake, fake, fake, fake, 4, 2, 96, 16, 0, 2, None) == pkv.PKV_EUNSUPPORTED
+
+    def pre(fn=lib.pkv_prefill_attention, codes=False, **kw):
+        a = dict(q=fake, k=fake, v=fake, ks=fake, vs=fake, t=fake, mb=4, qs=fake, mq=8, lens=fake, B=2, Hq=4, Hkv=2,
+                 D=64, bs=16, lay=0, NB=8, scale=0.125, out=fake, dt=2, ws=None, wsb=0, pb=0)
+        a.update(kw)
+        head = [a["q"], a["k"], a["v"]] + ([a["ks"], a["vs"]] if codes else [])
+        return fn(*head, a["t"], a["mb"], a["qs"], a["mq"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                  a["lay"], a["NB"], a["scale"], a["out"], a["dt"], a["ws"], a["wsb"], a["pb"], None)
+
+    assert pre(B=0) == pkv.PKV_OK and pre(mq=0) == pkv.PKV_OK
+    assert pre(qs=None) == pkv.PKV_EINVAL
+    assert pre(Hq=6, Hkv=4) == pkv.PKV_EINVAL
+    assert pre(D=96) == pkv.PKV_EUNSUPPORTED
+    assert pre(pb=129) == pkv.PKV_EINVAL
+    assert pre(lay=2) == pkv.PKV_EINVAL
+    assert pre(pb=1) == pkv.PKV_ESMALL  # several partitions per sequence, no workspace
+    for fn in (lib.pkv_prefill_attention_fp8, lib.pkv_prefill_attention_int8):
+        assert pre(fn, True, vs=None) == pkv.PKV_EINVAL
+        assert pre(fn, True, dt=0) == pkv.PKV_EUNSUPPORTED
+
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    sizes = (ctypes.c_int64 * 2)(32768, 32768)
+    assert lib.pkv_copy_blocks(ptrs, sizes, 0, 8, fake, 1, None) == pkv.PKV_EINVAL  # no tensors
+    assert lib.pkv_copy_blocks(ptrs, sizes, 5, 8, fake, 1, None) == pkv.PKV_EINVAL  # more than four
+    assert lib.pkv_copy_blocks(ptrs, sizes, 2, 8, None, 0, None) == pkv.PKV_OK  # nothing to copy
+    assert lib.pkv_copy_blocks(ptrs, sizes, 2, 8, None, 1, None) == pkv.PKV_EINVAL  # pairs missing
+    assert lib.pkv_copy_blocks((ctypes.c_void_p * 1)(0x1004), sizes, 1, 8, fake, 1, None) == pkv.PKV_EINVAL
+    assert lib.pkv_copy_blocks(ptrs, (ctypes.c_int64 * 1)(100), 1, 8, fake, 1, None) == pkv.PKV_EINVAL
