@@ -108,6 +108,8 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask) {
 using lds_void = __attribute__((address_space(3))) void;
 using s16x4_t = short __attribute__((ext_vector_type(4)));
 using lds_s16x4 = __attribute__((address_space(3))) s16x4_t;
+using i32x2_t = int __attribute__((ext_vector_type(2)));
+using lds_i32x2 = __attribute__((address_space(3))) i32x2_t;
 __device__ __forceinline__ lds_void* lds_ptr(char* p) { return (lds_void*)(p); }
 
 // IEEE maximum (a NaN operand gives NaN): unlike fmaxf it needs no operand
@@ -1384,6 +1386,11 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   static_assert(!kCodes || kSLoads * kW == 2 * kT, "scale rows split evenly over the waves");
   static_assert(!kTrLoad || kVLoads == kT, "one V block per wave per tile");
   static_assert(kVTileChunks % 64 == 0, "a wave's V chunks lie in one tile");
+  // E4M3 V codes (row order, 128 bytes a row): the 16-byte chunks of row r of
+  // the step's tile u are stored rotated by ((r >> 1) & 3) + 4 (u & 1), so the
+  // transposing reads of a half-wave (8 rows of each tile of a pair, two
+  // 8-byte halves of one chunk each) cover 256 distinct bytes of the bank space
+  auto v8_rot = [](int row, int u) { return ((row >> 1) & 3) | ((u & 1) << 2); };
   // the LDS buffers as separate objects: the compiler then tracks which
   // buffer each cache -> LDS load writes and waits only for the right ones
   __shared__ __attribute__((aligned(16))) char lds0[kBuf];
@@ -1547,7 +1554,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         const int cw = 64 * w + kThreads * i;  // the wave's first V chunk of the step
         const int u = cw / kVTileChunks;
         const int ch = cw - u * kVTileChunks + lane;
-        const int row = ch / kRowChunks, col = ch - (ch / kRowChunks) * kRowChunks;
+        const int row = ch / kRowChunks;
+        int col = ch - (ch / kRowChunks) * kRowChunks;
+        if constexpr (kConvWave) col ^= v8_rot(row, u);  // LDS chunk c of the row holds its chunk c ^ rot
         const __amdgpu_buffer_rsrc_t r = pick(rv, kThreads * i / kVTileChunks, kVHalf);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst + kKBytes + cw * 16), 16, row * rs + col * 16, 0, 0,
                                                  0);
@@ -1753,28 +1762,28 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         continue;
       }
       if constexpr (kConvWave) {
-        // codes of rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's D/16
-        // elements, converted straight into the A operand of each block mt
-        Fp8Regs<D> ta, tb;
+        // Transposing 8-bit reads (ds_read_b64_tr_b8): in each quarter-wave,
+        // lane s = 2e + h names 8 codes of key e (rows 4*q4 + e of tile 2pp for
+        // e < 4, rows 4*q4 + e - 4 of tile 2pp+1) at columns 16 mt + 8h, and
+        // lane i receives byte (i & 7) of lanes 2e + (i >> 3), e = 0..7: the
+        // eight keys' codes at column 16 mt + i, which converted in order are
+        // the A operand of output block mt (rows d = 16 mt + i).
+        const int e = ln >> 1, h = ln & 1;
+        const int tu = 2 * pp + (e >> 2), row = 4 * q4 + (e & 3);
+        const char* rb = vl + (tu * kTile + row) * kRowB + 8 * h;
+        const int rot = v8_rot(row, tu);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const char* ra = vl + (2 * pp * kTile + 4 * q4 + i) * kRowB + ln * (D / 16);
-          const u32x2 x = *reinterpret_cast<const u32x2*>(ra);
-          const u32x2 y = *reinterpret_cast<const u32x2*>(ra + kTile * kRowB);
-          ta.v[i][0] = x[0];
-          ta.v[i][1] = x[1];
-          tb.v[i][0] = y[0];
-          tb.v[i][1] = y[1];
-        }
-        u32x4 av[S::kE];
-        codes_v_operand<kQ, T, D>(ta, tb, av);
-#pragma unroll
-        for (int mt = 0; mt < S::kE; ++mt)
+        for (int mt = 0; mt < S::kE; ++mt) {
+          const auto x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(rb + (mt ^ rot) * 16));
+          const u32x2 c2 = __builtin_bit_cast(u32x2, x);
+          const u32x2 lo = codes4_to_16<kQ, T>(c2[0]), hi = codes4_to_16<kQ, T>(c2[1]);
+          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int rg = 0; rg < kR; ++rg) {
-            acc[rg][mt] = mfma_qk16<T>(av[mt], pw_hi[rg][pp], acc[rg][mt]);
-            acc[rg][mt] = mfma_qk16<T>(av[mt], pw_lo[rg][pp], acc[rg][mt]);
+            acc[rg][mt] = mfma_qk16<T>(av, pw_hi[rg][pp], acc[rg][mt]);
+            acc[rg][mt] = mfma_qk16<T>(av, pw_lo[rg][pp], acc[rg][mt]);
           }
+        }
         continue;
       }
       // V rows 4*q4 + i of tiles 2pp and 2pp+1, this lane's E elements,
@@ -1902,11 +1911,11 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     inv[rg] = l_tot[rg] > 0.f ? 1.0f / l_tot[rg] : 0.f;
   }
   // this lane's 4 x E output values of row group rg: d = 16 mt + 4*q4 + i
-  // (transposed V reads), else d = (4*q4 + i) * E + mt
+  // (transposed V reads, 16- or 8-bit), else d = (4*q4 + i) * E + mt
   auto write_out = [&](int rg, float scale_by) {
     if (!head_ok[rg]) return;
     char* orow = out + qidx[rg] * S::kRowBytes;
-    if constexpr (kTrV) {
+    if constexpr (kTrV || kConvWave) {
 #pragma unroll
       for (int mt = 0; mt < S::kE; ++mt) {
         const u32x2 wv = {to_bits16<T>(acc[rg][mt][0] * scale_by) | (to_bits16<T>(acc[rg][mt][1] * scale_by) << 16),
