@@ -81,10 +81,11 @@ def test_prefill_parity(torch_dev, layout, bs, dtype, shape):
 @pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 @pytest.mark.parametrize("dtype,shape,bs", [("bf16", (32, 8, 128), 16), ("f16", (16, 2, 128), 64),
+                                            ("bf16", (8, 8, 128), 16), ("bf16", (32, 1, 128), 32),
                                             ("bf16", (8, 8, 64), 16)], ids=lambda x: str(x))
 def test_prefill_fp8_parity(torch_dev, layout, fmt, dtype, shape, bs):
     """8-bit caches: head size 128 takes the LDS kernel (bf16 and fp16
-    queries), head size 64 the one-wave kernel."""
+    queries; GQA, MHA and MQA), head size 64 the one-wave kernel."""
     torch, dev = torch_dev
     Hq, Hkv, D = shape
     lens, q_start, max_q = chunk_layout()
