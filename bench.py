@@ -265,14 +265,17 @@ def run_prefill(args):
     flops = 4 * Hq * D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
     cpu = None
-    if args.cpu_budget > 0 and not q8:
+    if args.cpu_budget > 0:
         import oracle
         import time as _t
         # one sequence's chunk, the first rows only, on the host
         blocks = asg.blocks[0]
         idx = torch.from_numpy(blocks.astype(np.int64)).to(dev)
-        kh = wl.torch_to_raw(kc.index_select(0, idx), "bf16")
-        vh = wl.torch_to_raw(vc.index_select(0, idx), "bf16")
+        if q8:
+            kh, vh, ksh, vsh = (x.index_select(0, idx).cpu().numpy() for x in (kc, vc, ks, vs))
+        else:
+            kh = wl.torch_to_raw(kc.index_select(0, idx), "bf16")
+            vh = wl.torch_to_raw(vc.index_select(0, idx), "bf16")
         qh = wl.torch_to_raw(q[:C], "bf16")
         table = np.arange(len(blocks), dtype=np.int32)[None, :]
         from threadpoolctl import threadpool_limits
@@ -281,8 +284,12 @@ def run_prefill(args):
         with threadpool_limits(nt):
             while spent < min(args.cpu_budget, 10.0) and rows <= C:
                 t = _t.perf_counter()
-                oracle.prefill_attention(qh[:rows], kh, vh, table, [0, rows], [P + rows], cfg.scale, Hkv, bs, "bf16",
-                                         args.layout)
+                if q8:
+                    oracle.prefill_attention_fp8(qh[:rows], kh, vh, ksh, vsh, table, [0, rows], [P + rows], cfg.scale,
+                                                 Hkv, bs, "bf16", args.layout, fmt=fmt)
+                else:
+                    oracle.prefill_attention(qh[:rows], kh, vh, table, [0, rows], [P + rows], cfg.scale, Hkv, bs,
+                                             "bf16", args.layout)
                 spent = _t.perf_counter() - t
                 pairs_cpu = sum(P + i + 1 for i in range(rows))
                 rows *= 2
