@@ -408,6 +408,53 @@ def test_fused_step_zero_length_and_counters_reset(torch_dev):
     assert not ws[-256:].any(), "arrival counters not reset"
 
 
+def test_fused_step_replays_under_graph_capture(torch_dev):
+    """Two layers' fused steps captured in one graph and replayed three times,
+    with eager work on the same stream between the replays: every replay's
+    outputs equal the eager ones bit for bit (the arrival counters reset
+    inside the kernel; nothing in the step is a memset), and the appended
+    rows land in both layers' caches."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("graph", 0, 2, 6, 32, 8, 128, 16, "bf16", context_lens=(1, 17, 300, 1000, 64, 513))
+    wk = wl.make_host_workload(cfg)
+    q = wl.raw_to_torch(wk.q, "bf16", dev)
+    kn, vn = wl.raw_to_torch(wk.k_new, "bf16", dev), wl.raw_to_torch(wk.v_new, "bf16", dev)
+    t = torch.from_numpy(wk.block_tables).to(dev)
+    lens = torch.from_numpy(wk.context_lens).to(dev)
+    caches = [(wl.raw_to_torch(wk.k_cache, "bf16", dev), wl.raw_to_torch(wk.v_cache, "bf16", dev)) for _ in range(2)]
+    ws = [pkv.alloc_step_workspace(q, caches[0][0], t, 2) for _ in range(2)]
+    outs = [torch.empty_like(q) for _ in range(2)]
+
+    def steps():
+        for layer in range(2):
+            kc, vc = caches[layer]
+            pkv.decode_step(q, kn, vn, kc, vc, t, lens, cfg.scale, outs[layer], ws[layer], 2)
+
+    note("fused step: eager reference, then graph capture and replays")
+    steps()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    ref, _, _, _ = oracle_step(wk)
+    check_close(oracle.upcast(wl.torch_to_raw(eager[0], "bf16"), "bf16"), ref, "bf16", "graph eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan"))  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer in range(2):
+            assert torch.equal(outs[layer], eager[layer]), f"replay {r} layer {layer} differs"
+    for layer in range(2):
+        assert not ws[layer][-256:].any(), "arrival counters not reset"
+        for b, n in enumerate(wk.context_lens):
+            blk = int(wk.block_tables[b][(n - 1) // 16])
+            assert torch.equal(caches[layer][0][blk, :, (n - 1) % 16], kn[b])
+
+
 @pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "llama3_70b", "qwen25_7b_ragged"])
 def test_fused_step_full_size_sampled(torch_dev, cfg_name):
     torch, dev = torch_dev
