@@ -408,6 +408,30 @@ def test_fused_step_zero_length_and_counters_reset(torch_dev):
     assert not ws[-256:].any(), "arrival counters not reset"
 
 
+def test_fused_step_on_a_side_stream(torch_dev):
+    """The stream argument is honoured: a fused step launched on a second
+    stream (default priority), after inputs written on the current stream that
+    the side stream waits for, matches the reference once that stream is synchronized."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("stream", 0, 1, 3, 16, 4, 128, 16, "bf16", context_lens=(5, 129, 700))
+    wk = wl.make_host_workload(cfg)
+    t = torch.from_numpy(wk.block_tables).to(dev)
+    lens = torch.from_numpy(wk.context_lens).to(dev)
+    q = wl.raw_to_torch(wk.q, "bf16", dev)
+    kc, vc = wl.raw_to_torch(wk.k_cache, "bf16", dev), wl.raw_to_torch(wk.v_cache, "bf16", dev)
+    kn, vn = wl.raw_to_torch(wk.k_new, "bf16", dev), wl.raw_to_torch(wk.v_new, "bf16", dev)
+    ws = pkv.alloc_step_workspace(q, kc, t, 2)
+    out = torch.full_like(q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    note("fused step on a side stream")
+    pkv.decode_step(q, kn, vn, kc, vc, t, lens, cfg.scale, out, ws, 2, stream=side)
+    side.synchronize()
+    ref, kc_o, _, _ = oracle_step(wk)
+    check_close(oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16"), ref, "bf16", "side stream")
+    assert wl.torch_to_raw(kc, "bf16").tobytes() == kc_o.tobytes()
+
+
 def test_fused_step_replays_under_graph_capture(torch_dev):
     """Two layers' fused steps captured in one graph and replayed three times,
     with eager work on the same stream between the replays: every replay's
