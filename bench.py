@@ -63,62 +63,114 @@ def pool_assignment(cfg, lens, pkv, wl):
     return asg, slots, pool.stats()
 
 
-def cpu_samples(wkd, max_seqs=32):
-    """Host copies of layer 0's first sequences, taken before any append, for
-    timing the CPU reference."""
-    import torch
+def snapshot_layer0(wkd, fp8, dt):
+    """Host copies of layer 0's inputs, taken before any step runs: the whole
+    K/V pools in the timed layout (the new token's slot still holds NaN), the
+    queries, the new K/V rows, the block tables and the lengths."""
+    if fp8:
+        pools = [wkd.k_codes[0].cpu().numpy(), wkd.v_codes[0].cpu().numpy(), wkd.k_scales[0].cpu().numpy(),
+                 wkd.v_scales[0].cpu().numpy()]
+    else:
+        pools = [wl_raw(wkd.k_cache[0], dt), wl_raw(wkd.v_cache[0], dt)]
+    return dict(pools=pools, q=wl_raw(wkd.q[0], dt), kn=wl_raw(wkd.k_new[0], dt), vn=wl_raw(wkd.v_new[0], dt),
+                table=wkd.block_tables.cpu().numpy(), lens=np.asarray(wkd.context_lens, np.int32).copy())
+
+
+def wl_raw(t, dt):
     from paged_kv_cache_156_amd import workloads as wl
-    cfg = wkd.cfg
-    dt = cfg.dtype
-    samples = []
-    for b in range(len(wkd.context_lens)):
-        blocks = wkd.assignment.blocks[b]
-        idx = torch.from_numpy(blocks.astype(np.int64)).to(wkd.k_cache[0].device)
-        samples.append(dict(
-            kc=wl.torch_to_raw(wkd.k_cache[0].index_select(0, idx), dt),
-            vc=wl.torch_to_raw(wkd.v_cache[0].index_select(0, idx), dt),
-            q=wl.torch_to_raw(wkd.q[0][b:b + 1], dt), kn=wl.torch_to_raw(wkd.k_new[0][b:b + 1], dt),
-            vn=wl.torch_to_raw(wkd.v_new[0][b:b + 1], dt), n=int(wkd.context_lens[b]),
-            table=np.arange(len(blocks), dtype=np.int32)[None, :]))
-        if len(samples) >= max_seqs:
-            break
-    return samples
+    return wl.torch_to_raw(t, dt)
 
 
-def cpu_threads():
-    """BLAS threads for the CPU reference: the host's cores, capped by the
-    OMP_NUM_THREADS share the environment grants this process."""
-    n = os.cpu_count() or 1
-    env = os.environ.get("OMP_NUM_THREADS", "")
-    return max(1, min(n, int(env))) if env.isdigit() else n
+def pools_after(wkd, fp8, dt):
+    """Host copies of layer 0's pools as the timed steps left them."""
+    if fp8:
+        return [wkd.k_codes[0].cpu().numpy(), wkd.v_codes[0].cpu().numpy(), wkd.k_scales[0].cpu().numpy(),
+                wkd.v_scales[0].cpu().numpy()]
+    return [wl_raw(wkd.k_cache[0], dt), wl_raw(wkd.v_cache[0], dt)]
 
 
-def run_cpu_baseline(samples, cfg, budget_s):
-    """Time the CPU reference (BLAS on cpu_threads() threads) until
-    ``budget_s`` of work is done."""
+def oracle_check(snap, out0, after, cfg, layout, fp8, fmt, budget_s, min_seqs=32):
+    """The CPU reference on layer 0, timed, and compared with the GPU.
+
+    The reference appends every sequence's new token at its slot in the whole
+    layer-0 pool (the slot rule applied to the same block tables the GPU used),
+    then attends sequence by sequence through those tables until ``budget_s``
+    of work is done and at least ``min_seqs`` sequences (or all of them) are
+    checked. Each checked sequence's output is compared element by element with
+    the timed run's layer-0 output; the appended pools are compared byte for
+    byte with the GPU's. Runs on one thread: the reference gathers token by
+    token in a Python loop, whatever BLAS could offer.
+    """
     import oracle
     from threadpoolctl import threadpool_limits
-    with threadpool_limits(cpu_threads()):
-        return _run_cpu(samples, cfg, budget_s, oracle)
-
-
-def _run_cpu(samples, cfg, budget_s, oracle):
-    """Cycle over the sampled sequences until ``budget_s`` of CPU work is spent."""
-    import itertools
-    done, kv_bytes, t_total = 0, 0, 0.0
-    for s in itertools.cycle(samples):
+    dt, bs, Hkv = cfg.dtype, cfg.block_size, cfg.num_kv_heads
+    table, lens = snap["table"], snap["lens"]
+    pools = [p.copy() for p in snap["pools"]]
+    B = len(lens)
+    atol, rtol = (1e-5, 1e-5) if dt == "f32" else (2e-3, 1e-2)
+    esz = 1 if fp8 else (4 if dt == "f32" else 2)
+    row_bytes = cfg.head_dim * esz + (4 if fp8 else 0)
+    done, kv_bytes, worst, worst_ratio, bad = 0, 0, 0.0, 0.0, []
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        kc, vc = s["kc"].copy(), s["vc"].copy()
-        slots = oracle.slot_mapping(s["table"], [s["n"] - 1], cfg.block_size)
-        oracle.kv_append(kc, vc, s["kn"], s["vn"], slots, cfg.block_size)
-        oracle.decode_attention(s["q"], kc, vc, s["table"], [s["n"]], cfg.scale, cfg.num_kv_heads, cfg.block_size,
-                                cfg.dtype)
-        t_total += time.perf_counter() - t0
-        done += 1
-        kv_bytes += 2 * cfg.num_kv_heads * cfg.head_dim * (4 if cfg.dtype == "f32" else 2) * s["n"]
-        if t_total >= budget_s:
-            break
-    return done, kv_bytes, t_total
+        slots = oracle.slot_mapping(table, lens - 1, bs)
+        if fp8:
+            oracle.kv_append_fp8(*pools, snap["kn"], snap["vn"], slots, bs, dt, layout, fmt)
+        else:
+            oracle.kv_append(pools[0], pools[1], snap["kn"], snap["vn"], slots, bs, layout)
+        t_total = time.perf_counter() - t0
+        for b in range(B):
+            if done >= min(B, min_seqs) and t_total >= budget_s:
+                break
+            t = time.perf_counter()
+            if fp8:
+                ref = oracle.decode_attention_fp8(snap["q"], *pools, table, lens, cfg.scale, Hkv, bs, dt, seqs=[b],
+                                                  layout=layout, fmt=fmt)[b]
+            else:
+                ref = oracle.decode_attention(snap["q"], pools[0], pools[1], table, lens, cfg.scale, Hkv, bs, dt,
+                                              seqs=[b], layout=layout)[b]
+            t_total += time.perf_counter() - t
+            done += 1
+            kv_bytes += 2 * Hkv * row_bytes * int(lens[b])
+            got = oracle.upcast(out0[b], dt)
+            err = np.abs(got - ref)
+            ratio = float(np.max(err / (atol + rtol * np.abs(ref)))) if err.size else 0.0
+            if not np.isfinite(got).all() or not ratio <= 1.0:
+                bad.append(b)
+            worst, worst_ratio = max(worst, float(np.nanmax(err))), max(worst_ratio, ratio)
+    append_exact = all(a.tobytes() == p.tobytes() for a, p in zip(after, pools))
+    return dict(done=done, kv_bytes=kv_bytes, t=t_total, max_abs_err=worst, max_err_over_tol=worst_ratio,
+                bad_seqs=bad, append_bit_exact=append_exact, tol=f"|gpu - ref| <= {atol:g} + {rtol:g} |ref|")
+
+
+def time_stream(pkv, torch, wkd, L, fp8, lay, pb, kcache0, stream, args, step_kv):
+    """Read ceiling of the decode access pattern: every tile the decode launches
+    read, in their order, with nothing computed (same pools, tables and
+    partitions); ms per L-layer step and GB/s of K/V."""
+    sink = pkv.stream_sink(kcache0, wkd.block_tables, pb, layout=lay)
+
+    def stream_step():
+        for l in range(L):
+            if fp8:
+                pkv.stream_tiles(wkd.k_codes[l], wkd.v_codes[l], wkd.block_tables, wkd.context_lens_dev, pb, sink,
+                                 wkd.k_scales[l], wkd.v_scales[l], layout=lay)
+            else:
+                pkv.stream_tiles(wkd.k_cache[l], wkd.v_cache[l], wkd.block_tables, wkd.context_lens_dev, pb, sink,
+                                 layout=lay)
+
+    for _ in range(max(1, args.warmup)):
+        stream_step()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(args.steps):
+        stream_step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    stream_ms = s0.elapsed_time(s1) / args.steps
+    stream_gbs = step_kv / (stream_ms * 1e-3) / 1e9
+    log(f"stream ceiling: {stream_ms:.3f} ms per {L} launches = {stream_gbs:.0f} GB/s of K/V")
+    return stream_ms, stream_gbs
 
 
 def run_copy_blocks(args):
@@ -280,7 +332,7 @@ def run_prefill(args):
         table = np.arange(len(blocks), dtype=np.int32)[None, :]
         from threadpoolctl import threadpool_limits
         rows, spent, pairs_cpu = 1, 0.0, 0
-        nt = cpu_threads()
+        nt = 1  # the reference attends row by row in Python; BLAS is held to one thread
         with threadpool_limits(nt):
             while spent < min(args.cpu_budget, 10.0) and rows <= C:
                 t = _t.perf_counter()
@@ -294,8 +346,8 @@ def run_prefill(args):
                 pairs_cpu = sum(P + i + 1 for i in range(rows))
                 rows *= 2
         cpu = {"value": round(4 * Hq * D * pairs_cpu / spent / 1e12, 6), "unit": "TFLOP/s", "cores": nt,
-               "kind": "oracle", "sample": f"{rows // 2} query tokens of one sequence's chunk, fp64 NumPy with {nt} "
-                                           f"BLAS thread(s), {spent:.1f}s"}
+               "kind": "oracle", "sample": f"{rows // 2} query tokens of one sequence's chunk, fp64 NumPy on one "
+                                           f"thread, {spent:.1f}s"}
     result = {
         "metric": "chunked-prefill paged attention TFLOP/s (QK^T + PV over the causal triangle)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -331,8 +383,9 @@ def main():
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="cache block layout: HND [NB, Hkv, bs, D] (default) or NHD [NB, bs, Hkv, D]")
     ap.add_argument("--block-size", type=int, default=0, help="tokens per cache block (0 = the configuration's, 16)")
-    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
-                    help="decode: the decode step (default); copy_blocks: copy-on-write block copies; "
+    ap.add_argument("--op", choices=("decode", "stream", "copy_blocks", "prefill"), default="decode",
+                    help="decode: the decode step (default); stream: the read ceiling of the decode access pattern "
+                         "(the same tiles, nothing computed); copy_blocks: copy-on-write block copies; "
                          "prefill: chunked-prefill attention")
     ap.add_argument("--prefill-seqs", type=int, default=4)
     ap.add_argument("--prefill-chunk", type=int, default=512)
@@ -395,7 +448,7 @@ def main():
     log(f"device workload ready in {time.time() - t0:.1f}s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
 
-    samples = cpu_samples(wkd) if (args.cpu_budget > 0 and not fp8) else []
+    snap = snapshot_layer0(wkd, fp8, cfg.dtype) if (args.cpu_budget > 0 and args.op == "decode") else None
 
     max_blocks = wkd.block_tables.shape[1]
     pb = args.partition_blocks or pkv.decode_partition_blocks(B, Hq, Hkv, max_blocks, bs)
@@ -408,6 +461,28 @@ def main():
     slots_d = torch.from_numpy(slots).to(dev)
     outs = [torch.empty_like(wkd.q[l]) for l in range(L)]
     stream = torch.cuda.current_stream()
+    # K/V bytes read per layer: codes + one fp32 scale per row for 8-bit caches
+    sum_n = int(lens.sum())
+    kv_layer = 2 * Hkv * (D + 4) * sum_n if fp8 else 2 * Hkv * D * esz * sum_n
+    step_kv = kv_layer * L
+
+    if args.op == "stream":
+        stream_ms, stream_gbs = time_stream(pkv, torch, wkd, L, fp8, lay, pb, kcache0, stream, args, step_kv)
+        print(json.dumps({
+            "metric": "decode access-pattern read ceiling GB/s (K/V tiles through the block tables, nothing computed)",
+            "value": round(stream_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(stream_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": f"{fmt} codes + f32 row scales" if fp8 else cfg.dtype, "data": "synthetic",
+            "config": {"workload": f"{cfg.name}: the tiles of {L} decode launches ({lay} blocks of {bs}, partitions "
+                                   f"of {pb} blocks)", "layers": L, "partition_blocks": pb, "kv": args.kv,
+                       "layout": lay, "block_size": bs},
+            "frac_of_hbm_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "stream_tiles_kernel", "achieved": round(stream_gbs, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(stream_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "alg_bytes_per_launch": kv_layer,
+                         "avg_launch_us": round(stream_ms / L * 1e3, 2), "kernel_sha": kernel_sha()},
+            "cpu_baseline": None}), flush=True)
+        return
 
     def step(events=None):
         for l in range(L):
@@ -485,14 +560,10 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; partition kernel avg {part_avg_ms * 1e3:.1f} us")
 
     # algorithmic bytes
-    sum_n = int(lens.sum())
-    # K/V bytes read per layer: codes + one fp32 scale per row for FP8
-    kv_layer = 2 * Hkv * (D + 4) * sum_n if fp8 else 2 * Hkv * D * esz * sum_n
     q_out = 2 * B * Hq * D * esz
     tables = 4 * sum(-(-int(n) // bs) for n in lens) + 4 * B
     append = 2 * B * Hkv * D * esz + (2 * B * Hkv * (D + 4) if fp8 else 2 * B * Hkv * D * esz)  # fused step only
     part_alg = kv_layer + q_out + tables + (append if fused else 0)
-    step_kv = kv_layer * L
     gbs = step_kv / (ms_per_step * 1e-3) / 1e9
     achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
 
@@ -505,17 +576,33 @@ def main():
         if tr.get("kernel_sha") == kernel_sha() and tr.get("partition_blocks") == pb:
             traffic = tr.get("bytes_per_launch")
 
-    cpu = None
-    if samples:
-        done, cpu_bytes, cpu_t = run_cpu_baseline(samples, cfg, args.cpu_budget)
-        seq_layer_s = cpu_t / done
-        nt = cpu_threads()
-        cpu = {"value": round(cpu_bytes / cpu_t / 1e9, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
-               "seqs_per_s": round(1.0 / (seq_layer_s * L), 4),
-               "sample": f"{done} sequence-layer(s) (cycling over layer 0's first {len(samples)} sequences) of "
-                         f"{cfg.name}, append + attention in fp64 NumPy with {nt} BLAS thread(s), {cpu_t:.1f}s; "
-                         f"seqs/s extrapolated to {L} layers"}
+    stream_ms, stream_gbs = time_stream(pkv, torch, wkd, L, fp8, lay, pb, kcache0, stream, args, step_kv)
+
+    cpu, parity = None, None
+    if snap is not None:
+        log("CPU reference on layer 0 (append, then attention sequence by sequence) and comparison ...")
+        chk = oracle_check(snap, wl.torch_to_raw(outs[0], cfg.dtype), pools_after(wkd, fp8, cfg.dtype), cfg, lay,
+                           fp8, fmt, args.cpu_budget)
+        cpu = {"value": round(chk["kv_bytes"] / chk["t"] / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seqs_per_s": round(chk["done"] / (chk["t"] * L), 4),
+               "sample": f"layer 0 of {cfg.name}: the new token of all {B} sequences appended into the whole pool, "
+                         f"then attention for the first {chk['done']} sequences through the same block tables, "
+                         f"fp64 NumPy on one thread (a per-token Python gather), {chk['t']:.1f}s; seqs/s "
+                         f"extrapolated to {L} layers"}
+        parity = {"checked_seqs": chk["done"], "of_seqs": B, "max_abs_err": chk["max_abs_err"],
+                  "max_err_over_tol": round(chk["max_err_over_tol"], 4), "tol": chk["tol"],
+                  "append_bit_exact": chk["append_bit_exact"], "bad_seqs": chk["bad_seqs"][:16],
+                  "ok": chk["append_bit_exact"] and not chk["bad_seqs"]}
         log(f"cpu baseline: {cpu}")
+        log(f"parity against the CPU reference: {parity}")
+
+    # bytes of distinct cache rows read (shared prefix blocks counted once)
+    rows_seen = {}
+    for b, n in enumerate(lens):
+        for lb, pbk in enumerate(asg.blocks[b][: -(-int(n) // bs)]):
+            rows_seen[int(pbk)] = max(rows_seen.get(int(pbk), 0), min(bs, int(n) - lb * bs))
+    unique_tokens = sum(rows_seen.values())
+    unique_layer = 2 * Hkv * ((D + 4) if fp8 else D * esz) * unique_tokens
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2**20
@@ -548,8 +635,14 @@ def main():
                    "global_batch": B, "seq_len": int(lens.max()), "layers": L, "partition_blocks": pb,
                    "mode": args.mode, "kv": args.kv, "layout": lay, "block_size": bs},
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "stream_ceiling_gbps": round(stream_gbs, 2),
+        "frac_of_stream_ceiling": round(gbs / stream_gbs, 4),
         "seqs_per_s": round(B / (ms_per_step * 1e-3), 2),
         "kv_bytes_per_step": step_kv,
+        "unique_kv_bytes_per_step": unique_layer * L,
+        "unique_kv_gbps": round(unique_layer * L / (ms_per_step * 1e-3) / 1e9, 2),
+        "parity_checked_seqs": parity["checked_seqs"] if parity else 0,
+        "parity": parity,
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel<" + ("step" if fused else "split") + ">",
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -560,6 +653,9 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+    if parity is not None and not parity["ok"]:
+        log(f"PARITY FAILURE: {parity}")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

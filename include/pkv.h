@@ -136,9 +136,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t n
  *   q             device [num_seqs, num_heads, head_dim]
  *   k_cache, v_cache  device, in `layout` (see pkv_layout)
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]: entry [b][i]
- *                 is the physical block of logical block i of sequence b;
- *                 entries past ceil(context_lens[b] / block_size) are never
- *                 read (any value)
+ *                 is the physical block of logical block i of sequence b.
+ *                 Each partition reads every entry of its slice of the row
+ *                 (up to max_blocks_per_seq); entries past
+ *                 ceil(context_lens[b] / block_size) may hold any value:
+ *                 they are read and then ignored, and no K/V is fetched
+ *                 through them
  *   context_lens  device int32 [num_seqs]: tokens attended, the newest one
  *                 included; 0 gives an all-zero output row
  *   scale         multiplies q . k (1/sqrt(head_dim) for standard attention)
@@ -219,7 +222,10 @@ pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const
  *                 workspace must not run concurrently.
  * Every other argument as pkv_paged_decode_attention. The newest token's
  * block must be private to its sequence (the host pool's slot builder checks
- * this; here it is a precondition).
+ * this; here it is a precondition). A sequence whose context_lens[b] exceeds
+ * max_blocks_per_seq * block_size (a precondition violation) appends nothing:
+ * its length is clamped for reading, as in pkv_paged_decode_attention, and
+ * no cached token is overwritten.
  */
 size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
@@ -246,7 +252,9 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
  *   - quantization of a new row x (head_dim values, computed in fp32):
  *     amax = max |x|, scale = amax / 448, inv = 448 / amax (1 and 1 when
  *     amax == 0), code = E4M3 nearest to x * inv (ties to even, clamped to
- *     +-448, sign kept).
+ *     +-448, sign kept);
+ *   - a row holding a NaN or an infinity gets scale NaN and every code 0x7F
+ *     (E4M3 NaN), so each of its values reads back as NaN.
  * Queries and outputs stay bf16 or fp16 (dtype); codes are converted exactly
  * to that type in registers, scores and weights are scaled in fp32.
  *
@@ -289,7 +297,10 @@ pkv_status pkv_decode_step_fp8(const void* q, const void* k_new, const void* v_n
  *   - value attended over = code * scale;
  *   - quantization of a new row x (fp32): amax = max |x|, scale = amax / 127,
  *     inv = 127 / amax (1 and 1 when amax == 0), code = x * inv rounded to the
- *     nearest integer (ties to even), clamped to +-127 (-128 is never produced).
+ *     nearest integer (ties to even), clamped to +-127 (-128 is never produced
+ *     for a finite row);
+ *   - a row holding a NaN or an infinity gets scale NaN and every code -128
+ *     (0x80), so each of its values reads back as NaN.
  * Queries and outputs are bf16 or fp16 (f32 is EUNSUPPORTED); codes convert
  * exactly to those types. Arguments, layouts and errors as the _fp8 calls.
  */
@@ -391,6 +402,35 @@ pkv_status pkv_prefill_attention_fp8(const void* q, const void* k_cache, const v
 pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int32_t n_caches, int32_t num_blocks,
                            const int32_t* pairs, int32_t n_pairs, void* stream);
 
+/*
+ * pkv_stream_tiles -- a measurement call, not part of attention: the read
+ * ceiling of the decode access pattern. It launches the workgroups a decode
+ * launch over these caches would (one wave per (sequence, KV head, context
+ * partition), the same partitions, workgroup shape and XCD order), looks up
+ * each tile through block_tables and loads the K and V tiles (plus the row
+ * scales when given) with the same bounded nontemporal loads, and computes
+ * nothing but an XOR of the loaded words, written to sink. The time it takes
+ * is what the memory system gives for exactly the bytes decode attention must
+ * read (decode is bound by those reads: "Understanding KV Cache" §2.2).
+ *
+ *   k_cache, v_cache  device caches in `layout`, rows of row_bytes bytes per
+ *                 head (head_dim * element size: 64, 128, 256 or 512)
+ *   k_scales, v_scales  device fp32 row scales of 8-bit caches, or both NULL
+ *   block_tables, context_lens, max_blocks_per_seq, num_blocks, block_size
+ *                 as pkv_paged_decode_attention
+ *   partition_blocks  blocks per partition (> 0; pass the decode call's
+ *                 pkv_decode_partition_blocks to mirror it)
+ *   sink          device uint32, >= num_seqs * num_kv_heads * P * 64 words,
+ *                 P = ceil(max_blocks_per_seq / partition_blocks); overwritten
+ * Errors: EINVAL (null pointers, one scale pointer without the other, sizes,
+ * partition_blocks), EUNSUPPORTED (row_bytes, block_size), ESMALL (sink), EHIP.
+ */
+pkv_status pkv_stream_tiles(const void* k_cache, const void* v_cache, const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                            pkv_layout layout, int32_t num_blocks, int32_t partition_blocks, uint32_t* sink,
+                            size_t sink_words, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block pool, block tables and slot mapping                            */
 /* ------------------------------------------------------------------------ */
@@ -422,7 +462,10 @@ void pkv_pool_destroy(pkv_pool* pool);
 
 /* Grow sequence `seq` to new_len tokens, taking ceil(new_len / block_size)
  * minus its current block count from the free list. Shrinking is ERANGE.
- * ENOMEM if the pool runs dry (the sequence is left unchanged). */
+ * ENOMEM if the pool runs dry; EBUSY if the new positions would start inside
+ * a partial last block that another sequence or the prefix cache also holds
+ * (use pkv_seq_append_slots, which copies such a block first). On any error
+ * the sequence is left unchanged. */
 pkv_status pkv_seq_grow(pkv_pool* pool, int32_t seq, int32_t new_len);
 
 /* Make empty sequence `dst` share the first floor(n_tokens / block_size) FULL

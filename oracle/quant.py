@@ -23,6 +23,12 @@ INT8 (the page's other named option) follows the same rule with 127 as the
 largest code: scale = amax / 127, inv = 127 / amax (float32; amax = 0 gives 1
 and 1), code = float32(x * inv) rounded to the nearest integer (ties to even),
 clamped to [-127, 127]; the value is code * scale.
+
+A row holding a NaN or an infinity has no finite scale. The pages say nothing
+about such rows; the reading here is that the whole row becomes unreadable:
+scale NaN and every code set to the format's marker -- E4M3 0x7F (its NaN),
+INT8 -128 (the one code a finite row never gets) -- so every value of the row
+reads back as NaN, as a NaN in a 16-bit cache would make the attention NaN.
 """
 from __future__ import annotations
 
@@ -78,13 +84,15 @@ def quantize_rows(x: np.ndarray):
     last axis), following the module docstring step by step in float32.
     """
     x = np.asarray(x, dtype=np.float32)
-    amax = np.max(np.abs(x), axis=-1).astype(np.float32)
+    amax = np.max(np.abs(x), axis=-1).astype(np.float32)  # NaN if the row holds one
+    bad = ~np.isfinite(amax)
     zero = amax == 0
-    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    safe = np.where(zero | bad, np.float32(1), amax).astype(np.float32)
     scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
     inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
-    y = (x * inv[..., None]).astype(np.float32)
-    return e4m3_encode(y), scale
+    y = (np.where(bad[..., None], np.float32(0), x) * inv[..., None]).astype(np.float32)
+    codes = np.where(bad[..., None], np.uint8(0x7F), e4m3_encode(y)).astype(np.uint8)
+    return codes, np.where(bad, np.float32(np.nan), scale).astype(np.float32)
 
 
 def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -99,14 +107,16 @@ def quantize_rows_int8(x: np.ndarray):
     """INT8 codes (int8, x's shape) and float32 scales of the last axis of ``x``,
     following the module docstring step by step in float32."""
     x = np.asarray(x, dtype=np.float32)
-    amax = np.max(np.abs(x), axis=-1).astype(np.float32)
+    amax = np.max(np.abs(x), axis=-1).astype(np.float32)  # NaN if the row holds one
+    bad = ~np.isfinite(amax)
     zero = amax == 0
-    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    safe = np.where(zero | bad, np.float32(1), amax).astype(np.float32)
     scale = np.where(zero, np.float32(1), safe / np.float32(INT8_MAX)).astype(np.float32)
     inv = np.where(zero, np.float32(1), np.float32(INT8_MAX) / safe).astype(np.float32)
-    y = (x * inv[..., None]).astype(np.float32)
+    y = (np.where(bad[..., None], np.float32(0), x) * inv[..., None]).astype(np.float32)
     codes = np.clip(np.rint(y.astype(np.float64)), -INT8_MAX, INT8_MAX).astype(np.int8)
-    return codes, scale
+    codes = np.where(bad[..., None], np.int8(-128), codes).astype(np.int8)
+    return codes, np.where(bad, np.float32(np.nan), scale).astype(np.float32)
 
 
 def int8_decode(codes: np.ndarray) -> np.ndarray:

@@ -75,6 +75,8 @@ SIGNATURES = [
     ("pkv_prefill_attention_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
     ("pkv_copy_blocks", _i32, [_c.POINTER(_vp), _pi64, _i32, _i32, _vp, _i32, _vp]),
+    ("pkv_stream_tiles", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                                _sz, _vp]),
     ("pkv_pool_create", _i32, [_i32, _i32, _i32, _u64, _c.POINTER(_vp)]),
     ("pkv_pool_destroy", None, [_vp]),
     ("pkv_seq_grow", _i32, [_vp, _i32, _i32]),
@@ -351,6 +353,36 @@ def copy_blocks(caches, pairs, stream=None):
         raise ValueError("pairs must be [n, 2]")
     pp = _dev(pairs, "pairs", torch.int32) if n else None
     _check(load().pkv_copy_blocks(ptrs, sizes, len(caches), nb, pp, n, _stream_ptr(stream)), "pkv_copy_blocks")
+
+
+def stream_sink(k_cache, block_tables, partition_blocks: int, layout: str = "HND"):
+    """A device uint32 sink (held as int32) sized for stream_tiles over these caches."""
+    import torch
+    B, max_blocks = block_tables.shape
+    Hkv = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
+    parts = -(-max(int(max_blocks), 1) // partition_blocks)
+    return torch.empty(B * Hkv * parts * 64, dtype=torch.int32, device=k_cache.device)
+
+
+def stream_tiles(k_cache, v_cache, block_tables, context_lens, partition_blocks: int, sink, k_scales=None,
+                 v_scales=None, stream=None, layout: str = "HND"):
+    """Read every K/V tile a decode launch would read, in the same order,
+    computing nothing (the read ceiling of the access pattern)."""
+    import torch
+    if layout not in LAYOUT_CODES:
+        raise ValueError(f"layout must be one of {tuple(LAYOUT_CODES)}")
+    nb = k_cache.shape[0]
+    bs = k_cache.shape[2] if layout == "HND" else k_cache.shape[1]
+    Hkv = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
+    row_bytes = k_cache.shape[3] * k_cache.element_size()
+    B, max_blocks = block_tables.shape
+    ks = _dev(k_scales, "k_scales", torch.float32) if k_scales is not None else None
+    vs = _dev(v_scales, "v_scales", torch.float32) if v_scales is not None else None
+    _check(load().pkv_stream_tiles(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ks, vs,
+                                   _dev(block_tables, "block_tables", torch.int32), max_blocks,
+                                   _dev(context_lens, "context_lens", torch.int32), B, Hkv, row_bytes, bs,
+                                   LAYOUT_CODES[layout], nb, partition_blocks, _dev(sink, "sink", torch.int32),
+                                   sink.numel(), _stream_ptr(stream)), "pkv_stream_tiles")
 
 
 def decode_partition_blocks(num_seqs: int, num_heads: int, num_kv_heads: int, max_blocks: int,

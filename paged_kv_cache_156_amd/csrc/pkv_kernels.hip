@@ -449,28 +449,39 @@ __device__ __forceinline__ void codes_v_operand(const Fp8Regs<D>& a, const Fp8Re
 // Quantize values of one token row given the row's absolute maximum and the
 // format's largest code Q (448 for E4M3, 127 for INT8): scale = amax / Q,
 // inv = Q / amax (both fp32; amax == 0 -> 1, 1), and each code is the nearest
-// code to x * inv (ties to even, clamped to +-Q).
+// code to x * inv (ties to even, clamped to +-Q). A row holding a NaN or an
+// infinity has no finite scale: it gets scale NaN and every code set to the
+// format's marker (E4M3 0x7F, its NaN; INT8 0x80, the one code the rule
+// never writes), so every value of the row reads back as NaN. The row
+// maximum is taken with an IEEE maximum, which keeps a NaN.
 struct RowQuant {
   float scale, inv;
+  bool bad;  // the row holds a NaN or an infinity
 };
 template <int kQ>
 constexpr float kQMax = kQ == kQInt8 ? 127.0f : 448.0f;
 template <int kQ>
+constexpr unsigned kQMarker4 = kQ == kQInt8 ? 0x80808080u : 0x7f7f7f7fu;
+template <int kQ>
 __device__ __forceinline__ RowQuant row_quant(float amax) {
-  if (amax == 0.f) return {1.f, 1.f};
-  return {amax / kQMax<kQ>, kQMax<kQ> / amax};
+  if (!(amax <= 3.40282347e38f)) return {__builtin_nanf(""), 1.f, true};
+  if (amax == 0.f) return {1.f, 1.f, false};
+  return {amax / kQMax<kQ>, kQMax<kQ> / amax, false};
 }
 template <int kQ>
-__device__ __forceinline__ unsigned quant4(float x0, float x1, float x2, float x3, float inv) {
+__device__ __forceinline__ unsigned quant4(float x0, float x1, float x2, float x3, const RowQuant& q) {
+  const float inv = q.inv;
   auto c = [inv](float x) { return fminf(fmaxf(x * inv, -kQMax<kQ>), kQMax<kQ>); };
+  unsigned r;
   if constexpr (kQ == kQInt8) {
     auto b = [&](float x) { return static_cast<unsigned>(static_cast<int>(__builtin_rintf(c(x)))) & 0xffu; };
-    return b(x0) | (b(x1) << 8) | (b(x2) << 16) | (b(x3) << 24);
+    r = b(x0) | (b(x1) << 8) | (b(x2) << 16) | (b(x3) << 24);
   } else {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x0), c(x1), 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c(x2), c(x3), w, true);
-    return static_cast<unsigned>(w);
+    r = static_cast<unsigned>(w);
   }
+  return q.bad ? kQMarker4<kQ> : r;
 }
 
 template <typename T>
@@ -754,6 +765,9 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
   if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
   int n = a.context_lens[b];
+  // a length past the table's capacity is clamped for reading; the fused
+  // step then appends nothing (position n - 1 is not the new token's)
+  const bool len_fits = n <= cap;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   // prefill: this wave's 16 * kR query rows, their key limits, and the wave's span
   int q_tok0 = 0, min_limit = 0;
@@ -820,7 +834,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 
   // fused append: the partition holding position n-1 takes the new token's
   // K/V from k_new/v_new (row layout), in the same per-lane chunks the tiles use
-  const bool has_new = kStep && n > 0 && p == nparts - 1;
+  const bool has_new = kStep && n > 0 && len_fits && p == nparts - 1;
   const int new_t = has_new ? (n - 1) / kTile - blk0 : -1;  // tile index inside the partition
   const int new_row = (n - 1) % kTile;
   u32x4 kn[S::kNK];
@@ -837,9 +851,9 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
       for (int e = 0; e < D / 4; ++e) kx[e] = elt_to_float<T>(a.k_new + src + (q4 * (D / 4) + e) * S::kElt);
       float am = 0.f;
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) am = fmaxf(am, fabsf(kx[e]));
-      am = fmaxf(am, xor_shuffle(am, 16));
-      am = fmaxf(am, xor_shuffle(am, 32));
+      for (int e = 0; e < D / 4; ++e) am = fmax_nan(am, fabsf(kx[e]));
+      am = fmax_nan(am, xor_shuffle(am, 16));
+      am = fmax_nan(am, xor_shuffle(am, 32));
       const RowQuant kq = row_quant<kQ>(am);
       ks_new = kq.scale;
 #pragma unroll
@@ -848,7 +862,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 #pragma unroll
         for (int d = 0; d < 4; ++d)
           w[d] = quant4<kQ>(kx[16 * c + 4 * d], kx[16 * c + 4 * d + 1], kx[16 * c + 4 * d + 2], kx[16 * c + 4 * d + 3],
-                        kq.inv);
+                            kq);
         kn8[c] = u32x4{w[0], w[1], w[2], w[3]};
       }
       // V: this lane's D/16 values [ln*D/16, ...); the maximum spans the 16 lanes of a quarter
@@ -857,14 +871,14 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
       for (int e = 0; e < D / 16; ++e) vx[e] = elt_to_float<T>(a.v_new + src + (ln * (D / 16) + e) * S::kElt);
       float vm = 0.f;
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e) vm = fmaxf(vm, fabsf(vx[e]));
+      for (int e = 0; e < D / 16; ++e) vm = fmax_nan(vm, fabsf(vx[e]));
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) vm = fmaxf(vm, xor_shuffle(vm, m));
+      for (int m = 1; m < 16; m <<= 1) vm = fmax_nan(vm, xor_shuffle(vm, m));
       const RowQuant vq = row_quant<kQ>(vm);
       vs_new = vq.scale;
 #pragma unroll
       for (int w = 0; w < D / 64; ++w)
-        vn8[w] = quant4<kQ>(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq.inv);
+        vn8[w] = quant4<kQ>(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq);
       // write codes and scales into the slot (head group 0 only)
       const int r0 = tile_r0(new_t);
       if (hg == 0 && r0 >= 0) {
@@ -2021,6 +2035,119 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, const int3
 }
 
 // ---------------------------------------------------------------------------
+// Read ceiling of the decode access pattern (a measurement kernel): the same
+// workgroups, waves, partitions, XCD rotation, block-table lookups and
+// bounded nontemporal tile loads as a decode launch over the same cache, with
+// nothing computed but an XOR of the loaded words (stored to `sink`, one word
+// per lane and wave, so the loads stay live). Whatever rate this reaches is
+// what the memory system gives for these tiles in this order; the decode
+// kernels are measured against it.
+// ---------------------------------------------------------------------------
+struct StreamArgs {
+  const char* k;
+  const char* v;
+  const char* ks;  // per-row fp32 scales (8-bit caches), or null
+  const char* vs;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint32_t* sink;  // [B, Hkv, P, 64]
+  int32_t max_blocks;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t tiles_per_block;  // block_size / 16
+  int32_t pb_per_part;      // 16-row tiles per partition (<= 128)
+  int32_t num_parts;
+  int32_t cap_tokens;
+  int32_t row_bytes;   // one head's token row
+  int32_t nhd;         // token-major blocks: a head's rows num_kv_heads * row_bytes apart
+};
+
+template <int NC, bool kScales>  // NC: 16-byte chunks per lane per 16-row tile (row_bytes / 64)
+__global__ __launch_bounds__(64 * PKV_DECODE_WAVES) void stream_tiles_kernel(StreamArgs a) {
+  constexpr int kRowB = NC * 64;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int p = PKV_XCD_ROTATE ? static_cast<int>((blockIdx.x + blockIdx.y + gridDim.y * blockIdx.z) % gridDim.x)
+                               : static_cast<int>(blockIdx.x);
+  const int j = static_cast<int>(blockIdx.y) * static_cast<int>(blockDim.x >> 6) +
+                __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int b = blockIdx.z;
+  const int cap = a.cap_tokens;
+  int n = a.context_lens[b];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int ntiles = (n + kTile - 1) / kTile;
+  const int nparts = ntiles == 0 ? 1 : (ntiles + a.pb_per_part - 1) / a.pb_per_part;
+  if (p >= nparts) return;
+  const int blk0 = p * a.pb_per_part;
+  const int nblk = min(a.pb_per_part, ntiles - blk0);
+  const size_t trow = static_cast<size_t>(b) * a.max_blocks;
+  const int m = a.tiles_per_block;
+  const int max_tiles = a.max_blocks * m;
+  auto tile_row0 = [&](int lt) __attribute__((always_inline)) -> int {
+    const int lb = lt / m;
+    const int id = a.block_tables[trow + lb];
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) return -1;
+    const int sub = lt - lb * m;
+    return a.nhd ? (id * m + sub) * kTile * a.num_kv_heads + j : ((id * a.num_kv_heads + j) * m + sub) * kTile;
+  };
+  int my_r0 = -1, my_r02 = -1;
+  if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
+  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
+  const int rs = a.nhd ? kRowB * a.num_kv_heads : kRowB;  // bytes between a head's consecutive rows
+  const int ss = a.nhd ? 4 * a.num_kv_heads : 4;          // the same for the scales
+  constexpr int kAhead = 3, kRing = kAhead + 1;
+  u32x4 rk[kRing][NC], rv[kRing][NC], rks[kRing], rvs[kRing];
+  auto issue = [&](int u, int t) __attribute__((always_inline)) {  // u: ring slot (compile-time after unrolling)
+    const int tt = min(t, 127);
+    const int r0 = tt < 64 ? __builtin_amdgcn_readlane(my_r0, tt & 63) : __builtin_amdgcn_readlane(my_r02, tt & 63);
+    const bool ok = t < nblk && r0 >= 0;
+    const int rows = ok ? min(kTile, n - (blk0 + t) * kTile) : 0;
+    const size_t row0 = ok ? static_cast<size_t>(r0) : 0;
+    const __amdgpu_buffer_rsrc_t rk_ = tile_rsrc(a.k + row0 * kRowB, rows * rs);
+    const __amdgpu_buffer_rsrc_t rv_ = tile_rsrc(a.v + row0 * kRowB, rows * rs);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int byte = (c * 64 + lane) * 16;  // byte of the tile's packed [16, row] bytes
+      const int off = (byte / kRowB) * rs + byte % kRowB;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, kCacheNT);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b128(rv_, off, 0, kCacheNT);
+      rk[u][c] = u32x4{x[0], x[1], x[2], x[3]};
+      rv[u][c] = u32x4{y[0], y[1], y[2], y[3]};
+    }
+    if constexpr (kScales) {
+      const __amdgpu_buffer_rsrc_t rks_ = tile_rsrc(a.ks + row0 * 4, rows * ss);
+      const __amdgpu_buffer_rsrc_t rvs_ = tile_rsrc(a.vs + row0 * 4, rows * ss);
+      if (a.nhd) {  // one row's scale per lane of the first 16
+        rks[u] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rks_, (lane & 15) * ss, 0, kCacheNT), 0u, 0u, 0u};
+        rvs[u] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rvs_, (lane & 15) * ss, 0, kCacheNT), 0u, 0u, 0u};
+      } else {  // the tile's 16 scales, as the decode kernel reads them (16 bytes per quarter-wave)
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rks_, 16 * (lane >> 4), 0, kCacheNT);
+        const auto y = __builtin_amdgcn_raw_buffer_load_b128(rvs_, 16 * (lane >> 4), 0, kCacheNT);
+        rks[u] = u32x4{x[0], x[1], x[2], x[3]};
+        rvs[u] = u32x4{y[0], y[1], y[2], y[3]};
+      }
+    }
+  };
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  auto consume = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc ^= rk[u][c] ^ rv[u][c];
+    if constexpr (kScales) acc ^= rks[u] ^ rvs[u];
+  };
+#pragma unroll
+  for (int u = 0; u < kAhead; ++u) issue(u, u);
+  for (int t0 = 0; t0 < nblk; t0 += kRing) {
+#pragma unroll
+    for (int uu = 0; uu < kRing; ++uu) {
+      issue((uu + kAhead) % kRing, t0 + uu + kAhead);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
+      if (t0 + uu < nblk) consume(uu);
+    }
+  }
+  const size_t w = ((static_cast<size_t>(b) * a.num_kv_heads + j) * a.num_parts + p) * 64 + lane;
+  a.sink[w] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// ---------------------------------------------------------------------------
 // append: one thread per 16-byte chunk of a new token's head row
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k, const char* __restrict__ v,
@@ -2070,16 +2197,16 @@ __global__ __launch_bounds__(64) void append_q8_kernel(const char* __restrict__ 
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     x[e] = elt_to_float<Tin>(src + (lane * kPer + e) * sizeof(Tin));
-    am = fmaxf(am, fabsf(x[e]));
+    am = fmax_nan(am, fabsf(x[e]));
   }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, xor_shuffle(am, m));
+  for (int m = 1; m < 64; m <<= 1) am = fmax_nan(am, xor_shuffle(am, m));
   const RowQuant rq = row_quant<kQ>(am);
   const int64_t pb = slot / block_size;
   const int64_t off = slot - pb * block_size;
   const int64_t row = nhd ? (pb * block_size + off) * num_kv_heads + j : (pb * num_kv_heads + j) * block_size + off;
   char* dst = (is_v ? v_cache : k_cache) + row * D + lane * kPer;
-  const unsigned codes = quant4<kQ>(x[0], kPer > 1 ? x[kPer - 1] : 0.f, 0.f, 0.f, rq.inv);
+  const unsigned codes = quant4<kQ>(x[0], kPer > 1 ? x[kPer - 1] : 0.f, 0.f, 0.f, rq);
   if constexpr (kPer == 2) *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(codes & 0xffffu);
   else *reinterpret_cast<unsigned char*>(dst) = static_cast<unsigned char>(codes & 0xffu);
   if (lane == 0) (is_v ? v_scales : k_scales)[row] = rq.scale;
@@ -2515,6 +2642,15 @@ pkv_status append_codes(const void* k, const void* v, const int64_t* slot_mappin
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
+template <int NC>
+pkv_status launch_stream(const StreamArgs& a, int32_t num_seqs, bool scales, hipStream_t stream) {
+  const int w = decode_waves(static_cast<int64_t>(a.num_parts) * a.num_kv_heads * num_seqs, a.num_kv_heads);
+  const dim3 grid(a.num_parts, static_cast<unsigned>(a.num_kv_heads / w), num_seqs);
+  if (scales) hipLaunchKernelGGL((stream_tiles_kernel<NC, true>), grid, dim3(64 * w), 0, stream, a);
+  else hipLaunchKernelGGL((stream_tiles_kernel<NC, false>), grid, dim3(64 * w), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2760,6 +2896,52 @@ pkv_status pkv_decode_merge(const void* workspace, size_t workspace_bytes, const
   return decode_entry(nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, PKV_HND, 1, 0.f, out, dtype, workspace, workspace_bytes,
                       partition_blocks, kMerge, stream);
+}
+
+pkv_status pkv_stream_tiles(const void* k_cache, const void* v_cache, const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                            pkv_layout layout, int32_t num_blocks, int32_t partition_blocks, uint32_t* sink,
+                            size_t sink_words, void* stream) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0) return PKV_EINVAL;
+  if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
+  if (row_bytes != 64 && row_bytes != 128 && row_bytes != 256 && row_bytes != 512) return PKV_EUNSUPPORTED;
+  if (!valid_block_size(block_size)) return PKV_EUNSUPPORTED;
+  if (partition_blocks <= 0 || static_cast<int64_t>(partition_blocks) * (block_size / kTile) > kMaxPartitionBlocks)
+    return PKV_EINVAL;
+  if ((k_scales == nullptr) != (v_scales == nullptr)) return PKV_EINVAL;
+  if (static_cast<int64_t>(num_blocks) * num_kv_heads * block_size > INT32_MAX) return PKV_EUNSUPPORTED;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX) return PKV_EINVAL;
+  if (num_kv_heads > 65535 || num_seqs > 65535) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return PKV_EINVAL;
+  if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;
+  StreamArgs a{};
+  a.k = static_cast<const char*>(k_cache);
+  a.v = static_cast<const char*>(v_cache);
+  a.ks = reinterpret_cast<const char*>(k_scales);
+  a.vs = reinterpret_cast<const char*>(v_scales);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.sink = sink;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.tiles_per_block = block_size / kTile;
+  a.pb_per_part = partition_blocks * a.tiles_per_block;
+  a.num_parts = static_cast<int32_t>(ceil_div64(max_blocks_per_seq, partition_blocks));
+  a.cap_tokens = max_blocks_per_seq * block_size;
+  a.row_bytes = row_bytes;
+  a.nhd = layout == PKV_NHD;
+  if (sink_words < static_cast<size_t>(num_seqs) * num_kv_heads * a.num_parts * 64) return PKV_ESMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool sc = k_scales != nullptr;
+  switch (row_bytes) {
+    case 64: return launch_stream<1>(a, num_seqs, sc, s);
+    case 128: return launch_stream<2>(a, num_seqs, sc, s);
+    case 256: return launch_stream<4>(a, num_seqs, sc, s);
+    default: return launch_stream<8>(a, num_seqs, sc, s);
+  }
 }
 
 }  // extern "C"

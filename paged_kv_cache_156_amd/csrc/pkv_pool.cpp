@@ -228,6 +228,15 @@ pkv_status pkv_seq_grow(pkv_pool* pool, int32_t seq, int32_t new_len) {
   if (!valid_seq(pool, seq) || new_len < 0) return PKV_EINVAL;
   if (new_len < pool->seq_len[seq]) return PKV_ERANGE;
   auto& blocks = pool->seq_blocks[seq];
+  // Growing writes new positions into the partial last block; when another
+  // sequence holds it too (after a fork) or the prefix cache owns it, those
+  // writes would land in shared state, so refuse (pkv_seq_append_slots is the
+  // path that copies such a block first).
+  const int32_t len = pool->seq_len[seq];
+  if (new_len > len && len % pool->block_size != 0) {
+    const int32_t last = blocks[len / pool->block_size];
+    if (pool->refcount[last] > 1 || pool->cached[last]) return PKV_EBUSY;
+  }
   const int64_t need = ceil_div(new_len, pool->block_size) - static_cast<int64_t>(blocks.size());
   if (need > static_cast<int64_t>(available(pool))) return PKV_ENOMEM;
   for (int64_t i = 0; i < need; ++i) blocks.push_back(take_block(pool));

@@ -242,58 +242,104 @@ def test_shared_prefix_blocks(torch_dev):
 
 
 # ---------------------------------------------------------------------------
-# full-size configurations: sampled sequences against the reference
+# full-size configurations against the reference
 # ---------------------------------------------------------------------------
-def sampled_reference(torch, wkd, seqs, layer=0):
-    """Copy the sampled sequences' blocks (before the append) to the host,
-    renumber them into a small pool, and run the reference on it."""
+def pool_reference(torch, wkd, seqs, layer=0):
+    """The reference on one layer's whole pools, as the GPU sees them: host
+    copies taken before any append, every sequence's new token appended at its
+    slot through the same block tables, then attention for ``seqs``. Returns
+    (ref [B, Hq, D], NaN outside ``seqs``; K pool; V pool after the append)."""
     cfg = wkd.cfg
     dt = cfg.dtype
-    out = {}
-    for b in seqs:
-        blocks = wkd.assignment.blocks[b]
-        idx = torch.from_numpy(blocks.astype(np.int64)).to(wkd.k_cache[layer].device)
-        kc = wl.torch_to_raw(wkd.k_cache[layer].index_select(0, idx), dt)
-        vc = wl.torch_to_raw(wkd.v_cache[layer].index_select(0, idx), dt)
-        table = np.arange(len(blocks), dtype=np.int32)[None, :]
-        n = int(wkd.context_lens[b])
-        q = wl.torch_to_raw(wkd.q[layer][b:b + 1], dt)
-        kn = wl.torch_to_raw(wkd.k_new[layer][b:b + 1], dt)
-        vn = wl.torch_to_raw(wkd.v_new[layer][b:b + 1], dt)
-        slots = oracle.slot_mapping(table, [n - 1], cfg.block_size)
-        oracle.kv_append(kc, vc, kn, vn, slots, cfg.block_size)
-        out[b] = oracle.decode_attention(q, kc, vc, table, [n], cfg.scale, cfg.num_kv_heads, cfg.block_size, dt)[0]
-    return out
+    kc = wl.torch_to_raw(wkd.k_cache[layer], dt)
+    vc = wl.torch_to_raw(wkd.v_cache[layer], dt)
+    table = wkd.block_tables.cpu().numpy()
+    lens = np.asarray(wkd.context_lens, np.int32)
+    slots = oracle.slot_mapping(table, lens - 1, cfg.block_size)
+    oracle.kv_append(kc, vc, wl.torch_to_raw(wkd.k_new[layer], dt), wl.torch_to_raw(wkd.v_new[layer], dt), slots,
+                     cfg.block_size)
+    ref = oracle.decode_attention(wl.torch_to_raw(wkd.q[layer], dt), kc, vc, table, lens, cfg.scale,
+                                  cfg.num_kv_heads, cfg.block_size, dt, seqs=seqs)
+    return ref, kc, vc
 
 
-@pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "mha_contrast", "llama3_70b", "qwen25_7b_ragged"])
-def test_full_size_config_sampled(torch_dev, cfg_name):
-    torch, dev = torch_dev
-    cfg = wl.CONFIG_BY_NAME[cfg_name]
-    note(f"full-size config {cfg.name}: drawing one layer on the device")
+def partition_class_seqs(lens, pb, bs, at_least=16):
+    """One sequence of every partition count (first in batch order), then the
+    shortest remaining ones until ``at_least`` are chosen."""
+    parts = [max(1, -(-(-(-int(n) // bs)) // pb)) for n in lens]
+    pick = {}
+    for b, c in enumerate(parts):
+        pick.setdefault(c, b)
+    chosen = set(pick.values())
+    for b in np.argsort(lens, kind="stable"):
+        if len(chosen) >= at_least:
+            break
+        chosen.add(int(b))
+    return sorted(chosen), sorted(set(parts))
+
+
+def check_full_size(torch, dev, cfg, seqs, fused, what):
+    """Draw one layer on the device, run the split path (append, then
+    attention) or the fused step (twice on one workspace), and compare
+    ``seqs``' outputs with the reference and the whole pools byte for byte."""
     wkd = wl.make_device_workload(cfg, dev, layers=1)
     lens = wkd.context_lens
     B = len(lens)
-    order = np.argsort(lens)
-    seqs = sorted({int(order[0]), int(order[-1]), int(order[B // 2]), 0})
-    note(f"  reference on sampled sequences {seqs} (lengths {[int(lens[s]) for s in seqs]})")
-    ref = sampled_reference(torch, wkd, seqs)
-    slots = pkv.slot_mapping_from_tables(wkd.assignment.table(), lens - 1, cfg.block_size)
-    pkv.kv_append(wkd.k_new[0], wkd.v_new[0], torch.from_numpy(slots).to(dev), wkd.k_cache[0], wkd.v_cache[0])
+    note(f"  {what}: reference over the whole layer pool, {len(seqs)} of {B} sequences")
+    ref, kc_o, vc_o = pool_reference(torch, wkd, seqs)
+    pb = pkv.decode_partition_blocks(B, cfg.num_heads, cfg.num_kv_heads, wkd.block_tables.shape[1], cfg.block_size)
+    note(f"  {what}: launch, partition_blocks={pb}")
     out = torch.full_like(wkd.q[0], float("nan"))
-    ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables)
-    note(f"  launch: partition_blocks={pkv.decode_partition_blocks(B, cfg.num_heads, cfg.num_kv_heads, wkd.block_tables.shape[1], cfg.block_size)}")
-    pkv.paged_decode_attention(wkd.q[0], wkd.k_cache[0], wkd.v_cache[0], wkd.block_tables, wkd.context_lens_dev,
-                               cfg.scale, out, ws)
+    if fused:
+        ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables)
+        for _ in range(2):  # the append is idempotent; the second call also checks the counter reset
+            pkv.decode_step(wkd.q[0], wkd.k_new[0], wkd.v_new[0], wkd.k_cache[0], wkd.v_cache[0], wkd.block_tables,
+                            wkd.context_lens_dev, cfg.scale, out, ws)
+    else:
+        slots = pkv.slot_mapping_from_tables(wkd.assignment.table(), lens - 1, cfg.block_size)
+        pkv.kv_append(wkd.k_new[0], wkd.v_new[0], torch.from_numpy(slots).to(dev), wkd.k_cache[0], wkd.v_cache[0])
+        ws = pkv.alloc_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables)
+        pkv.paged_decode_attention(wkd.q[0], wkd.k_cache[0], wkd.v_cache[0], wkd.block_tables,
+                                   wkd.context_lens_dev, cfg.scale, out, ws)
     torch.cuda.synchronize()
     o = oracle.upcast(wl.torch_to_raw(out, cfg.dtype), cfg.dtype)
-    assert np.isfinite(o).all()
-    # a property at any size: every output is a convex combination of V rows,
-    # so it lies within [min V, max V] of its KV head (here: |o| <= max |V|)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    # a property at any size: every output is a convex combination of V rows
     vmax = float(wkd.v_cache[0].float().abs().nan_to_num(0).max())
     assert np.abs(o).max() <= vmax * (1 + 1e-2)
-    for b, r in ref.items():
-        check_close(o[b], r, cfg.dtype, f"{cfg.name} seq {b}")
+    for b in seqs:
+        check_close(o[b], ref[b], cfg.dtype, f"{what} seq {b} (n={int(lens[b])})")
+    # the whole pools after the append: the new K and V rows in their slots,
+    # every other byte (NaN poison included) unchanged
+    assert wl.torch_to_raw(wkd.k_cache[0], cfg.dtype).tobytes() == kc_o.tobytes(), f"{what}: K pool differs"
+    assert wl.torch_to_raw(wkd.v_cache[0], cfg.dtype).tobytes() == vc_o.tobytes(), f"{what}: V pool differs"
+    del wkd, out, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+@pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "mha_contrast", "llama3_70b"])
+def test_full_size_every_sequence(torch_dev, cfg_name, fused):
+    """The uniform full-size configurations: every sequence of the layer."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME[cfg_name]
+    note(f"full-size {cfg.name}, {'fused step' if fused else 'split path'}: every sequence")
+    check_full_size(torch, dev, cfg, list(range(cfg.num_seqs)), fused, f"{cfg.name} {'fused' if fused else 'split'}")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+def test_full_size_ragged_every_partition_count(torch_dev, fused):
+    """The ragged configuration: at least 16 sequences, one of every
+    partition count the launch produces."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME["qwen25_7b_ragged"]
+    lens, asg = wl.make_structure(cfg)
+    pb = pkv.decode_partition_blocks(len(lens), cfg.num_heads, cfg.num_kv_heads, asg.table().shape[1],
+                                     cfg.block_size)
+    seqs, classes = partition_class_seqs(lens, pb, cfg.block_size)
+    note(f"full-size {cfg.name}, {'fused' if fused else 'split'}: sequences {seqs}, partition counts {classes}")
+    assert len(seqs) >= 16
+    check_full_size(torch, dev, cfg, seqs, fused, f"{cfg.name} {'fused' if fused else 'split'}")
 
 
 def test_phases_equal_fused_call(torch_dev):
@@ -408,6 +454,39 @@ def test_fused_step_zero_length_and_counters_reset(torch_dev):
     assert not ws[-256:].any(), "arrival counters not reset"
 
 
+def test_fused_step_over_long_length_appends_nothing(torch_dev):
+    """A length past the table's capacity is a precondition violation: the
+    fused step clamps it for reading and must not write the new token over a
+    cached one. The other sequences append and attend as usual."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("overlong", 0, 1, 3, 16, 4, 128, 16, "bf16", context_lens=(40, 300, 77))
+    wk = wl.make_host_workload(cfg)
+    cap = wk.block_tables.shape[1] * 16
+    lens = wk.context_lens.copy()
+    lens[1] = cap + 5
+    q = wl.raw_to_torch(wk.q, "bf16", dev)
+    kc, vc = wl.raw_to_torch(wk.k_cache, "bf16", dev), wl.raw_to_torch(wk.v_cache, "bf16", dev)
+    kn, vn = wl.raw_to_torch(wk.k_new, "bf16", dev), wl.raw_to_torch(wk.v_new, "bf16", dev)
+    t = torch.from_numpy(wk.block_tables).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    note(f"fused step with one length ({lens[1]}) past the table capacity ({cap})")
+    for pb in (0, 2):
+        ws = pkv.alloc_step_workspace(q, kc, t, pb)
+        out = torch.full_like(q, float("nan"))
+        pkv.decode_step(q, kn, vn, kc, vc, t, lens_d, cfg.scale, out, ws, pb)
+        torch.cuda.synchronize()
+        # the reference appends sequences 0 and 2 only (slot -1 skips sequence 1)
+        slots = oracle.slot_mapping(wk.block_tables, [lens[0] - 1, -1, lens[2] - 1], 16)
+        kc_o, vc_o = wk.k_cache.copy(), wk.v_cache.copy()
+        oracle.kv_append(kc_o, vc_o, wk.k_new, wk.v_new, slots, 16)
+        assert wl.torch_to_raw(kc, "bf16").tobytes() == kc_o.tobytes(), "K pool changed outside the appended slots"
+        assert wl.torch_to_raw(vc, "bf16").tobytes() == vc_o.tobytes(), "V pool changed outside the appended slots"
+        ref = oracle.decode_attention(wk.q, kc_o, vc_o, wk.block_tables, lens, cfg.scale, 4, 16, "bf16", seqs=[0, 2])
+        o = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
+        for b in (0, 2):
+            check_close(o[b], ref[b], "bf16", f"over-long neighbour, seq {b}, pb={pb}")
+
+
 def test_fused_step_on_a_side_stream(torch_dev):
     """The stream argument is honoured: a fused step launched on a second
     stream (default priority), after inputs written on the current stream that
@@ -479,28 +558,82 @@ def test_fused_step_replays_under_graph_capture(torch_dev):
             assert torch.equal(caches[layer][0][blk, :, (n - 1) % 16], kn[b])
 
 
-@pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "llama3_70b", "qwen25_7b_ragged"])
-def test_fused_step_full_size_sampled(torch_dev, cfg_name):
-    torch, dev = torch_dev
-    cfg = wl.CONFIG_BY_NAME[cfg_name]
-    note(f"fused step, full-size config {cfg.name}")
-    wkd = wl.make_device_workload(cfg, dev, layers=1)
-    lens = wkd.context_lens
-    order = np.argsort(lens)
-    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(lens) // 2])})
-    ref = sampled_reference(torch, wkd, seqs)
-    out = torch.full_like(wkd.q[0], float("nan"))
-    ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_cache[0], wkd.block_tables)
-    pkv.decode_step(wkd.q[0], wkd.k_new[0], wkd.v_new[0], wkd.k_cache[0], wkd.v_cache[0], wkd.block_tables,
-                    wkd.context_lens_dev, cfg.scale, out, ws)
-    torch.cuda.synchronize()
-    o = oracle.upcast(wl.torch_to_raw(out, cfg.dtype), cfg.dtype)
-    assert np.isfinite(o).all()
-    for b, r in ref.items():
-        check_close(o[b], r, cfg.dtype, f"fused {cfg.name} seq {b}")
-    # the appended token landed in its slot, bit for bit
-    for b in seqs:
+# ---------------------------------------------------------------------------
+# the read-ceiling measurement kernel reads exactly the bytes decode reads
+# ---------------------------------------------------------------------------
+def stream_expected(kc, vc, ks, vs, table, lens, Hkv, bs, pb, nhd):
+    """Host model of pkv_stream_tiles' sink: per (sequence, KV head,
+    partition) wave and lane, the XOR of the 16-byte chunks that lane loads
+    from every valid row of the partition's tiles (rows past the length read
+    as zero), folded to one 32-bit word."""
+    R = kc.shape[-1] * kc.dtype.itemsize
+    nc = R // 64
+    m = bs // 16
+    B = len(lens)
+    P = -(-table.shape[1] // pb)
+    sink = np.zeros((B, Hkv, P, 64), np.uint32)
+    for b in range(B):
         n = int(lens[b])
-        pb = int(wkd.assignment.blocks[b][(n - 1) // 16])
-        got_k = wl.torch_to_raw(wkd.k_cache[0][pb, :, (n - 1) % 16], cfg.dtype)
-        assert got_k.tobytes() == wl.torch_to_raw(wkd.k_new[0][b], cfg.dtype).tobytes()
+        ntiles = -(-n // 16)
+        for j in range(Hkv):
+            for p in range(P):
+                acc = np.zeros((64, 4), np.uint32)
+                for lt in range(p * pb * m, min((p + 1) * pb * m, ntiles)):
+                    blk, sub = int(table[b, lt // m]), lt % m
+                    rows = min(16, n - lt * 16)
+                    for cache, sc in ((kc, ks), (vc, vs)):
+                        t = cache[blk, sub * 16:sub * 16 + 16, j] if nhd else cache[blk, j, sub * 16:sub * 16 + 16]
+                        tile = np.zeros(16 * R, np.uint8)
+                        tile[:rows * R] = np.ascontiguousarray(t[:rows]).view(np.uint8).reshape(-1)
+                        words = tile.view(np.uint32).reshape(nc, 64, 4)
+                        acc ^= np.bitwise_xor.reduce(words, axis=0)
+                        if sc is not None:
+                            srow = np.zeros(16, np.float32)
+                            srow[:rows] = (sc[blk, sub * 16:sub * 16 + rows, j] if nhd
+                                           else sc[blk, j, sub * 16:sub * 16 + rows])
+                            sw = srow.view(np.uint32)
+                            if nhd:  # one row's scale per lane of the first 16, in word 0
+                                acc[:, 0] ^= np.tile(sw, 4)
+                            else:  # quarter q of the wave loads scales 4q .. 4q+3
+                                acc ^= np.repeat(sw.reshape(4, 4), 16, axis=0)
+                if p * pb * m < max(ntiles, 1):
+                    sink[b, j, p] = acc[:, 0] ^ acc[:, 1] ^ acc[:, 2] ^ acc[:, 3]
+    return sink
+
+
+@pytest.mark.parametrize("kind", ["bf16_hnd", "bf16_nhd", "f32_hnd", "fp8_hnd", "fp8_nhd", "bf16_bs64"])
+def test_stream_tiles_reads_exactly_the_decode_bytes(torch_dev, kind):
+    torch, dev = torch_dev
+    dt = "f32" if kind.startswith("f32") else "bf16"
+    bs = 64 if kind.endswith("bs64") else 16
+    nhd = kind.endswith("nhd")
+    cfg = wl.DecodeConfig("stream", 0, 1, 5, 16, 4, 128, bs, dt, context_lens=(1, 17, 200, 513, 1000))
+    if kind.startswith("fp8"):
+        wk = wl.make_host_workload_fp8(cfg)
+        kc, vc, ks, vs = wk.k_codes, wk.v_codes, wk.k_scales, wk.v_scales
+    else:
+        wk = wl.make_host_workload(cfg)
+        kc = wk.k_cache.view(np.int16) if dt == "bf16" else wk.k_cache
+        vc = wk.v_cache.view(np.int16) if dt == "bf16" else wk.v_cache
+        ks = vs = None
+    if nhd:
+        kc, vc = wl.to_layout(kc, "NHD"), wl.to_layout(vc, "NHD")
+        ks = None if ks is None else wl.to_layout(ks, "NHD")
+        vs = None if vs is None else wl.to_layout(vs, "NHD")
+    table = np.ascontiguousarray(wk.block_tables, np.int32)
+    lay = "NHD" if nhd else "HND"
+    td = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    for pb in ((1, 3, 8) if bs == 16 else (1, 2)):
+        note(f"stream_tiles {kind} partition_blocks={pb}")
+        sink = pkv.stream_sink(td(kc), td(table), pb, layout=lay)
+        sink.fill_(-1)
+        pkv.stream_tiles(td(kc), td(vc), td(table), td(wk.context_lens), pb, sink,
+                         None if ks is None else td(ks), None if vs is None else td(vs), layout=lay)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32).reshape(len(wk.context_lens), 4, -1, 64)
+        exp = stream_expected(kc, vc, ks, vs, table, wk.context_lens, 4, bs, pb, nhd)
+        live = np.zeros(got.shape[:3], bool)  # waves past a sequence's last partition write nothing
+        for b, n in enumerate(wk.context_lens):
+            live[b, :, :max(1, -(-(-(-int(n) // 16)) // (pb * bs // 16)))] = True
+        assert np.array_equal(got[live], exp[live])
+        assert np.all(got[~live] == 0xFFFFFFFF)

@@ -113,6 +113,62 @@ def test_fp8_append_extreme_rows(torch_dev, fmt):
     assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} append, extreme rows")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_8bit_append_non_finite_rows(torch_dev, fmt, in_dtype):
+    """Rows holding a NaN or an infinity: scale NaN and every code the
+    format's marker, bit for bit with the reference, for the separate append
+    and the fused step; rows of the other heads and sequences unaffected, and
+    the fused outputs of clean sequences still match the reference."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("nonfinite", 0, 1, 4, 8, 2, 128, 16, in_dtype if in_dtype != "f32" else "bf16",
+                          context_lens=(3, 20, 33, 50))
+    wk = wl.make_host_workload_fp8(cfg)
+    if in_dtype == "f32":  # the separate append also takes fp32 rows
+        wk_new_k = oracle.upcast(wk.k_new, "bf16").astype(np.float32)
+        wk_new_v = oracle.upcast(wk.v_new, "bf16").astype(np.float32)
+    else:
+        wk_new_k, wk_new_v = wk.k_new.copy(), wk.v_new.copy()
+    nan_bits = {"bf16": np.uint16(0x7FC0), "f32": np.float32(np.nan)}[in_dtype]
+    pinf = {"bf16": np.uint16(0x7F80), "f32": np.float32(np.inf)}[in_dtype]
+    ninf = {"bf16": np.uint16(0xFF80), "f32": np.float32(-np.inf)}[in_dtype]
+    wk_new_k[0, 0, 7] = nan_bits   # sequence 0, KV head 0: K row with a NaN
+    wk_new_v[1, 1, 100] = pinf     # sequence 1, KV head 1: V row with +Inf
+    wk_new_k[2, 1, 0] = ninf       # sequence 2, KV head 1: K row with -Inf
+    note(f"{fmt} append of rows with NaN / Inf ({in_dtype} input)")
+    d = to_dev(torch, dev, wk)
+    slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
+    tdt = in_dtype
+    pkv.kv_append_fp8(wl.raw_to_torch(wk_new_k, tdt, dev), wl.raw_to_torch(wk_new_v, tdt, dev),
+                      torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"], fmt=fmt)
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = wk.k_codes.copy(), wk.v_codes.copy(), wk.k_scales.copy(), wk.v_scales.copy()
+    oracle.kv_append_fp8(kc, vc, ks, vs, wk_new_k, wk_new_v, slots, 16, in_dtype, fmt=fmt)
+    marker = 0x7F if fmt == "e4m3" else 0x80
+    blk, off = slots[0] // 16, slots[0] % 16
+    assert np.all(kc[blk, 0, off] == marker) and np.isnan(ks[blk, 0, off])  # the reading, as the reference states it
+    assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} append with non-finite rows")
+    if in_dtype != "bf16":
+        return
+    note(f"{fmt} fused step with non-finite new rows")
+    d = to_dev(torch, dev, wk)
+    d["kn"], d["vn"] = wl.raw_to_torch(wk_new_k, "bf16", dev), wl.raw_to_torch(wk_new_v, "bf16", dev)
+    for pb in (0, 1):
+        out = torch.full_like(d["q"], float("nan"))
+        ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], pb)
+        pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                            cfg.scale, out, ws, pb, fmt=fmt)
+        torch.cuda.synchronize()
+        assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} fused step with non-finite rows")
+        ref = oracle.decode_attention_fp8(wk.q, kc, vc, ks, vs, wk.block_tables, wk.context_lens, cfg.scale,
+                                          cfg.num_kv_heads, 16, "bf16", fmt=fmt)
+        o = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
+        check_close(o[3], ref[3], f"{fmt} fused step, clean sequence 3, pb={pb}")
+        check_close(o[0, 4:], ref[0, 4:], f"{fmt} fused step, sequence 0, clean KV head 1, pb={pb}")
+        # the query heads of KV head 0 read the NaN row: NaN in the reference and on the GPU
+        assert np.isnan(ref[0, :4]).all() and np.isnan(o[0, :4]).all()
+
+
 EDGE_LENS = (1, 2, 15, 16, 17, 33, 128, 129, 257, 600, 1100, 2049)
 SHAPES = [(4, 2, 64), (32, 8, 128), (8, 8, 64), (64, 8, 128), (28, 4, 128), (64, 2, 128)]
 

@@ -276,3 +276,25 @@ def test_step_8bit_prefill_and_copy_reject_bad_arguments_without_gpu():
     assert lib.pkv_copy_blocks(ptrs, sizes, 2, 8, None, 1, None) == pkv.PKV_EINVAL  # pairs missing
     assert lib.pkv_copy_blocks((ctypes.c_void_p * 1)(0x1004), sizes, 1, 8, fake, 1, None) == pkv.PKV_EINVAL
     assert lib.pkv_copy_blocks(ptrs, (ctypes.c_int64 * 1)(100), 1, 8, fake, 1, None) == pkv.PKV_EINVAL
+
+
+def test_stream_tiles_rejects_bad_arguments_without_gpu():
+    """The read-ceiling measurement call checks its arguments before any HIP call."""
+    lib = pkv.load()
+    fake = ctypes.c_void_p(0x1000)
+
+    def st(**kw):
+        a = dict(k=fake, v=fake, ks=None, vs=None, t=fake, mb=4, lens=fake, B=2, Hkv=2, rb=256, bs=16, lay=0, NB=8,
+                 pb=2, sink=fake, words=2 * 2 * 2 * 64)
+        a.update(kw)
+        return lib.pkv_stream_tiles(a["k"], a["v"], a["ks"], a["vs"], a["t"], a["mb"], a["lens"], a["B"], a["Hkv"],
+                                    a["rb"], a["bs"], a["lay"], a["NB"], a["pb"], a["sink"], a["words"], None)
+
+    assert st(B=0) == pkv.PKV_OK
+    assert st(k=None) == pkv.PKV_EINVAL
+    assert st(sink=None) == pkv.PKV_EINVAL
+    assert st(ks=fake) == pkv.PKV_EINVAL  # one scale tensor without the other
+    assert st(pb=0) == pkv.PKV_EINVAL and st(pb=129) == pkv.PKV_EINVAL
+    assert st(rb=96) == pkv.PKV_EUNSUPPORTED and st(bs=24) == pkv.PKV_EUNSUPPORTED
+    assert st(lay=2) == pkv.PKV_EINVAL
+    assert st(words=2 * 2 * 2 * 64 - 1) == pkv.PKV_ESMALL  # B x Hkv x partitions x 64 words

@@ -41,6 +41,30 @@ def test_fork_then_append_copies_the_shared_partial_block():
     assert pairs.shape == (0, 2) and slots.tolist() == [fresh * 16 + 3, blocks0[1] * 16 + 3]
 
 
+def test_grow_into_a_shared_partial_block_is_refused():
+    # after a fork both sequences hold the partial last block; growing one of
+    # them would put its new positions into the other's block
+    pool = new_pool(16)
+    pool.grow(0, 18)
+    pool.fork(1, 0)
+    before = pool.seq_info(0)
+    with pytest.raises(pkv.PkvError) as e:
+        pool.grow(0, 20)
+    assert e.value.status == pkv.PKV_EBUSY
+    after = pool.seq_info(0)
+    assert after[0] == before[0] and np.array_equal(after[1], before[1])
+    # the copy-on-write path still serves it, and growing the private copy works
+    slots, pairs = pool.append_slots([0])
+    assert pairs.shape == (1, 2)
+    pool.grow(0, 40)
+    assert pool.seq_info(0)[0] == 40
+    # a grow that starts at a block boundary takes fresh blocks: allowed while shared
+    pool.grow(2, 32)
+    pool.fork(3, 2)
+    pool.grow(2, 33)
+    assert pool.seq_info(2)[0] == 33 and pool.stats()["shared_blocks"] >= 2
+
+
 def test_fork_at_block_boundary_needs_no_copy():
     pool = new_pool(16)
     pool.grow(0, 32)

@@ -63,6 +63,36 @@ def test_row_quantization_bound_and_amax():
     assert np.all(s0 == 1) and not c0.any()
 
 
+def test_e4m3_hand_worked_row():
+    # amax 7 -> scale 7/448 = 2^-6 and inv 64, both exact in float32; each
+    # code below is worked out by hand from x * 64:
+    #   7 -> 448 = 0x7E; -3.5 -> -224 = 2^7 * 1.75 = 0xF6; 0.25 -> 16 = 0x58;
+    #   1 -> 64 = 0x68; 0.09765625 -> 6.25, a tie between 6.0 (m = 4) and 6.5
+    #   (m = 5): the even code 0x4C; 0.1f -> 6.4000001 -> 6.5 = 0x4D;
+    #   2^-14 -> 2^-8 = subnormal 2 * 2^-9 = 0x02; -2^-17 -> -2^-11, below half
+    #   the smallest subnormal: -0 = 0x80; 0 -> 0x00
+    x = np.array([[7.0, -3.5, 0.25, 1.0, 0.09765625, 0.1, 2.0 ** -14, -2.0 ** -17, 0.0]], np.float32)
+    codes, scale = q.quantize_rows(x)
+    assert scale.dtype == np.float32 and scale[0] == np.float32(2.0 ** -6)
+    assert codes[0].tolist() == [0x7E, 0xF6, 0x58, 0x68, 0x4C, 0x4D, 0x02, 0x80, 0x00]
+    # a different constant (447 instead of 448) moves the scale off 2^-6
+    assert np.float32(7.0) / np.float32(447.0) != scale[0]
+
+
+def test_non_finite_rows_read_back_as_nan():
+    # reading for rows holding a NaN or an infinity: scale NaN, every code the
+    # format's marker (E4M3 0x7F = NaN; INT8 -128), other rows untouched
+    x = np.array([[1.0, np.nan, 2.0, 0.5], [1.0, -np.inf, 0.0, 0.5], [7.0, -3.5, 0.25, 1.0]], np.float32)
+    codes, scale = q.quantize_rows(x)
+    assert np.all(codes[:2] == 0x7F) and np.all(np.isnan(scale[:2]))
+    assert scale[2] == np.float32(2.0 ** -6) and codes[2].tolist() == [0x7E, 0xF6, 0x58, 0x68]
+    assert np.all(np.isnan(q.dequantize_rows(codes[:2], scale[:2])))
+    c8, s8 = q.quantize_rows_int8(x)
+    assert np.all(c8[:2] == -128) and np.all(np.isnan(s8[:2]))
+    assert c8[2].tolist() == [127, -64, 5, 18] and s8[2] == np.float32(7.0) / np.float32(127.0)
+    assert np.all(np.isnan(q.int8_decode(c8[:2]) * s8[:2, None]))
+
+
 def test_planted_encoder_mistakes_are_caught():
     x = np.array([q.e4m3_value(0x38) + 0.0625], np.float32)  # exact tie between 1.0 and 1.125
     assert int(q.e4m3_encode(x)[0]) == 0x38  # ties go to the even code (1.0)
