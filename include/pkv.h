@@ -238,6 +238,31 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
                            void* stream);
 
 /*
+ * pkv_decode_step_noalloc -- pkv_decode_step without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. The partition
+ * results and arrival counters live in a library-owned device array of
+ * 64 MiB per GPU (held until the process ends; its first 64 KiB are the
+ * counters). The call allocates and frees nothing.
+ *   - Limits: at most 16384 work units (num_seqs * num_kv_heads *
+ *     ceil((num_heads / num_kv_heads) / 16)) and
+ *     pkv_decode_step_workspace_bytes(...) <= 64 MiB - 64 KiB for this shape
+ *     and partition_blocks; larger shapes return PKV_ESMALL before any GPU
+ *     work (pick longer partitions, or use pkv_decode_step).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (two streams, two threads) race and give wrong results. Each
+ *     completed call leaves the counters at zero for the next; the first call
+ *     on a device also enqueues a small fill kernel that clears them.
+ * Every other argument, the result and the errors as pkv_decode_step.
+ */
+pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                                   int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                   int32_t partition_blocks, void* stream);
+
+/*
  * FP8 KV cache. The pages name low-precision KV storage (INT8/FP8) with
  * higher-precision arithmetic ("KV Cache and Inference Optimization", section
  * "KV quantization") without fixing a format; these calls use:

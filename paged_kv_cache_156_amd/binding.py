@@ -57,6 +57,8 @@ SIGNATURES = [
     ("pkv_decode_step_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     ("pkv_decode_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
+    ("pkv_decode_step_noalloc", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _f32, _vp, _i32, _i32, _vp]),
     ("pkv_kv_append_fp8", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     ("pkv_paged_decode_attention_fp8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                               _i32, _i32, _f32, _vp, _i32, _vp, _sz, _i32, _vp]),
@@ -481,6 +483,22 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
                                 float(scale), a["out"], a["code"], a["ws"], a["wsb"], int(partition_blocks),
                                 _stream_ptr(stream))
     _check(st, "pkv_decode_step")
+    return out
+
+
+def decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                        partition_blocks: int = 0, stream=None, layout: str = "HND"):
+    """``decode_step`` whose partition results live in the library's own
+    device array (no workspace, nothing allocated; see pkv_decode_step_noalloc)."""
+    a = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, None, layout)
+    B, Hkv, D = a["B"], a["Hkv"], a["D"]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new / v_new must be [B, Hkv, D]")
+    st = load().pkv_decode_step_noalloc(a["q"], _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
+                                        a["k"], a["v"], a["t"], a["mb"], a["lens"], B, a["Hq"], Hkv, D, a["bs"],
+                                        a["lay"], a["NB"], float(scale), a["out"], a["code"], int(partition_blocks),
+                                        _stream_ptr(stream))
+    _check(st, "pkv_decode_step_noalloc")
     return out
 
 

@@ -46,6 +46,8 @@
 #include <pkv.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 using f32x4 = float __attribute__((ext_vector_type(4)));
@@ -2423,6 +2425,50 @@ PrefillSplit prefill_split(const PrefillPlan& plan, int32_t num_seqs, int32_t nu
   return r;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch of pkv_decode_step_noalloc (for callers that cannot
+// allocate): one fixed array per device, held until the process ends. Its
+// first kScratchCounterBytes hold the fused step's arrival counters, the rest
+// its partition results. Host code never uses the array's name as an
+// address (on the host it only names the symbol): the device address comes
+// from hipGetSymbolAddress, once per device, and is kept per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;         // 64 MiB in all
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;  // 16384 arrival counters
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// Device address of this device's scratch, set up on its first use: the
+// symbol's address with this device current, and its counter region cleared
+// by a fill kernel on `stream` (a kernel rather than a memset node, so a
+// first call made under graph capture stays correct on every replay).
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[64] = {};
+pkv_status scratch_on_device(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PKV_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return PKV_EHIP;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                       static_cast<int64_t>(kScratchCounterBytes / 4));
+    if (hipGetLastError() != hipSuccess) return PKV_EHIP;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 // Validate, fill DecodeArgs and launch the requested phases. Pointers the
 // chosen phases never read may be null (the merge needs no q or caches).
 pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -2432,7 +2478,7 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
                         size_t workspace_bytes, int32_t partition_blocks, unsigned phases, void* stream,
                         const void* k_new = nullptr,
                         const void* v_new = nullptr, const float* k_scales = nullptr,
-                        const float* v_scales = nullptr, int codes = 0) {
+                        const float* v_scales = nullptr, int codes = 0, bool static_scratch = false) {
   const bool fp8 = codes != 0;  // 8-bit codes (E4M3 or INT8) with per-row scales
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
   if ((phases & kPartitions) && num_blocks <= 0) return PKV_EINVAL;
@@ -2484,7 +2530,20 @@ pkv_status decode_entry(const void* q, const void* k_cache, const void* v_cache,
   a.v_cache_w = const_cast<char*>(static_cast<const char*>(v_cache));
   if (a.num_parts > 1) {
     char* ws = const_cast<char*>(static_cast<const char*>(workspace));
-    if (phases & kFusedStep) {
+    if ((phases & kFusedStep) && static_scratch) {
+      // the library's own device array: counters at its start (a fixed place,
+      // so every completed call leaves them zero for the next, whatever its
+      // shape), then partials and lse values
+      const StepLayout L = step_layout(num_seqs, num_heads, num_kv_heads, head_dim, a.num_parts);
+      if (L.ctr_bytes > kScratchCounterBytes || L.o_bytes + L.lse_bytes > kScratchBytes - kScratchCounterBytes)
+        return PKV_ESMALL;
+      char* sp = nullptr;
+      const pkv_status st = scratch_on_device(static_cast<hipStream_t>(stream), &sp);
+      if (st != PKV_OK) return st;
+      a.counters = reinterpret_cast<int32_t*>(sp);
+      a.ws_o = reinterpret_cast<float*>(sp + kScratchCounterBytes);
+      a.ws_lse = reinterpret_cast<float*>(sp + kScratchCounterBytes + L.o_bytes);
+    } else if (phases & kFusedStep) {
       const StepLayout L = step_layout(num_seqs, num_heads, num_kv_heads, head_dim, a.num_parts);
       if (!workspace || workspace_bytes < L.total()) return PKV_ESMALL;
       a.ws_o = reinterpret_cast<float*>(ws);
@@ -2750,6 +2809,17 @@ pkv_status pkv_decode_step(const void* q, const void* k_new, const void* v_new, 
   return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, workspace,
                       workspace_bytes, partition_blocks, kFusedStep, stream, k_new, v_new);
+}
+
+pkv_status pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_layout layout,
+                                   int32_t num_blocks, float scale, void* out, pkv_dtype dtype,
+                                   int32_t partition_blocks, void* stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, layout, num_blocks, scale, out, dtype, nullptr, 0,
+                      partition_blocks, kFusedStep, stream, k_new, v_new, nullptr, nullptr, 0, true);
 }
 
 pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int32_t n_caches, int32_t num_blocks,

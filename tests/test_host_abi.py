@@ -298,3 +298,28 @@ def test_stream_tiles_rejects_bad_arguments_without_gpu():
     assert st(rb=96) == pkv.PKV_EUNSUPPORTED and st(bs=24) == pkv.PKV_EUNSUPPORTED
     assert st(lay=2) == pkv.PKV_EINVAL
     assert st(words=2 * 2 * 2 * 64 - 1) == pkv.PKV_ESMALL  # B x Hkv x partitions x 64 words
+
+
+def test_noalloc_step_checks_its_limits_without_gpu():
+    """pkv_decode_step_noalloc validates its arguments and the size of its
+    own device array before any HIP call."""
+    lib = pkv.load()
+    fake = ctypes.c_void_p(0x1000)
+
+    def na(**kw):
+        a = dict(q=fake, kn=fake, vn=fake, k=fake, v=fake, t=fake, mb=4, lens=fake, B=2, Hq=4, Hkv=2, D=64, bs=16,
+                 lay=0, NB=8, scale=0.125, out=fake, dt=2, pb=0)
+        a.update(kw)
+        return lib.pkv_decode_step_noalloc(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["t"], a["mb"], a["lens"],
+                                           a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["lay"], a["NB"], a["scale"],
+                                           a["out"], a["dt"], a["pb"], None)
+
+    assert na(B=0) == pkv.PKV_OK
+    assert na(kn=None) == pkv.PKV_EINVAL
+    assert na(Hq=6, Hkv=4) == pkv.PKV_EINVAL
+    assert na(D=96) == pkv.PKV_EUNSUPPORTED
+    # partials beyond 64 MiB - 64 KiB: 64 units x 2048 partitions x 8 KiB
+    assert pkv.decode_step_workspace_bytes(8, 64, 8, 128, 2048, 1) > (64 << 20)
+    assert na(B=8, Hq=64, Hkv=8, D=128, mb=2048, NB=16, pb=1) == pkv.PKV_ESMALL
+    # more than 16384 arrival counters (4096 sequences x 8 KV heads, two partitions each)
+    assert na(B=4096, Hq=8, Hkv=8, D=64, mb=2, NB=16, pb=1) == pkv.PKV_ESMALL
