@@ -750,23 +750,38 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   const int row_step = kNHD ? a.num_kv_heads : 1;  // cache rows between consecutive tokens of one head
   // First cache row of each of this partition's tiles (lane i: tile blk0 + i,
   // and blk0 + 64 + i for partitions longer than 64 tiles), -1 where the
-  // table names a block outside the pool. The table is read together with
-  // the sequence length, bounded by the table width rather than by the
-  // length, so the first K/V loads wait for one round trip, not two.
+  // table names a block outside the pool. The sequence length (a scalar
+  // load) and the table entries are requested together, bounded by the table
+  // width rather than by the length, and nothing is computed on an entry
+  // inside a lane-dependent branch, so the first K/V loads wait for one round
+  // trip, not two.
+  // (a vector-memory load, so that it is issued beside the table loads and
+  // shares their wait; as a scalar load it was placed after that wait)
+  int n = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
+      tile_rsrc(reinterpret_cast<const char*>(a.context_lens), (b + 1) * 4), b * 4, 0, 0));
   const size_t trow = static_cast<size_t>(b) * a.max_blocks;
   const int m = a.tiles_per_block;
   const int max_tiles = a.max_blocks * m;
-  auto tile_row0 = [&](int lt) -> int {
-    const int lb = lt / m;
-    const int id = a.block_tables[trow + lb];
+  auto table_id = [&](int lt) -> int {  // every lane loads (an in-range entry); out-of-range tiles get -1
+    const int lbc = min(lt, max_tiles - 1) / m;
+    const int id = a.block_tables[trow + lbc];
+    return lt < max_tiles ? id : -1;
+  };
+  auto row_of = [&](int id, int lt) -> int {
     if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) return -1;
-    const int sub = lt - lb * m;
+    const int sub = lt - (lt / m) * m;
     return kNHD ? (id * m + sub) * kTile * a.num_kv_heads + j : ((id * a.num_kv_heads + j) * m + sub) * kTile;
   };
-  int my_r0 = -1, my_r02 = -1;
-  if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
-  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
-  int n = a.context_lens[b];
+  const int raw0 = table_id(blk0 + lane);  // an unconditional load: its wait falls at the first use
+  const int id0 = lane < a.pb_per_part ? raw0 : -1;
+  int id1 = -1;
+  if (a.pb_per_part > 64) {  // wave-uniform
+    const int raw1 = table_id(blk0 + 64 + lane);
+    id1 = 64 + lane < a.pb_per_part ? raw1 : -1;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the length and table loads are issued before any wait on them
+  n = __builtin_amdgcn_readfirstlane(n);
+  const int my_r0 = row_of(id0, blk0 + lane), my_r02 = row_of(id1, blk0 + 64 + lane);
   // a length past the table's capacity is clamped for reading; the fused
   // step then appends nothing (position n - 1 is not the new token's)
   const bool len_fits = n <= cap;
@@ -2074,26 +2089,36 @@ __global__ __launch_bounds__(64 * PKV_DECODE_WAVES) void stream_tiles_kernel(Str
                 __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int b = blockIdx.z;
   const int cap = a.cap_tokens;
+  // the same start as the decode kernels: length and table entries requested together
   int n = a.context_lens[b];
+  const int blk0 = p * a.pb_per_part;
+  const size_t trow = static_cast<size_t>(b) * a.max_blocks;
+  const int m = a.tiles_per_block;
+  const int max_tiles = a.max_blocks * m;
+  auto table_id = [&](int lt) __attribute__((always_inline)) -> int {
+    const int lbc = min(lt, max_tiles - 1) / m;
+    const int id = a.block_tables[trow + lbc];
+    return lt < max_tiles ? id : -1;
+  };
+  auto row_of = [&](int id, int lt) __attribute__((always_inline)) -> int {
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) return -1;
+    const int sub = lt - (lt / m) * m;
+    return a.nhd ? (id * m + sub) * kTile * a.num_kv_heads + j : ((id * a.num_kv_heads + j) * m + sub) * kTile;
+  };
+  const int raw0 = table_id(blk0 + lane);
+  const int id0 = lane < a.pb_per_part ? raw0 : -1;
+  int id1 = -1;
+  if (a.pb_per_part > 64) {  // wave-uniform
+    const int raw1 = table_id(blk0 + 64 + lane);
+    id1 = 64 + lane < a.pb_per_part ? raw1 : -1;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the length and table loads are issued before any wait on them
   n = n < 0 ? 0 : (n > cap ? cap : n);
   const int ntiles = (n + kTile - 1) / kTile;
   const int nparts = ntiles == 0 ? 1 : (ntiles + a.pb_per_part - 1) / a.pb_per_part;
   if (p >= nparts) return;
-  const int blk0 = p * a.pb_per_part;
   const int nblk = min(a.pb_per_part, ntiles - blk0);
-  const size_t trow = static_cast<size_t>(b) * a.max_blocks;
-  const int m = a.tiles_per_block;
-  const int max_tiles = a.max_blocks * m;
-  auto tile_row0 = [&](int lt) __attribute__((always_inline)) -> int {
-    const int lb = lt / m;
-    const int id = a.block_tables[trow + lb];
-    if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) return -1;
-    const int sub = lt - lb * m;
-    return a.nhd ? (id * m + sub) * kTile * a.num_kv_heads + j : ((id * a.num_kv_heads + j) * m + sub) * kTile;
-  };
-  int my_r0 = -1, my_r02 = -1;
-  if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
-  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
+  const int my_r0 = row_of(id0, blk0 + lane), my_r02 = row_of(id1, blk0 + 64 + lane);
   const int rs = a.nhd ? kRowB * a.num_kv_heads : kRowB;  // bytes between a head's consecutive rows
   const int ss = a.nhd ? 4 * a.num_kv_heads : 4;          // the same for the scales
   constexpr int kAhead = 3, kRing = kAhead + 1;
