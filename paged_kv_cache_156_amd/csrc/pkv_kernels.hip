@@ -308,9 +308,12 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const char* kt, c
 // FP8 (OCP E4M3) caches: one code byte per element plus one fp32 scale per
 // token row of one KV head; the value attended over is code * scale.
 // ---------------------------------------------------------------------------
-// Raw registers of one FP8 block. K: lane (q4, r) holds token r's bytes
-// [q4*D/4, q4*D/4 + D/4) (MFMA chunk c = bytes 8c..8c+7 of that slice, the
-// queries use the same d order). V: rows 4*q4 + i, bytes [r*D/16, r*D/16 + D/16).
+// Raw registers of one FP8 block. K: lane (q4, r) holds token r's 16-byte
+// chunks q4 + 4c (c < D/64), so each load instruction reads 64 contiguous
+// bytes of every row (scattered 16-byte pieces per instruction cost a
+// measured 5% of the stream rate); MFMA chunk c is bytes 8c..8c+7 of the
+// lane's chunks taken in order, and the queries use the same d order
+// (k_slice_elt). V: rows 4*q4 + i, bytes [r*D/16, r*D/16 + D/16).
 // ks / vs: the scales of rows 4*q4 + i.
 template <int D>
 struct Fp8Regs {
@@ -318,6 +321,11 @@ struct Fp8Regs {
   unsigned v[4][D / 64];
   f32x4 ks, vs;
 };
+// element index (d) of the e-th K code a lane (q4, r) holds: chunk q4 + 4 (e / 16), byte e % 16
+template <int D>
+__device__ __forceinline__ int k_slice_elt(int q4, int e) {
+  return (q4 + 4 * (e >> 4)) * 16 + (e & 15);
+}
 
 // rs: code row stride in bytes (D for HND, num_kv_heads * D for NHD); the
 // scales of consecutive rows are adjacent for HND and num_kv_heads apart for NHD.
@@ -331,7 +339,7 @@ __device__ __forceinline__ void load_block_fp8(Fp8Regs<D>& r, const char* kt, co
   const __amdgpu_buffer_rsrc_t rvs = tile_rsrc(vst, rows * ss);
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * rs + q4 * (D / 4) + 16 * c, 0, kCacheNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * rs + (q4 + 4 * c) * 16, 0, kCacheNT);
     r.k[c] = u32x4{v[0], v[1], v[2], v[3]};
   }
 #pragma unroll
@@ -825,47 +833,72 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
     return t < 64 ? __builtin_amdgcn_readlane(my_r0, t & 63) : __builtin_amdgcn_readlane(my_r02, t & 63);
   };
 
-  // this lane's query row (column of the score tile): a head of the GQA group
-  // (decode) or a (token, head) pair of the chunk (prefill); qidx indexes the
-  // [*, Hq] rows of q and out
-  bool head_ok[kR];
-  size_t qidx[kR];
-  u32x4 qv[kR][S::kNK];  // Q as the B operand, same chunk permutation as K
-#pragma unroll
-  for (int rg = 0; rg < kR; ++rg) {
-    const int hin = kPrefill ? row_hin[rg] : hg * 16 + ln;  // head index inside the GQA group
-    head_ok[rg] = kPrefill ? row_ok[rg] : hin < a.group;
-    const int hq = j * a.group + (head_ok[rg] ? hin : 0);
-    qidx[rg] = kPrefill ? (static_cast<size_t>(q_tok0) + (head_ok[rg] ? row_tok[rg] : 0)) * a.num_heads + hq
-                        : static_cast<size_t>(b) * a.num_heads + hq;
-    const char* qrow = a.q + qidx[rg] * S::kRowBytes;
-#pragma unroll
-    for (int c = 0; c < S::kNK; ++c) {
-      // byte offset of 16-byte chunk c: same-type caches (4c + q4) * 16 (the K
-      // tile's chunk order); FP8 caches (T is 16-bit) elements q4 * D/4 + 8c
-      const int off = kFp8 ? (q4 * (D / 4) + 8 * c) * 2 : (4 * c + q4) * 16;
-      static_assert(kFp8 ? (D / 4) * 2 <= S::kRowBytes : true, "query slice must lie inside the row");
-      qv[rg][c] = head_ok[rg] ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0, 0, 0, 0};
-    }
-  }
-
-  // fused append: the partition holding position n-1 takes the new token's
-  // K/V from k_new/v_new (row layout), in the same per-lane chunks the tiles use
+  // Fused append: the partition holding position n-1 takes the new token's
+  // K/V from k_new/v_new and uses them from registers. They are read here,
+  // right after the table (so no earlier wait covers them); 8-bit rows are
+  // quantized only when the tile that holds position n-1 comes up (the
+  // partition's last), and the row is written to its slot after the loop,
+  // where the store's completion overlaps the merge's own wait.
   const bool has_new = kStep && n > 0 && len_fits && p == nparts - 1;
   const int new_t = has_new ? (n - 1) / kTile - blk0 : -1;  // tile index inside the partition
   const int new_row = (n - 1) % kTile;
-  u32x4 kn[S::kNK];
+  u32x4 kn[S::kNK];   // 16-bit caches: the new K in the tile's chunk order
   unsigned vn[S::kVDW];
-  u32x4 kn8[D / 64];  // FP8: quantized new K slice (this lane's q4 slice)
+  constexpr int kNewK = kFp8 ? D / 32 : 1;  // 8-bit caches: this lane's D/4 16-bit K values (its K chunks)
+  u32x4 knr[kNewK];
+  unsigned vnr[kFp8 ? D / 32 : 1];          // and its D/16 V values
+  u32x4 kn8[D / 64];  // 8-bit: the quantized K chunks and V codes of the new row
   unsigned vn8[D / 64];
   float ks_new = 1.f, vs_new = 1.f;
-  if constexpr (kStep && kFp8) {
+  if constexpr (kStep) {
     if (has_new) {  // wave-uniform
       const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + j) * S::kRowBytes;
-      // K: this lane's D/4 values [q4*D/4, ...); the row maximum spans the 4 quarters
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int c = 0; c < kNewK; ++c)
+          knr[c] = *reinterpret_cast<const u32x4*>(a.k_new + src + k_slice_elt<D>(q4, 8 * c) * S::kElt);
+        const char* vsrc = a.v_new + src + ln * (D / 16) * S::kElt;
+        if constexpr (D / 32 == 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(vsrc);
+          vnr[0] = x[0];
+          vnr[1] = x[1];
+          vnr[2] = x[2];
+          vnr[3] = x[3];
+        } else {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(vsrc);
+          vnr[0] = x[0];
+          vnr[1] = x[1];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < S::kNK; ++c) kn[c] = *reinterpret_cast<const u32x4*>(a.k_new + src + (4 * c + q4) * 16);
+        const char* vsrc = a.v_new + src + ln * S::kE * S::kElt;
+        if constexpr (S::kVDW == 2) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
+          vn[0] = w[0];
+          vn[1] = w[1];
+        } else {
+#pragma unroll
+          for (int w = 0; w < S::kVDW; w += 4) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(vsrc + w * 4);
+            vn[w] = x[0];
+            vn[w + 1] = x[1];
+            vn[w + 2] = x[2];
+            vn[w + 3] = x[3];
+          }
+        }
+      }
+    }
+  }
+  // 8-bit caches: quantize the new K and V rows (scale = row amax / Q)
+  auto quantize_new = [&]() __attribute__((always_inline)) {
+    if constexpr (kStep && kFp8) {
+      // K: this lane's D/4 values (its K chunks); the row maximum spans the 4 quarters
       float kx[D / 4];
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) kx[e] = elt_to_float<T>(a.k_new + src + (q4 * (D / 4) + e) * S::kElt);
+      for (int c = 0; c < kNewK; ++c)
+#pragma unroll
+        for (int h = 0; h < 8; ++h) kx[8 * c + h] = from_bits16<T>((knr[c][h >> 1] >> (16 * (h & 1))) & 0xffffu);
       float am = 0.f;
 #pragma unroll
       for (int e = 0; e < D / 4; ++e) am = fmax_nan(am, fabsf(kx[e]));
@@ -885,7 +918,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
       // V: this lane's D/16 values [ln*D/16, ...); the maximum spans the 16 lanes of a quarter
       float vx[D / 16];
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e) vx[e] = elt_to_float<T>(a.v_new + src + (ln * (D / 16) + e) * S::kElt);
+      for (int e = 0; e < D / 16; ++e) vx[e] = from_bits16<T>((vnr[e >> 1] >> (16 * (e & 1))) & 0xffffu);
       float vm = 0.f;
 #pragma unroll
       for (int e = 0; e < D / 16; ++e) vm = fmax_nan(vm, fabsf(vx[e]));
@@ -896,57 +929,30 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 #pragma unroll
       for (int w = 0; w < D / 64; ++w)
         vn8[w] = quant4<kQ>(vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3], vq);
-      // write codes and scales into the slot (head group 0 only)
-      const int r0 = tile_r0(new_t);
-      if (hg == 0 && r0 >= 0) {
-        const size_t row = static_cast<size_t>(r0) + static_cast<size_t>(new_row) * row_step;
-        if (ln == 0) {
-#pragma unroll
-          for (int c = 0; c < D / 64; ++c)
-            *reinterpret_cast<u32x4*>(a.k_cache_w + row * D + q4 * (D / 4) + 16 * c) = kn8[c];
-        }
-        if (q4 == 0) {
-          char* vd = a.v_cache_w + row * D + ln * (D / 16);
-          if constexpr (D / 64 == 2) *reinterpret_cast<u32x2*>(vd) = u32x2{vn8[0], vn8[1]};
-          else *reinterpret_cast<unsigned*>(vd) = vn8[0];
-        }
-        if (lane == 0) {
-          reinterpret_cast<float*>(const_cast<char*>(a.k_scales))[row] = ks_new;
-          reinterpret_cast<float*>(const_cast<char*>(a.v_scales))[row] = vs_new;
-        }
-      }
     }
-  }
-  if constexpr (kStep && !kFp8) {
-    if (has_new) {
-      const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + j) * S::kRowBytes;
+  };
+
+  // this lane's query row (column of the score tile): a head of the GQA group
+  // (decode) or a (token, head) pair of the chunk (prefill); qidx indexes the
+  // [*, Hq] rows of q and out
+  bool head_ok[kR];
+  size_t qidx[kR];
+  u32x4 qv[kR][S::kNK];  // Q as the B operand, same chunk permutation as K
 #pragma unroll
-      for (int c = 0; c < S::kNK; ++c) kn[c] = *reinterpret_cast<const u32x4*>(a.k_new + src + (4 * c + q4) * 16);
-      const char* vsrc = a.v_new + src + ln * S::kE * S::kElt;
-      if constexpr (S::kVDW == 2) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
-        vn[0] = w[0];
-        vn[1] = w[1];
-      } else {
+  for (int rg = 0; rg < kR; ++rg) {
+    const int hin = kPrefill ? row_hin[rg] : hg * 16 + ln;  // head index inside the GQA group
+    head_ok[rg] = kPrefill ? row_ok[rg] : hin < a.group;
+    const int hq = j * a.group + (head_ok[rg] ? hin : 0);
+    qidx[rg] = kPrefill ? (static_cast<size_t>(q_tok0) + (head_ok[rg] ? row_tok[rg] : 0)) * a.num_heads + hq
+                        : static_cast<size_t>(b) * a.num_heads + hq;
+    const char* qrow = a.q + qidx[rg] * S::kRowBytes;
 #pragma unroll
-        for (int w = 0; w < S::kVDW; w += 4) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(vsrc + w * 4);
-          vn[w] = x[0];
-          vn[w + 1] = x[1];
-          vn[w + 2] = x[2];
-          vn[w + 3] = x[3];
-        }
-      }
-      // write it into its slot (one head group writes; the others only read)
-      const int r0 = tile_r0(new_t);
-      if (hg == 0 && r0 >= 0) {
-        const size_t dst = (static_cast<size_t>(r0) + static_cast<size_t>(new_row) * row_step) * S::kRowBytes;
-        if (ln == 0) {
-#pragma unroll
-          for (int c = 0; c < S::kNK; ++c) *reinterpret_cast<u32x4*>(a.k_cache_w + dst + (4 * c + q4) * 16) = kn[c];
-        }
-        if (q4 == 0) store_dwords<S::kVDW>(a.v_cache_w + dst + ln * S::kE * S::kElt, vn);
-      }
+    for (int c = 0; c < S::kNK; ++c) {
+      // byte offset of 16-byte chunk c: same-type caches (4c + q4) * 16 (the K
+      // tile's chunk order); 8-bit caches (T is 16-bit) the 8 elements of MFMA
+      // chunk c of the lane's K codes
+      const int off = kFp8 ? k_slice_elt<D>(q4, 8 * c) * 2 : (4 * c + q4) * 16;
+      qv[rg][c] = head_ok[rg] ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -988,6 +994,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
       if (t == new_t) {  // wave-uniform
         valid = new_row + 1;
         if constexpr (kFp8) {
+          quantize_new();
           if (ln == new_row) {
 #pragma unroll
             for (int c = 0; c < D / 64; ++c) rr.k[c] = kn8[c];
@@ -1267,6 +1274,39 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
         load_ring(ring[slot], tile, ring_rows[slot]);
         __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
         if (t0 + uu < nblk) process(ring[u], ring_rows[u], t0 + uu);
+      }
+    }
+  }
+
+  // fused append: the new K/V (codes and scales for 8-bit caches) into the
+  // slot of position n-1 (head group 0 writes; the others only read)
+  if constexpr (kStep) {
+    const int r0 = has_new ? tile_r0(new_t) : -1;
+    if (has_new && hg == 0 && r0 >= 0) {  // wave-uniform
+      const size_t row = static_cast<size_t>(r0) + static_cast<size_t>(new_row) * row_step;
+      if constexpr (kFp8) {
+        if (nblk == 0) quantize_new();  // (not reached: a partition holding position n-1 has a tile)
+        if (ln == 0) {
+#pragma unroll
+          for (int c = 0; c < D / 64; ++c)
+            *reinterpret_cast<u32x4*>(a.k_cache_w + row * D + (q4 + 4 * c) * 16) = kn8[c];
+        }
+        if (q4 == 0) {
+          char* vd = a.v_cache_w + row * D + ln * (D / 16);
+          if constexpr (D / 64 == 2) *reinterpret_cast<u32x2*>(vd) = u32x2{vn8[0], vn8[1]};
+          else *reinterpret_cast<unsigned*>(vd) = vn8[0];
+        }
+        if (lane == 0) {
+          reinterpret_cast<float*>(const_cast<char*>(a.k_scales))[row] = ks_new;
+          reinterpret_cast<float*>(const_cast<char*>(a.v_scales))[row] = vs_new;
+        }
+      } else {
+        const size_t dst = row * S::kRowBytes;
+        if (ln == 0) {
+#pragma unroll
+          for (int c = 0; c < S::kNK; ++c) *reinterpret_cast<u32x4*>(a.k_cache_w + dst + (4 * c + q4) * 16) = kn[c];
+        }
+        if (q4 == 0) store_dwords<S::kVDW>(a.v_cache_w + dst + ln * S::kE * S::kElt, vn);
       }
     }
   }
