@@ -46,6 +46,7 @@
 #include <pkv.h>
 #include <stdint.h>
 
+#include <array>
 #include <mutex>
 
 namespace {
@@ -556,6 +557,19 @@ struct DecodeArgs {
   int32_t q_tiles;         // 16-row query tiles per (sequence, KV head): ceil(max_q_len * group / 16)
 };
 
+// Dynamic LDS of the decode kernel when its waves are partitions of one unit
+// (fused step): each wave's normalised partial, lane-major per 16-byte chunk,
+// then the waves' lse values, then an arrival counter.
+extern __shared__ __align__(16) char pkv_dyn_lds[];
+// Then the exchange area of a partly filled group's preloaded tile rows
+// (128 per wave) and the counter.
+constexpr size_t wg_merge_xchg_offset(int waves, int head_dim) {
+  return static_cast<size_t>(waves) * (head_dim / 16) * 64 * 16 + static_cast<size_t>(waves) * 16 * 4;
+}
+constexpr size_t wg_merge_lds_bytes(int waves, int head_dim) {
+  return wg_merge_xchg_offset(waves, head_dim) + static_cast<size_t>(waves) * 128 * 4 + 16;
+}
+
 // Fused merge of a wave's kR row groups (16 query rows each) over the
 // partitions of its work unit `unit`, from the partition kernel itself.
 // Partials are stored lane-major per (work unit, row group) (each store
@@ -714,10 +728,13 @@ constexpr int prefill_row_groups(pkv_dtype dtype) { return dtype == PKV_F32 ? 2 
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 4
 #endif
+#ifndef PKV_WG_PARTS  // HND decode: the waves of a workgroup are partitions of one unit
+#define PKV_WG_PARTS 1
+#endif
 template <int kMode>
 constexpr int kDecodeWaves = kMode == kModePrefill ? 1 : PKV_DECODE_WAVES;
 
-template <typename T, int D, int kMode, int kQ, bool kNHD>
+template <typename T, int D, int kMode, int kQ, bool kNHD, bool kWgp = false>
 __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_kernel(DecodeArgs a) {
   constexpr bool kFp8 = kQ != 0;  // the caches hold 8-bit codes with per-row scales
   constexpr bool kStep = kMode == kModeStep;
@@ -739,22 +756,34 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   // p of every unit would land on XCD p % 8, and the low partitions, which
   // every sequence has, would crowd the first XCDs. Rotating the partitions
   // by the unit index starts each unit on another XCD.
-  const int p = PKV_XCD_ROTATE ? static_cast<int>((blockIdx.x + blockIdx.y + gridDim.y * blockIdx.z) % gridDim.x)
-                               : static_cast<int>(blockIdx.x);
+  //
+  // HND decode with several waves per workgroup: the waves are consecutive
+  // partitions of one unit (wave w takes partition W * x + w of the
+  // workgroup's rotated index x), so a unit's partials meet in the
+  // workgroup's LDS instead of global memory. Otherwise (NHD, whose blocks
+  // interleave the heads row by row): consecutive KV heads of one partition.
+  constexpr bool kWgParts = kWgp && kStep && !kNHD && kMaxW > 1;
+  const int wv = kMaxW == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int W = static_cast<int>(blockDim.x >> 6);
+  const int xr = PKV_XCD_ROTATE ? static_cast<int>((blockIdx.x + blockIdx.y + gridDim.y * blockIdx.z) % gridDim.x)
+                                : static_cast<int>(blockIdx.x);
+  const int p = kWgParts ? xr * W + wv : xr;
   const int units_per_head = kPrefill ? a.q_tiles : a.head_groups;  // work units per (sequence, KV head)
   const int jg = blockIdx.y / units_per_head;  // KV head, or group of blockDim / 64 heads
   // head group (decode) or query tile (prefill; in descending order: later
   // tiles see more keys, and the longest workgroups start first)
   const int ui = kPrefill ? units_per_head - 1 - static_cast<int>(blockIdx.y - jg * units_per_head)
                           : static_cast<int>(blockIdx.y - jg * units_per_head);
-  const int j = kMaxW == 1 ? jg
-                           : jg * static_cast<int>(blockDim.x >> 6) +
-                                 __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int j = (kMaxW == 1 || kWgParts) ? jg : jg * W + wv;
+  if constexpr (kWgParts) {  // the LDS arrival counter starts at zero
+    if (threadIdx.x == 0) *reinterpret_cast<int*>(pkv_dyn_lds + wg_merge_lds_bytes(W, D) - 16) = 0;
+    __syncthreads();
+  }
   const int hg = kPrefill ? 0 : ui;
   const int b = blockIdx.z;
 
   const int cap = a.cap_tokens;
-  const int blk0 = p * a.pb_per_part;  // first tile of the partition
+  int blk0 = p * a.pb_per_part;  // first tile of the partition
   const int row_step = kNHD ? a.num_kv_heads : 1;  // cache rows between consecutive tokens of one head
   // First cache row of each of this partition's tiles (lane i: tile blk0 + i,
   // and blk0 + 64 + i for partitions longer than 64 tiles), -1 where the
@@ -789,7 +818,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   }
   __builtin_amdgcn_sched_barrier(0);  // the length and table loads are issued before any wait on them
   n = __builtin_amdgcn_readfirstlane(n);
-  const int my_r0 = row_of(id0, blk0 + lane), my_r02 = row_of(id1, blk0 + 64 + lane);
+  int my_r0 = row_of(id0, blk0 + lane), my_r02 = row_of(id1, blk0 + 64 + lane);
   // a length past the table's capacity is clamped for reading; the fused
   // step then appends nothing (position n - 1 is not the new token's)
   const bool len_fits = n <= cap;
@@ -826,9 +855,47 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
     if (n == 0) return;  // no rows: the unit does nothing (its merge counter stays untouched)
   }
   const int nblk_seq = (n + kTile - 1) / kTile;  // tiles the wave reads
-  const int nparts = nblk_seq == 0 ? 1 : (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
-  if (p >= nparts) return;
-  const int nblk = min(a.pb_per_part, nblk_seq - blk0);  // may be 0 only when n == 0
+  int nparts = nblk_seq == 0 ? 1 : (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
+  int nblk = 0;
+  int ngroups = 1;  // partition-grouped workgroups of a unit (fused step)
+  bool grouped = false;
+  if constexpr (kWgParts) {  // wave-uniform
+    // The unit's tiles in groups of W full partitions, one group per
+    // workgroup. A group that the sequence fills only in part (its last,
+    // or a short sequence's only group) splits its tiles evenly over all W
+    // waves; the waves exchange their preloaded tile rows through LDS, so
+    // no wave waits for a second table read and no wave sits idle.
+    const int gt = W * a.pb_per_part;  // tiles of a full group
+    if (nblk_seq == 0) {  // nothing to read: one wave writes the zero row
+      if (wv != 0) return;
+      nparts = 1;
+    } else {
+      grouped = true;
+      ngroups = (nblk_seq + gt - 1) / gt;
+      if (xr >= ngroups) return;  // the whole workgroup
+      nparts = W * ngroups;
+      const int g0 = xr * gt;
+      const int len = min(gt, nblk_seq - g0);
+      if (len < gt) {  // workgroup-uniform
+        const int base = len / W, rem = len % W;
+        blk0 = g0 + wv * base + min(wv, rem);
+        nblk = base + (wv < rem ? 1 : 0);
+        int* xt = reinterpret_cast<int*>(pkv_dyn_lds + wg_merge_xchg_offset(W, D));  // [W][pb_per_part]
+        if (lane < a.pb_per_part) xt[wv * a.pb_per_part + lane] = my_r0;
+        if (64 + lane < a.pb_per_part) xt[wv * a.pb_per_part + 64 + lane] = my_r02;
+        __syncthreads();
+        const int off = blk0 - g0;
+        my_r0 = lane < nblk ? xt[off + lane] : -1;
+        my_r02 = 64 + lane < nblk ? xt[off + 64 + lane] : -1;
+      } else {
+        nblk = a.pb_per_part;
+      }
+    }
+  }
+  if (!grouped) {
+    if (p >= nparts) return;
+    nblk = min(a.pb_per_part, nblk_seq - blk0);  // may be 0 only when n == 0
+  }
   auto tile_r0 = [&](int t) -> int {  // t wave-uniform, < 128
     return t < 64 ? __builtin_amdgcn_readlane(my_r0, t & 63) : __builtin_amdgcn_readlane(my_r02, t & 63);
   };
@@ -836,10 +903,10 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   // Fused append: the partition holding position n-1 takes the new token's
   // K/V from k_new/v_new and uses them from registers. They are read here,
   // right after the table (so no earlier wait covers them); 8-bit rows are
-  // quantized only when the tile that holds position n-1 comes up (the
-  // partition's last), and the row is written to its slot after the loop,
-  // where the store's completion overlaps the merge's own wait.
-  const bool has_new = kStep && n > 0 && len_fits && p == nparts - 1;
+  // quantized just before the first tile loads, and the row is written to
+  // its slot after the loop, where the store's completion overlaps the
+  // merge's own wait.
+  const bool has_new = kStep && n > 0 && len_fits && nblk > 0 && blk0 + nblk == nblk_seq;
   const int new_t = has_new ? (n - 1) / kTile - blk0 : -1;  // tile index inside the partition
   const int new_row = (n - 1) % kTile;
   u32x4 kn[S::kNK];   // 16-bit caches: the new K in the tile's chunk order
@@ -994,7 +1061,6 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
       if (t == new_t) {  // wave-uniform
         valid = new_row + 1;
         if constexpr (kFp8) {
-          quantize_new();
           if (ln == new_row) {
 #pragma unroll
             for (int c = 0; c < D / 64; ++c) rr.k[c] = kn8[c];
@@ -1236,6 +1302,9 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   int ring_rows[kPairs ? 2 * kNP : kRing];
   if constexpr (kPairs) {
     if (nblk > 0) {
+      // 8-bit caches: the new row, read right after the table, is quantized
+      // before the first tile loads go out (only the quantized row stays live)
+      if (has_new) quantize_new();
 #pragma unroll
       for (int u = 0; u < 2 * (kNP - 1); ++u) {
         const size_t tile = block_src(u, ring_rows[u]);
@@ -1285,7 +1354,6 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
     if (has_new && hg == 0 && r0 >= 0) {  // wave-uniform
       const size_t row = static_cast<size_t>(r0) + static_cast<size_t>(new_row) * row_step;
       if constexpr (kFp8) {
-        if (nblk == 0) quantize_new();  // (not reached: a partition holding position n-1 has a tile)
         if (ln == 0) {
 #pragma unroll
           for (int c = 0; c < D / 64; ++c)
@@ -1348,6 +1416,66 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg) write_out(rg, inv[rg]);
     return;
+  }
+  if constexpr (kWgParts) {
+    if (grouped) {  // wave-uniform
+      // Merge the workgroup's partitions of this unit in LDS: each wave leaves
+      // its normalised partial and lse, counts its arrival, and the last of the
+      // `active` waves combines them (exact log-sum-exp merge). A unit whose
+      // partitions span several workgroups then merges the workgroup results
+      // through global memory (fused_merge), one partial per workgroup.
+      const int active = W;  // every wave of the group takes part (some with no tiles: lse = -inf)
+      const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * units_per_head + ui;
+      const MergeSpace ms{a.ws_o, a.ws_lse, a.counters, a.num_parts};
+      if (active > 1) {
+        constexpr int kE = S::kE;
+        f32x4* po = reinterpret_cast<f32x4*>(pkv_dyn_lds);                       // [W][kE][64]
+        float* pl = reinterpret_cast<float*>(pkv_dyn_lds + static_cast<size_t>(W) * kE * 64 * 16);  // [W][16]
+        int* ctr = reinterpret_cast<int*>(pkv_dyn_lds + wg_merge_lds_bytes(W, D) - 16);
+#pragma unroll
+        for (int k = 0; k < kE; ++k) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int idx = 4 * k + e;  // value index i * E + mt
+            v[e] = acc[0][idx % kE][idx / kE] * inv[0];
+          }
+          po[(wv * kE + k) * 64 + lane] = v;
+        }
+        if (lane < 16) pl[wv * 16 + lane] = m_run[0] + __builtin_amdgcn_logf(l_tot[0]);
+        int prev = 0;
+        if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0 is active (the unit's first row is real)
+        if (prev != active - 1) return;
+        float M = kNegInf;
+        for (int w2 = 0; w2 < active; ++w2) M = fmaxf(M, pl[w2 * 16 + ln]);
+        float L = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < kE; ++mt) acc[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w2 = 0; w2 < active; ++w2) {
+          const float wt = __builtin_amdgcn_exp2f(pl[w2 * 16 + ln] - M);
+          L += wt;
+#pragma unroll
+          for (int k = 0; k < kE; ++k) {
+            const f32x4 v = po[(w2 * kE + k) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int idx = 4 * k + e;
+              acc[0][idx % kE][idx / kE] += wt * v[e];
+            }
+          }
+        }
+        if (ngroups == 1) {
+          write_out(0, 1.0f / L);
+          return;
+        }
+        m_run[0] = M;
+        l_tot[0] = L;
+        inv[0] = 1.0f / L;
+      }
+      fused_merge<D, kR>(ms, unit, xr, ngroups, lane, acc, m_run, l_tot, inv, write_out);
+      return;
+    }
   }
   if constexpr (kMode == kModeSplit) {
     static_assert(kR == 1, "the split path has one row group");
@@ -2341,8 +2469,32 @@ int device_cus() {
   }
   return cus[dev];
 }
-// Waves per decode workgroup: the most (up to PKV_DECODE_WAVES, dividing the
-// KV head count) that still leave a workgroup for every compute unit.
+// HND fused step: waves per workgroup when the waves are consecutive
+// partitions of one unit (sequence, KV head, head group), or 1 to keep the
+// head-grouped mapping. `resident(w)` is the number of workgroups of w waves
+// one compute unit holds; every choice leaves a workgroup for every compute
+// unit. Wide groups leave fewer partials to merge through global memory, and
+// a unit that one group covers merges in LDS alone. But a group's last wave
+// does that global merge after its siblings have left, and a new workgroup
+// needs as many free wave slots on one compute unit as it has waves: in a
+// grid that runs in several waves of workgroups, wide groups whose members
+// end at different times (ragged batches) leave slots idle. Hence the widest
+// groups when the grid is resident all at once or one group covers a unit,
+// else groups of 2.
+template <typename Resident>
+int partition_waves(int64_t parts, int64_t units, Resident resident) {
+  if (!PKV_WG_PARTS) return 1;
+  const int64_t cus = device_cus();
+  for (int w = PKV_DECODE_WAVES; w > 1; w /= 2) {
+    const int64_t groups = ceil_div64(parts, w), wgs = groups * units;
+    if (parts < w || wgs < cus) continue;
+    if (w == 2 || groups == 1 || wgs <= static_cast<int64_t>(resident(w)) * cus) return w;
+  }
+  return 1;
+}
+// NHD decode: waves per workgroup, one per KV head: the most (up to
+// PKV_DECODE_WAVES, dividing the KV head count) that still leave a workgroup
+// for every compute unit.
 int decode_waves(int64_t waves, int32_t num_kv_heads) {
   for (int w = PKV_DECODE_WAVES; w > 1; w /= 2)
     if (num_kv_heads % w == 0 && waves / w >= device_cus()) return w;
@@ -2352,10 +2504,34 @@ int decode_waves(int64_t waves, int32_t num_kv_heads) {
 template <typename T, int D, int kQ, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
   static_assert(kDecodeWaves<kModeSplit> == kDecodeWaves<kModeStep>, "one bound for both modes");
+  // waves = consecutive KV heads of one partition
   const int w = decode_waves(static_cast<int64_t>(a.num_parts) * a.num_kv_heads * a.head_groups * num_seqs,
                              a.num_kv_heads);
   const dim3 grid(a.num_parts, static_cast<unsigned>(a.num_kv_heads / w * a.head_groups), num_seqs);
   if (phases & kFusedStep) {
+    if constexpr (!kNHD) {  // waves = consecutive partitions of one unit, merged in LDS
+      constexpr auto kernel = decode_partition_kernel<T, D, kModeStep, kQ, false, true>;
+      // resident workgroups per compute unit, by waves per workgroup (same on every device)
+      static const std::array<int, PKV_DECODE_WAVES + 1> occ = [] {
+        std::array<int, PKV_DECODE_WAVES + 1> r{};
+        for (int v = 2; v <= PKV_DECODE_WAVES; v *= 2) {
+          int nb = 0;
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64 * v, wg_merge_lds_bytes(v, D)) !=
+              hipSuccess)
+            nb = 0;  // unknown: the grouped mapping is not used
+          r[v] = nb;
+        }
+        return r;
+      }();
+      const int wp = partition_waves(a.num_parts, static_cast<int64_t>(num_seqs) * a.num_kv_heads * a.head_groups,
+                                     [&](int v) { return occ[v]; });
+      if (wp > 1) {
+        const dim3 g(static_cast<unsigned>(ceil_div64(a.num_parts, wp)),
+                     static_cast<unsigned>(a.num_kv_heads * a.head_groups), num_seqs);
+        hipLaunchKernelGGL(kernel, g, dim3(64 * wp), wg_merge_lds_bytes(wp, D), stream, a);
+        return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+      }
+    }
     hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64 * w), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }

@@ -415,6 +415,40 @@ def test_fused_step_shapes_and_edge_lengths(torch_dev, dtype, shape):
         fused_parity(torch, dev, wk, pb, f"fused {dtype} {shape} pb={pb}")
 
 
+def grouped_lens(B, max_len, seed):
+    """Lengths around every tile, partition and group boundary of the grouped
+    launches below, then seeded uniform draws; the longest is ``max_len``."""
+    edge = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512]
+    lens = [n for n in edge if n <= max_len] + [max_len - 1, max_len]
+    rng = np.random.default_rng(seed)
+    lens += rng.integers(1, max_len + 1, size=B - len(lens)).tolist()
+    return tuple(int(n) for n in lens[:B])
+
+
+# (B, Hq, Hkv, D, partition_blocks, longest context). On a 256-CU MI355X these
+# fused steps run the partition-grouped workgroups (each workgroup's waves are
+# consecutive partitions of one (sequence, KV head) unit, merged in LDS):
+# 256 units x 2 groups of 4 partitions (fp32: 4 groups of 2, the grid being
+# larger than the resident count); 256 x 1 group of 4; 128 units x 2 groups
+# of 2 (the second partly filled).
+GROUPED = [(64, 28, 4, 128, 4, 512), (64, 28, 4, 128, 8, 512), (32, 32, 4, 128, 8, 384)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("case", GROUPED, ids=lambda c: "B{}_{}x{}_pb{}_n{}".format(c[0], c[1], c[2], c[4], c[5]))
+def test_fused_step_grouped_workgroups_ragged(torch_dev, dtype, case):
+    """Ragged lengths through the partition-grouped fused step: full and
+    partly filled groups, groups split unevenly over their waves, units whose
+    partitions span one or several workgroups."""
+    torch, dev = torch_dev
+    B, Hq, Hkv, D, pb, max_len = case
+    lens = grouped_lens(B, max_len, seed=B + pb)
+    cfg = wl.DecodeConfig("grouped", 0, 1, B, Hq, Hkv, D, 16, dtype, context_lens=lens)
+    wk = wl.make_host_workload(cfg, seed=4000 + pb + max_len)
+    note(f"fused step, grouped workgroups: {dtype} B={B} Hq={Hq} Hkv={Hkv} pb={pb} max_len={max_len}")
+    fused_parity(torch, dev, wk, pb, f"grouped {dtype} {case}")
+
+
 def test_fused_step_tiny_config_and_shared_prefix(torch_dev):
     torch, dev = torch_dev
     note("fused step: tiny fp32 config")

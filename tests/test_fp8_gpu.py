@@ -210,6 +210,34 @@ def test_fp8_attention_and_fused_step(torch_dev, q_dtype, shape, fmt):
         assert outs[0].tobytes() == outs[1].tobytes()
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("pb", [4, 8])
+def test_8bit_fused_step_grouped_workgroups_ragged(torch_dev, fmt, pb):
+    """64 sequences x 4 KV heads (256 units), ragged lengths up to 512: on a
+    256-CU MI355X the fused step's workgroups are consecutive partitions of
+    one unit, merged in LDS, with full, partly filled and uneven groups."""
+    torch, dev = torch_dev
+    edge = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512]
+    rng = np.random.default_rng(pb)
+    lens = tuple(edge + rng.integers(1, 513, size=64 - len(edge)).tolist())
+    cfg = wl.DecodeConfig("grouped8", 0, 1, 64, 28, 4, 128, 16, "bf16", context_lens=lens)
+    wk = wl.make_host_workload_fp8(cfg, seed=5000 + pb)
+    ref, kc, vc, ks, vs = oracle_fp8(wk, fmt)
+    note(f"{fmt} fused step, grouped workgroups: pb={pb}")
+    d = to_dev(torch, dev, wk)
+    ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], pb)
+    outs = []
+    for _ in range(2):
+        out = torch.full_like(d["q"], float("nan"))
+        pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                            cfg.scale, out, ws, pb, fmt=fmt)
+        torch.cuda.synchronize()
+        outs.append(wl.torch_to_raw(out, "bf16"))
+    assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} grouped fused step")
+    check_close(oracle.upcast(outs[0], "bf16"), ref, f"{fmt} grouped fused step pb={pb}")
+    assert outs[0].tobytes() == outs[1].tobytes()
+
+
 def test_fp8_full_size_70b_sampled(torch_dev):
     torch, dev = torch_dev
     cfg = wl.CONFIG_BY_NAME["llama3_70b"]
