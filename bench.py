@@ -374,6 +374,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layers to loop (0 = the configuration's count)")
     ap.add_argument("--partition-blocks", type=int, default=0, help="blocks per partition (0 = library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU-reference work (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed timing of the same steps")
     ap.add_argument("--mode", choices=("fused", "split"), default="fused",
                     help="fused: one decode_step launch per layer (append + attention + merge); "
                          "split: kv_append, decode_partitions, decode_merge")
@@ -553,6 +554,32 @@ def main():
         step_ev[k][1].record(stream)
     torch.cuda.synchronize()
     step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    # The same step captured once into a HIP graph and replayed K times: the
+    # kernels are the same; the graph removes the host launch path between
+    # them. Reported beside the eager figures, which stay the headline.
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        assert all(torch.isfinite(o).all().item() for o in outs[:2]), "non-finite attention output after replay"
+        del g
+        log(f"graph replay: {graph_ms:.3f} ms/step")
     # In fused mode the step is exactly one launch of the kernel per layer, so
     # the timed region's events give its average launch duration directly (an
     # event pair around each launch adds several microseconds of its own).
@@ -638,6 +665,11 @@ def main():
         "stream_ceiling_gbps": round(stream_gbs, 2),
         "frac_of_stream_ceiling": round(gbs / stream_gbs, 4),
         "seqs_per_s": round(B / (ms_per_step * 1e-3), 2),
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4), "value": round(step_kv / (graph_ms * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(step_kv / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(graph_ms / L * 1e3, 2),
+            "note": "the same steps captured into one HIP graph and replayed; value above is the eager stream"},
         "kv_bytes_per_step": step_kv,
         "unique_kv_bytes_per_step": unique_layer * L,
         "unique_kv_gbps": round(unique_layer * L / (ms_per_step * 1e-3) / 1e9, 2),

@@ -903,7 +903,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   // Fused append: the partition holding position n-1 takes the new token's
   // K/V from k_new/v_new and uses them from registers. They are read here,
   // right after the table (so no earlier wait covers them); 8-bit rows are
-  // quantized just before the first tile loads, and the row is written to
+  // quantized once the first tile loads are out, and the row is written to
   // its slot after the loop, where the store's completion overlaps the
   // merge's own wait.
   const bool has_new = kStep && n > 0 && len_fits && nblk > 0 && blk0 + nblk == nblk_seq;
@@ -1302,14 +1302,15 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   int ring_rows[kPairs ? 2 * kNP : kRing];
   if constexpr (kPairs) {
     if (nblk > 0) {
-      // 8-bit caches: the new row, read right after the table, is quantized
-      // before the first tile loads go out (only the quantized row stays live)
-      if (has_new) quantize_new();
 #pragma unroll
       for (int u = 0; u < 2 * (kNP - 1); ++u) {
         const size_t tile = block_src(u, ring_rows[u]);
         load_ring(ring[u], tile, ring_rows[u]);
       }
+      // 8-bit caches: the new row, read right after the table, is quantized
+      // while the first tiles are in flight (only the quantized row stays live)
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_new) quantize_new();
       for (int t0 = 0; t0 < nblk; t0 += 2 * kNP) {
 #pragma unroll
         for (int pp = 0; pp < kNP; ++pp) {
