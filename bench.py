@@ -40,6 +40,35 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def copy_calibration(args, torch, dev):
+    """--copy-calibration-mib: one device-to-device copy of that size, so a
+    counter run can read FETCH_SIZE / WRITE_SIZE for known bytes beside the
+    kernel it measures."""
+    if not args.copy_calibration_mib:
+        return
+    n = args.copy_calibration_mib * 2**20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {args.copy_calibration_mib} MiB device-to-device copy done")
+
+
+def profile_traffic(name, pb):
+    """HBM bytes per launch from a committed counter summary under profiles/,
+    if it was taken on this kernel source and partition size (else None)."""
+    tfile = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(tfile):
+        return None
+    with open(tfile) as f:
+        tr = json.load(f)
+    if tr.get("kernel_sha") == kernel_sha() and tr.get("partition_blocks") == pb:
+        return tr.get("bytes_per_launch")
+    return None
+
+
 def pool_assignment(cfg, lens, pkv, wl):
     """Block lists, slot mapping and tables from libpkv's host block pool."""
     bs = cfg.block_size
@@ -313,6 +342,7 @@ def run_prefill(args):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    copy_calibration(args, torch, dev)
     pairs = B * sum(P + i + 1 for i in range(C))  # (query token, visible key) pairs
     flops = 4 * Hq * D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
@@ -469,6 +499,9 @@ def main():
 
     if args.op == "stream":
         stream_ms, stream_gbs = time_stream(pkv, torch, wkd, L, fp8, lay, pb, kcache0, stream, args, step_kv)
+        copy_calibration(args, torch, dev)
+        geom = "" if (lay == "HND" and bs == 16) else f"_{lay.lower()}_bs{bs}"
+        traffic = profile_traffic(f"stream{'_' + args.kv if fp8 else ''}{geom}_{cfg.name}_traffic.json", pb)
         print(json.dumps({
             "metric": "decode access-pattern read ceiling GB/s (K/V tiles through the block tables, nothing computed)",
             "value": round(stream_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -480,7 +513,7 @@ def main():
             "frac_of_hbm_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
             "roofline": {"bound": "hbm", "kernel": "stream_tiles_kernel", "achieved": round(stream_gbs, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(stream_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "alg_bytes_per_launch": kv_layer,
+                         "traffic": traffic, "alg_bytes_per_launch": kv_layer,
                          "avg_launch_us": round(stream_ms / L * 1e3, 2), "kernel_sha": kernel_sha()},
             "cpu_baseline": None}), flush=True)
         return
@@ -594,14 +627,8 @@ def main():
     gbs = step_kv / (ms_per_step * 1e-3) / 1e9
     achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
 
-    traffic = None
     geom = "" if (lay == "HND" and bs == 16) else f"_{lay.lower()}_bs{bs}"
-    tfile = os.path.join(ROOT, "profiles", f"decode_{args.mode}{'_' + args.kv if fp8 else ''}{geom}_{cfg.name}_traffic.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_sha() and tr.get("partition_blocks") == pb:
-            traffic = tr.get("bytes_per_launch")
+    traffic = profile_traffic(f"decode_{args.mode}{'_' + args.kv if fp8 else ''}{geom}_{cfg.name}_traffic.json", pb)
 
     stream_ms, stream_gbs = time_stream(pkv, torch, wkd, L, fp8, lay, pb, kcache0, stream, args, step_kv)
 
@@ -631,15 +658,7 @@ def main():
     unique_tokens = sum(rows_seen.values())
     unique_layer = 2 * Hkv * ((D + 4) if fp8 else D * esz) * unique_tokens
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * 2**20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b2 = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b2.copy_(a)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {args.copy_calibration_mib} MiB device-to-device copy done")
+    copy_calibration(args, torch, dev)
 
     result = {
         "metric": "paged decode attention K/V-read GB/s (% of HBM peak) and seqs/s at 1 GPU",
