@@ -429,9 +429,10 @@ pkv_status pkv_copy_blocks(void* const* caches, const int64_t* block_bytes, int3
 
 /*
  * pkv_stream_tiles -- a measurement call, not part of attention: the read
- * ceiling of the decode access pattern. It launches the workgroups a decode
- * launch over these caches would (one wave per (sequence, KV head, context
- * partition), the same partitions, workgroup shape and XCD order), looks up
+ * ceiling of the decode access pattern. It launches one wave per (sequence,
+ * KV head, context partition) over the decode call's partitions, in the
+ * workgroups and XCD order of the split decode launch (consecutive KV heads of
+ * one partition per workgroup), looks up
  * each tile through block_tables and loads the K and V tiles (plus the row
  * scales when given) with the same bounded nontemporal loads, and computes
  * nothing but an XOR of the loaded words, written to sink. The time it takes

@@ -2222,12 +2222,13 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, const int3
 
 // ---------------------------------------------------------------------------
 // Read ceiling of the decode access pattern (a measurement kernel): the same
-// workgroups, waves, partitions, XCD rotation, block-table lookups and
-// bounded nontemporal tile loads as a decode launch over the same cache, with
-// nothing computed but an XOR of the loaded words (stored to `sink`, one word
-// per lane and wave, so the loads stay live). Whatever rate this reaches is
-// what the memory system gives for these tiles in this order; the decode
-// kernels are measured against it.
+// partitions, block-table lookups and bounded nontemporal tile loads as a
+// decode launch over the same cache, in the split decode launch's workgroups
+// (consecutive KV heads of one partition) and XCD rotation, with nothing
+// computed but an XOR of the loaded words (stored to `sink`, one word per lane
+// and wave, so the loads stay live). Whatever rate this reaches is what the
+// memory system gives for these tiles; the decode kernels are measured
+// against it.
 // ---------------------------------------------------------------------------
 struct StreamArgs {
   const char* k;
