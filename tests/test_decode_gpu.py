@@ -449,6 +449,31 @@ def test_fused_step_grouped_workgroups_ragged(torch_dev, dtype, case):
     fused_parity(torch, dev, wk, pb, f"grouped {dtype} {case}")
 
 
+def multi_round_lens(B, max_len, seed):
+    """Zero lengths, lengths around tile and partition boundaries (partitions
+    of 2 tiles: 32 tokens) and exact multiples of a partition, then seeded
+    draws; the longest is max_len."""
+    edge = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 320, 511, 512, 513, 0]
+    rng = np.random.default_rng(seed)
+    lens = edge + [max_len] + rng.integers(1, max_len + 1, size=B - len(edge) - 1).tolist()
+    return tuple(int(n) for n in lens[:B])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_step_multi_round_ragged(torch_dev, dtype):
+    """64 ragged sequences x 4 KV heads with partitions of 2 tiles: on a 256-CU
+    MI355X the fused step's grid runs in several rounds of workgroups, in
+    partition-grouped workgroups of two waves, most units spanning several
+    workgroups. Zero-length sequences, single tiles and exact partition
+    multiples included; two calls on one workspace (the counters reset)."""
+    torch, dev = torch_dev
+    lens = multi_round_lens(64, 700, seed=7)
+    cfg = wl.DecodeConfig("multiround", 0, 1, 64, 28, 4, 128, 16, dtype, context_lens=lens)
+    wk = wl.make_host_workload(cfg, seed=4400)
+    note(f"fused step, multi-round grid: {dtype}, 64 ragged sequences up to 700 tokens, partition_blocks=2")
+    fused_parity(torch, dev, wk, 2, f"multi-round {dtype}")
+
+
 def test_fused_step_tiny_config_and_shared_prefix(torch_dev):
     torch, dev = torch_dev
     note("fused step: tiny fp32 config")

@@ -238,6 +238,36 @@ def test_8bit_fused_step_grouped_workgroups_ragged(torch_dev, fmt, pb):
     assert outs[0].tobytes() == outs[1].tobytes()
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_8bit_fused_step_multi_round_ragged(torch_dev, fmt):
+    """The fused step over 8-bit caches on a grid of several rounds of
+    workgroups: 64 ragged sequences (zero lengths included) x 4 KV heads,
+    partitions of 2 tiles, two calls."""
+    torch, dev = torch_dev
+    edge = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 320, 511, 512, 513, 0, 700]
+    rng = np.random.default_rng(11)
+    lens = tuple(edge + rng.integers(1, 701, size=64 - len(edge)).tolist())
+    cfg = wl.DecodeConfig("multiround8", 0, 1, 64, 28, 4, 128, 16, "bf16", context_lens=lens)
+    wk = wl.make_host_workload_fp8(cfg, seed=5500)
+    ref, kc, vc, ks, vs = oracle_fp8(wk, fmt)
+    note(f"{fmt} fused step, multi-round grid")
+    d = to_dev(torch, dev, wk)
+    ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], 2)
+    outs = []
+    for _ in range(2):
+        out = torch.full_like(d["q"], float("nan"))
+        pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                            cfg.scale, out, ws, 2, fmt=fmt)
+        torch.cuda.synchronize()
+        outs.append(wl.torch_to_raw(out, "bf16"))
+    assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} multi-round fused step")
+    o = oracle.upcast(outs[0], "bf16")
+    zero = [b for b, n in enumerate(lens) if n == 0]
+    assert not o[zero].any(), "zero-length sequences must give zero rows"
+    check_close(o, ref, f"{fmt} multi-round fused step")
+    assert outs[0].tobytes() == outs[1].tobytes()
+
+
 def test_fp8_full_size_70b_sampled(torch_dev):
     torch, dev = torch_dev
     cfg = wl.CONFIG_BY_NAME["llama3_70b"]
