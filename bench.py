@@ -250,6 +250,7 @@ def run_copy_blocks(args):
     torch.cuda.synchronize()
     ref_gbs = bytes_launch / (c0.elapsed_time(c1) / args.steps * 1e-3) / 1e9
     del src, dst
+    copy_calibration(args, torch, dev)
     cpu = None
     if args.cpu_budget > 0:
         import oracle
