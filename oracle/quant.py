@@ -56,10 +56,13 @@ _POS_VALUES = np.array([e4m3_value(c) for c in _POS_CODES], dtype=np.float64)
 assert np.all(np.diff(_POS_VALUES) > 0)
 
 
+# the value of every code, from e4m3_value (built once: decoding looks codes up)
+_E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     """float64 values of uint8 codes."""
-    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
-    return table[np.asarray(codes, dtype=np.uint8)]
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:

@@ -268,32 +268,72 @@ def test_8bit_fused_step_multi_round_ragged(torch_dev, fmt):
     assert outs[0].tobytes() == outs[1].tobytes()
 
 
-def test_fp8_full_size_70b_sampled(torch_dev):
-    torch, dev = torch_dev
-    cfg = wl.CONFIG_BY_NAME["llama3_70b"]
-    note("fp8 full-size Llama-3-70B layer: drawing on the device")
+def check_full_size_8bit(torch, dev, cfg, seqs, fmt, what):
+    """Draw one layer of 8-bit codes and row scales on the device (the bench's
+    generator), run the fused step twice on one workspace, and compare the
+    outputs of ``seqs`` with the reference over the whole pool (every
+    sequence's new token appended first) and the code and scale pools byte
+    for byte after the append."""
     wkd = wl.make_device_workload_fp8(cfg, dev, layers=1)
-    seqs = [0, 13, 31]
-    refs = {}
-    for b in seqs:  # reference on the sampled sequences' blocks, copied back before the append
-        idx = torch.from_numpy(wkd.assignment.blocks[b].astype(np.int64)).to(dev)
-        kc = wkd.k_codes[0].index_select(0, idx).cpu().numpy()
-        vc = wkd.v_codes[0].index_select(0, idx).cpu().numpy()
-        ks = wkd.k_scales[0].index_select(0, idx).cpu().numpy()
-        vs = wkd.v_scales[0].index_select(0, idx).cpu().numpy()
-        table = np.arange(len(idx), dtype=np.int32)[None, :]
-        n = int(wkd.context_lens[b])
-        slots = oracle.slot_mapping(table, [n - 1], 16)
-        oracle.kv_append_fp8(kc, vc, ks, vs, wl.torch_to_raw(wkd.k_new[0][b:b + 1], "bf16"),
-                             wl.torch_to_raw(wkd.v_new[0][b:b + 1], "bf16"), slots, 16, "bf16")
-        refs[b] = oracle.decode_attention_fp8(wl.torch_to_raw(wkd.q[0][b:b + 1], "bf16"), kc, vc, ks, vs, table, [n],
-                                              cfg.scale, cfg.num_kv_heads, 16, "bf16")[0]
+    lens = np.asarray(wkd.context_lens, np.int32)
+    B = len(lens)
+    note(f"  {what}: reference over the whole layer pool, {len(seqs)} of {B} sequences")
+    kc = wkd.k_codes[0].cpu().numpy()
+    vc = wkd.v_codes[0].cpu().numpy()
+    ks = wkd.k_scales[0].cpu().numpy()
+    vs = wkd.v_scales[0].cpu().numpy()
+    table = wkd.block_tables.cpu().numpy()
+    slots = oracle.slot_mapping(table, lens - 1, cfg.block_size)
+    oracle.kv_append_fp8(kc, vc, ks, vs, wl.torch_to_raw(wkd.k_new[0], cfg.dtype),
+                         wl.torch_to_raw(wkd.v_new[0], cfg.dtype), slots, cfg.block_size, cfg.dtype, fmt=fmt)
+    ref = oracle.decode_attention_fp8(wl.torch_to_raw(wkd.q[0], cfg.dtype), kc, vc, ks, vs, table, lens, cfg.scale,
+                                      cfg.num_kv_heads, cfg.block_size, cfg.dtype, seqs=seqs, fmt=fmt)
+    note(f"  {what}: fused step x2")
     out = torch.full_like(wkd.q[0], float("nan"))
     ws = pkv.alloc_step_workspace(wkd.q[0], wkd.k_codes[0], wkd.block_tables)
-    pkv.decode_step_fp8(wkd.q[0], wkd.k_new[0], wkd.v_new[0], wkd.k_codes[0], wkd.v_codes[0], wkd.k_scales[0],
-                        wkd.v_scales[0], wkd.block_tables, wkd.context_lens_dev, cfg.scale, out, ws)
+    for _ in range(2):
+        pkv.decode_step_fp8(wkd.q[0], wkd.k_new[0], wkd.v_new[0], wkd.k_codes[0], wkd.v_codes[0], wkd.k_scales[0],
+                            wkd.v_scales[0], wkd.block_tables, wkd.context_lens_dev, cfg.scale, out, ws, fmt=fmt)
     torch.cuda.synchronize()
-    o = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
-    assert np.isfinite(o).all()
-    for b, r in refs.items():
-        check_close(o[b], r, f"fp8 70B seq {b}")
+    o = oracle.upcast(wl.torch_to_raw(out, cfg.dtype), cfg.dtype)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    for b in seqs:
+        check_close(o[b], ref[b], f"{what} seq {b} (n={int(lens[b])})")
+    assert wkd.k_codes[0].cpu().numpy().tobytes() == kc.tobytes(), f"{what}: K codes differ"
+    assert wkd.v_codes[0].cpu().numpy().tobytes() == vc.tobytes(), f"{what}: V codes differ"
+    assert wkd.k_scales[0].cpu().numpy().tobytes() == ks.tobytes(), f"{what}: K scales differ"
+    assert wkd.v_scales[0].cpu().numpy().tobytes() == vs.tobytes(), f"{what}: V scales differ"
+    del wkd, out, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_8bit_full_size_70b_every_sequence(torch_dev, fmt):
+    """The Llama-3-70B layer over 8-bit caches: every sequence of the layer."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME["llama3_70b"]
+    note(f"{fmt} full-size Llama-3-70B layer, fused step: every sequence")
+    check_full_size_8bit(torch, dev, cfg, list(range(cfg.num_seqs)), fmt, f"{fmt} 70B")
+
+
+def test_fp8_full_size_ragged_every_partition_count(torch_dev):
+    """The ragged Qwen2.5-7B batch over E4M3 caches: at least 16 sequences,
+    one of every partition count the launch produces."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME["qwen25_7b_ragged"]
+    lens, asg = wl.make_structure(cfg)
+    pb = pkv.decode_partition_blocks(len(lens), cfg.num_heads, cfg.num_kv_heads, asg.table().shape[1],
+                                     cfg.block_size)
+    parts = [max(1, -(-(-(-int(n) // cfg.block_size)) // pb)) for n in lens]
+    pick = {}
+    for b, c in enumerate(parts):
+        pick.setdefault(c, b)
+    seqs = set(pick.values())
+    for b in np.argsort(lens, kind="stable"):
+        if len(seqs) >= 16:
+            break
+        seqs.add(int(b))
+    seqs = sorted(seqs)
+    note(f"e4m3 full-size {cfg.name}, fused step: sequences {seqs}")
+    check_full_size_8bit(torch, dev, cfg, seqs, "e4m3", "e4m3 ragged")
+
