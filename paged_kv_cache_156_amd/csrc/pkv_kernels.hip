@@ -757,11 +757,13 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   // every sequence has, would crowd the first XCDs. Rotating the partitions
   // by the unit index starts each unit on another XCD.
   //
-  // HND decode with several waves per workgroup: the waves are consecutive
-  // partitions of one unit (wave w takes partition W * x + w of the
-  // workgroup's rotated index x), so a unit's partials meet in the
-  // workgroup's LDS instead of global memory. Otherwise (NHD, whose blocks
-  // interleave the heads row by row): consecutive KV heads of one partition.
+  // The partition-grouped instance (kWgp: the HND fused step, when the host
+  // picks it): the waves are consecutive partitions of one unit (wave w takes
+  // partition W * x + w of the workgroup's rotated index x), so a unit's
+  // partials meet in the workgroup's LDS instead of global memory. Otherwise
+  // (the split path, NHD caches, whose blocks interleave the heads row by
+  // row, and grids the host keeps head-grouped): consecutive KV heads of one
+  // partition.
   constexpr bool kWgParts = kWgp && kStep && !kNHD && kMaxW > 1;
   const int wv = kMaxW == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int W = static_cast<int>(blockDim.x >> 6);
