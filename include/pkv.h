@@ -113,7 +113,8 @@ pkv_status pkv_kv_append(const void* k, const void* v, const int64_t* slot_mappi
  * Each partition covers this many blocks of one sequence and one KV head;
  * partial results are merged exactly with a log-sum-exp combine. Returns 0
  * for an unsupported block_size. A partition may span at most 2048 tokens
- * (partition_blocks * block_size <= 2048) in every call below.
+ * (partition_blocks * block_size <= 2048) in every call below, except the
+ * prefill calls' workgroup kernel (see pkv_prefill_attention): 16384.
  */
 int32_t pkv_decode_partition_blocks(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                     int32_t max_blocks_per_seq, int32_t block_size);
@@ -380,12 +381,19 @@ pkv_status pkv_prefill_attention_int8(const void* q, const void* k_cache, const 
  *   workspace     >= pkv_prefill_workspace_bytes(...) bytes, zero-filled before
  *                 its first use; each completed call leaves its counters at
  *                 zero (calls sharing a workspace must not overlap)
+ *   partition_blocks  blocks per partition: partition_blocks * block_size
+ *                 <= 16384 for the workgroup kernel, <= 2048 for the
+ *                 one-wave kernel (see below); 0 = the library's choice,
+ *                 16384 or 1024 tokens, halved while the launch would have
+ *                 fewer than 512 work units
  * Every other argument as pkv_paged_decode_attention. Work unit: a group of
  * (query token, query head) rows of one KV head and one context partition --
  * 128 rows in a four-wave workgroup that shares each K/V tile through LDS for
  * 16-bit caches (8-bit caches: head size 128) and scale > 0, 64 (16-bit
- * queries) or 32 (fp32) rows in one wave otherwise; split contexts are merged in the kernel by the partition that
- * finishes last. The workspace size covers every variant.
+ * queries) or 32 (fp32) rows in one wave otherwise; split contexts are merged
+ * in the kernel by the partition that finishes last. The workspace size
+ * covers every variant. A workgroup reads the table entries of its partition
+ * up to the last key its rows see.
  * Errors as pkv_paged_decode_attention.
  */
 size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -60,7 +60,15 @@ using s16x4 = short __attribute__((ext_vector_type(4)));
 using f16x4 = _Float16 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 16;  // token rows per MFMA tile; a cache block holds block_size / 16 tiles
-constexpr int kMaxPartitionBlocks = 128;  // 16-row tiles per partition: two tile addresses per lane
+// 16-row tiles per partition of the decode, stream and one-wave prefill
+// kernels: two tile addresses per lane
+constexpr int kMaxPartitionBlocks = 128;
+// 16-row tiles per partition of the LDS prefill kernel, whose partition's
+// tile rows sit in an LDS table (4 bytes a tile)
+#ifndef PKV_PREFILL_MAX_TILES
+#define PKV_PREFILL_MAX_TILES 1024
+#endif
+constexpr int kMaxPrefillTiles = PKV_PREFILL_MAX_TILES;
 
 // K/V blocks kept in flight per wave ahead of the one being consumed
 #ifndef PKV_AHEAD_16BIT
@@ -1599,6 +1607,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds1[kBuf];
   __shared__ __attribute__((aligned(16))) char lds2[kBufs > 2 ? kBuf : 16];
   __shared__ __attribute__((aligned(16))) char ldsx[kXBytes];
+  __shared__ int trows[kMaxPrefillTiles];  // the partition's tile rows (-1: id outside the pool)
 
   // The lambdas below capture only locals: a lambda that referenced `a`
   // would take its address, and next to the cache -> LDS loads (which may
@@ -1651,7 +1660,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   const int nparts = (nblk_seq + a.pb_per_part - 1) / a.pb_per_part;
   if (p >= nparts) return;
   const int blk0 = p * a.pb_per_part;
-  const int nblk = min(a.pb_per_part, nblk_seq - blk0);
+  const int nblk = min(min(a.pb_per_part, kMaxPrefillTiles), nblk_seq - blk0);  // the host keeps pb in bounds
 
   // this wave's rows: kR groups of 16, row r = token r / g, head r % g
   const int r0 = wg_r0 + w * kR * kTile;
@@ -1682,8 +1691,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   }
   const float c = a.qk_scale;  // > 0: the host routes other scales to the one-wave kernel
 
-  // first cache row of each of the partition's tiles (lane i: tile blk0 + i
-  // and blk0 + 64 + i), -1 for a block id outside the pool
+  // first cache row of each of the partition's tiles, from the block table
+  // into LDS once (a thread per tile), -1 for a block id outside the pool;
+  // the barrier before the first loads publishes the table
   const size_t trow = static_cast<size_t>(b) * a.max_blocks;
   const int m = a.tiles_per_block;
   const int max_tiles = a.max_blocks * m;
@@ -1694,16 +1704,14 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     const int sub = lt - lb * m;
     return kNHD ? (bid * m + sub) * kTile * num_kv_heads + j : ((bid * num_kv_heads + j) * m + sub) * kTile;
   };
-  int my_r0 = -1, my_r02 = -1;
-  if (lane < a.pb_per_part && blk0 + lane < max_tiles) my_r0 = tile_row0(blk0 + lane);
-  if (64 + lane < a.pb_per_part && blk0 + 64 + lane < max_tiles) my_r02 = tile_row0(blk0 + 64 + lane);
+  for (int t = tid; t < nblk; t += kThreads) trows[t] = blk0 + t < max_tiles ? tile_row0(blk0 + t) : -1;
+  __syncthreads();
   const int rs = kRowB * (kNHD ? a.num_kv_heads : 1);  // bytes between a head's consecutive token rows
   const int ss = kNHD ? 4 * a.num_kv_heads : 4;        // 8-bit: bytes between their scales
   // first cache row of the partition's tile t and its rows to fetch: 0 past
   // the partition end or for an id outside the pool (nothing is read then)
   auto tile_src = [&](int t, int& valid) -> size_t {
-    const int tt = min(t, 127);
-    const int r = tt < 64 ? __builtin_amdgcn_readlane(my_r0, tt & 63) : __builtin_amdgcn_readlane(my_r02, tt & 63);
+    const int r = __builtin_amdgcn_readfirstlane(trows[min(t, nblk - 1)]);
     const bool ok = t < nblk && r >= 0;
     valid = ok ? min(kTile, n_wg - (blk0 + t) * kTile) : 0;
     return ok ? static_cast<size_t>(r) : 0;
@@ -2631,15 +2639,16 @@ struct PrefillPlan {
   int32_t rows_per_unit;   // (token, head) rows of one KV head per work unit
   int32_t slots_per_unit;  // 16-row groups per unit: partial slots and counters
   int32_t longest;         // longest automatic partition, 16-row tiles
+  int32_t max_tiles;       // longest partition the kernel takes, 16-row tiles
 };
 PrefillPlan prefill_plan(pkv_dtype dtype, int codes, int32_t head_dim, float scale) {
   const float c = scale * kLog2e;  // the LDS kernel applies c > 0 inside the exponent
   if (PKV_PREFILL_LDS && (codes == 0 || head_dim == 128) && dtype != PKV_F32 && c > 0.f && c <= 3.0e38f) {
     const int32_t groups = prefill_waves(head_dim) * PKV_PREFILL_LDS_ROWS;
-    return {true, groups * kTile, groups, kMaxPartitionBlocks};
+    return {true, groups * kTile, groups, kMaxPrefillTiles, kMaxPrefillTiles};
   }
   const int32_t kR = prefill_row_groups(dtype);
-  return {false, kR * kTile, kR, 64};
+  return {false, kR * kTile, kR, 64, kMaxPartitionBlocks};
 }
 // query tiles (work units) per (sequence, KV head) for a chunk of up to
 // max_q_len tokens
@@ -2833,7 +2842,8 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   if (num_blocks <= 0 || num_heads % num_kv_heads != 0 || elt_bytes(dtype) == 0) return PKV_EINVAL;
   if (!valid_block_size(block_size) || (head_dim != 64 && head_dim != 128)) return PKV_EUNSUPPORTED;
   if (layout != PKV_HND && layout != PKV_NHD) return PKV_EINVAL;
-  if (partition_blocks < 0 || static_cast<int64_t>(partition_blocks) * (block_size / kTile) > kMaxPartitionBlocks)
+  const PrefillPlan plan = prefill_plan(dtype, codes, head_dim, scale);
+  if (partition_blocks < 0 || static_cast<int64_t>(partition_blocks) * (block_size / kTile) > plan.max_tiles)
     return PKV_EINVAL;
   if (static_cast<int64_t>(num_blocks) * num_kv_heads * block_size > INT32_MAX) return PKV_EUNSUPPORTED;
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX) return PKV_EINVAL;
@@ -2842,7 +2852,6 @@ pkv_status prefill_entry(const void* q, const void* k_cache, const void* v_cache
   if (!q || !k_cache || !v_cache || !block_tables || !q_start || !context_lens || !out) return PKV_EINVAL;
   if (fp8 && (!k_scales || !v_scales)) return PKV_EINVAL;
   if (max_blocks_per_seq == 0) max_blocks_per_seq = 1;
-  const PrefillPlan plan = prefill_plan(dtype, codes, head_dim, scale);
   const PrefillSplit split = prefill_split(plan, num_seqs, num_heads, num_kv_heads, head_dim, max_q_len,
                                            max_blocks_per_seq, block_size, partition_blocks);
   const int64_t qt = split.q_tiles;

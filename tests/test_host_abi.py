@@ -261,7 +261,12 @@ def test_step_8bit_prefill_and_copy_reject_bad_arguments_without_gpu():
     assert pre(qs=None) == pkv.PKV_EINVAL
     assert pre(Hq=6, Hkv=4) == pkv.PKV_EINVAL
     assert pre(D=96) == pkv.PKV_EUNSUPPORTED
-    assert pre(pb=129) == pkv.PKV_EINVAL
+    # partition limits: 1024 tiles for the LDS kernel (16-bit caches, scale > 0),
+    # 128 for the one-wave kernel (fp32 caches, other scales)
+    assert pre(pb=1025) == pkv.PKV_EINVAL
+    assert pre(bs=64, pb=257) == pkv.PKV_EINVAL
+    assert pre(dt=0, pb=129) == pkv.PKV_EINVAL
+    assert pre(scale=-0.125, pb=129) == pkv.PKV_EINVAL
     assert pre(lay=2) == pkv.PKV_EINVAL
     assert pre(pb=1) == pkv.PKV_ESMALL  # several partitions per sequence, no workspace
     for fn in (lib.pkv_prefill_attention_fp8, lib.pkv_prefill_attention_int8):

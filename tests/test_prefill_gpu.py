@@ -78,6 +78,35 @@ def test_prefill_parity(torch_dev, layout, bs, dtype, shape):
         assert outs[0].tobytes() == outs[1].tobytes(), "repeated call differs"
 
 
+
+def test_prefill_partitions_at_the_table_limit(torch_dev):
+    """Contexts past the LDS kernel's longest partition (1024 tiles, 16384
+    tokens): the automatic choice gives a full-length partition plus a short
+    one, merged in the kernel; the longest explicit partition, and two
+    partitions of 520 tiles, give the reference too."""
+    torch, dev = torch_dev
+    chunks = ((16500, 48), (3000, 17), (16384 - 20, 20))
+    lens = np.array([a + c for a, c in chunks], np.int32)
+    q_start = np.concatenate([[0], np.cumsum([c for _, c in chunks])]).astype(np.int32)
+    cfg = wl.DecodeConfig("prefill_long", 0, 1, len(lens), 8, 1, 128, 16, "bf16", context_lens=tuple(lens))
+    wk = wl.make_host_workload(cfg, seed=7301)
+    kc, vc = wk.k_cache.copy(), wk.v_cache.copy()
+    oracle.kv_append(kc, vc, wk.k_new, wk.v_new, oracle.slot_mapping(wk.block_tables, lens - 1, 16), 16)
+    q = wl.draw_values(np.random.default_rng(3), (int(q_start[-1]), 8, 128), "bf16")
+    ref = oracle.prefill_attention(q, kc, vc, wk.block_tables, q_start, lens, cfg.scale, 1, 16, "bf16", "HND")
+    kcd, vcd, qd = (wl.raw_to_torch(x, "bf16", dev) for x in (kc, vc, q))
+    t = torch.from_numpy(np.ascontiguousarray(wk.block_tables, np.int32)).to(dev)
+    ld, qs = torch.from_numpy(lens).to(dev), torch.from_numpy(q_start).to(dev)
+    max_q = max(c for _, c in chunks)
+    for pb in (0, 1024, 520):
+        note(f"prefill at the table limit pb={pb}")
+        ws = pkv.alloc_prefill_workspace(qs, 8, kcd, t, max_q, pb)
+        assert ws is not None  # the longest context takes two partitions
+        out = torch.full_like(qd, float("nan"))
+        pkv.prefill_attention(qd, kcd, vcd, t, qs, max_q, ld, cfg.scale, out, ws, pb)
+        torch.cuda.synchronize()
+        check_close(oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16"), ref, "bf16", f"table limit pb={pb}")
+
 @pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 @pytest.mark.parametrize("dtype,shape,bs", [("bf16", (32, 8, 128), 16), ("f16", (16, 2, 128), 64),
