@@ -1607,7 +1607,9 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds1[kBuf];
   __shared__ __attribute__((aligned(16))) char lds2[kBufs > 2 ? kBuf : 16];
   __shared__ __attribute__((aligned(16))) char ldsx[kXBytes];
-  __shared__ int trows[kMaxPrefillTiles];  // the partition's tile rows (-1: id outside the pool)
+  // the partition's tile rows (-1: id outside the pool), then room for the
+  // reads of whole steps past its end (their entries are not used)
+  __shared__ __attribute__((aligned(16))) int trows[kMaxPrefillTiles + 8];
 
   // The lambdas below capture only locals: a lambda that referenced `a`
   // would take its address, and next to the cache -> LDS loads (which may
@@ -1666,7 +1668,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   const int r0 = wg_r0 + w * kR * kTile;
   const bool wave_rows = r0 < rows;
   const int n_w = wave_rows ? first + min(r0 + kR * kTile - 1, rows - 1) / a.group + 1 : 0;
-  const int min_limit = first + r0 / a.group + 1;  // the smallest key limit of the wave's rows
+  // the smallest key limit of the wave's rows (uniform: kept in a scalar register)
+  const int min_limit = __builtin_amdgcn_readfirstlane(first + r0 / a.group + 1);
   int my_limit[kR];
   bool head_ok[kR];
   size_t qidx[kR];
@@ -1704,17 +1707,38 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
     const int sub = lt - lb * m;
     return kNHD ? (bid * m + sub) * kTile * num_kv_heads + j : ((bid * num_kv_heads + j) * m + sub) * kTile;
   };
-  for (int t = tid; t < nblk; t += kThreads) trows[t] = blk0 + t < max_tiles ? tile_row0(blk0 + t) : -1;
+  // (a loop of fixed trip count: values computed in a loop whose exit
+  // depends on the lane would count as divergent after it)
+  static_assert(kMaxPrefillTiles % kThreads == 0, "table entries per thread");
+#pragma unroll
+  for (int i = 0; i < kMaxPrefillTiles / kThreads; ++i) {
+    const int t = tid + kThreads * i;
+    if (t < nblk) trows[t] = blk0 + t < max_tiles ? tile_row0(blk0 + t) : -1;
+  }
   __syncthreads();
   const int rs = kRowB * (kNHD ? a.num_kv_heads : 1);  // bytes between a head's consecutive token rows
   const int ss = kNHD ? 4 * a.num_kv_heads : 4;        // 8-bit: bytes between their scales
-  // first cache row of the partition's tile t and its rows to fetch: 0 past
-  // the partition end or for an id outside the pool (nothing is read then)
-  auto tile_src = [&](int t, int& valid) -> size_t {
-    const int r = __builtin_amdgcn_readfirstlane(trows[min(t, nblk - 1)]);
-    const bool ok = t < nblk && r >= 0;
-    valid = ok ? min(kTile, n_wg - (blk0 + t) * kTile) : 0;
-    return ok ? static_cast<size_t>(r) : 0;
+  // first cache row of each of step s's tiles and their rows to fetch, from
+  // one LDS read of the step's table entries: 0 past the partition end or for
+  // an id outside the pool (nothing is read then)
+  static_assert(kT * (kMaxPrefillTiles / kT + 2) <= kMaxPrefillTiles + 8, "table reads of steps past the end");
+  auto step_src = [&](int s, size_t (&row)[kT], int (&valid)[kT]) __attribute__((always_inline)) {
+    int e[kT];
+    if constexpr (kT == 4) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(trows + kT * s);
+      for (int u = 0; u < kT; ++u) e[u] = static_cast<int>(x[u]);
+    } else {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(trows + kT * s);
+      for (int u = 0; u < kT; ++u) e[u] = static_cast<int>(x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      const int t = kT * s + u;
+      const int r = __builtin_amdgcn_readfirstlane(e[u]);
+      const bool ok = t < nblk && r >= 0;
+      valid[u] = ok ? min(kTile, n_wg - (blk0 + t) * kTile) : 0;
+      row[u] = ok ? static_cast<size_t>(r) : 0;
+    }
   };
 
   const int nsteps = (nblk + kT - 1) / kT;  // steps of kT tiles
@@ -1723,11 +1747,12 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   // each tile's valid row count goes to `valid` for the step's softmax
   auto fetch = [&](int s, char* dst, int (&valid)[kT]) __attribute__((always_inline)) {
     __amdgpu_buffer_rsrc_t rk[kT], rv[kT];
+    size_t row[kT];
+    step_src(s, row, valid);
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
-      const size_t r0 = tile_src(kT * s + u, valid[u]);
-      rk[u] = tile_rsrc(k_cache + r0 * kRowB, valid[u] * rs);
-      rv[u] = tile_rsrc(v_cache + r0 * kRowB, valid[u] * rs);
+      rk[u] = tile_rsrc(k_cache + row[u] * kRowB, valid[u] * rs);
+      rv[u] = tile_rsrc(v_cache + row[u] * kRowB, valid[u] * rs);
     }
     // the tile of a wave's i-th load: t0, or t0 + 1 for the upper half of the
     // waves where one tile's K (or V) is half of what the workgroup loads at once
@@ -1779,9 +1804,8 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < kSLoads; ++i) {
         const int jj = w + kW * i, tile = jj >> 1;
-        int vv;
-        const size_t r0 = tile_src(kT * s + tile, vv);
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(((jj & 1) ? v_scales : k_scales) + r0 * 4, vv * ss);
+        const __amdgpu_buffer_rsrc_t r =
+            tile_rsrc(((jj & 1) ? v_scales : k_scales) + row[tile] * 4, valid[tile] * ss);
         if (lane < kTile)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               r, lds_ptr(dst + kKBytes + kVBytes + (jj & 1) * (kT * kTile * 4) + tile * (kTile * 4)), 4, lane * ss,
@@ -1882,7 +1906,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
         // zero); keys past a row's position are masked: lane (q4, .) keeps
         // its rows 4*q4 + i below both limits (the test to enter is wave-uniform)
         const int key = key0 + u * kTile;
-        if (valid[u] < kTile || key + kTile > min_limit) {
+        if (__builtin_amdgcn_readfirstlane(valid[u]) < kTile || key + kTile > min_limit) {
           const int lim = min(valid[u], my_limit[rg] - key) - 4 * q4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) sc[rg][u][i] = i < lim ? sc[rg][u][i] : kNegInf;
