@@ -1896,22 +1896,31 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   auto attend = [&](const char* vl, int s, f32x4 (&sc)[kR][kT], const int (&valid)[kT], const char* sl)
                     __attribute__((always_inline)) {
     const int key0 = (blk0 + kT * s) * kTile;
+    // rows past a tile's valid count were not fetched (they read as zero);
+    // keys past a row's position are masked: lane (q4, .) keeps its rows
+    // 4*q4 + i below both limits. The tests are wave-uniform, and a step of
+    // full tiles below every row's limit (all but a partition's last ones)
+    // skips them with one.
+    int vmin = kTile;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) vmin = min(vmin, __builtin_amdgcn_readfirstlane(valid[u]));
+    if (vmin < kTile || key0 + kT * kTile > min_limit) {
+#pragma unroll
+      for (int rg = 0; rg < kR; ++rg)
+#pragma unroll
+        for (int u = 0; u < kT; ++u) {
+          const int key = key0 + u * kTile;
+          if (__builtin_amdgcn_readfirstlane(valid[u]) < kTile || key + kTile > min_limit) {
+            const int lim = min(valid[u], my_limit[rg] - key) - 4 * q4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[rg][u][i] = i < lim ? sc[rg][u][i] : kNegInf;
+          }
+        }
+    }
     float mx[kR];
     bool grow_any = false;
 #pragma unroll
     for (int rg = 0; rg < kR; ++rg) {
-#pragma unroll
-      for (int u = 0; u < kT; ++u) {
-        // rows past a tile's valid count were not fetched (they read as
-        // zero); keys past a row's position are masked: lane (q4, .) keeps
-        // its rows 4*q4 + i below both limits (the test to enter is wave-uniform)
-        const int key = key0 + u * kTile;
-        if (__builtin_amdgcn_readfirstlane(valid[u]) < kTile || key + kTile > min_limit) {
-          const int lim = min(valid[u], my_limit[rg] - key) - 4 * q4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[rg][u][i] = i < lim ? sc[rg][u][i] : kNegInf;
-        }
-      }
       float m4 = kNegInf;
 #pragma unroll
       for (int u = 0; u < kT; ++u)
