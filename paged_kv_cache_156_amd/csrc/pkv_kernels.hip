@@ -101,6 +101,11 @@ constexpr int kMaxPrefillTiles = PKV_PREFILL_MAX_TILES;
 #ifndef PKV_PAIR_RING_8BIT  // the same for 8-bit caches
 #define PKV_PAIR_RING_8BIT 2
 #endif
+#ifndef PKV_KRING_8BIT  // 8-bit K of head size 128 (HND) through a per-wave LDS ring
+#define PKV_KRING_8BIT 1
+#endif
+// bytes of that ring per wave: the ring's tiles of 16 rows x 128 codes
+constexpr size_t kKRingWaveBytes = size_t(2) * PKV_PAIR_RING_8BIT * 16 * 128;
 #ifndef PKV_RING_ROTATIONS
 #define PKV_RING_ROTATIONS 3
 #endif
@@ -338,7 +343,7 @@ __device__ __forceinline__ int k_slice_elt(int q4, int e) {
 
 // rs: code row stride in bytes (D for HND, num_kv_heads * D for NHD); the
 // scales of consecutive rows are adjacent for HND and num_kv_heads apart for NHD.
-template <int D, bool kNHD>
+template <int D, bool kNHD, bool kLoadK = true>
 __device__ __forceinline__ void load_block_fp8(Fp8Regs<D>& r, const char* kt, const char* vt, const char* kst,
                                                const char* vst, int rows, int q4, int ln, int rs) {
   const int ss = kNHD ? rs / D * 4 : 4;  // scale row stride, bytes
@@ -347,7 +352,7 @@ __device__ __forceinline__ void load_block_fp8(Fp8Regs<D>& r, const char* kt, co
   const __amdgpu_buffer_rsrc_t rks = tile_rsrc(kst, rows * ss);
   const __amdgpu_buffer_rsrc_t rvs = tile_rsrc(vst, rows * ss);
 #pragma unroll
-  for (int c = 0; c < D / 64; ++c) {
+  for (int c = 0; c < (kLoadK ? D / 64 : 0); ++c) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ln * rs + (q4 + 4 * c) * 16, 0, kCacheNT);
     r.k[c] = u32x4{v[0], v[1], v[2], v[3]};
   }
@@ -1055,12 +1060,67 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
     if (kStep && t == new_t) rows = new_row;  // the new row comes from registers
     return ok ? static_cast<size_t>(r0) : 0;
   };
-  auto load_ring = [&](R& r, size_t row0, int rows) {
-    if constexpr (kFp8) {
+  // 8-bit K of head size 128 in HND caches goes through a per-wave LDS ring
+  // (one 2 KiB slot per ring tile, in the dynamic LDS after the workgroup
+  // merge area). Read straight into registers, a lane's K takes 64 bytes of
+  // each of 16 rows per load, which measured 4-5% of the stream rate below
+  // 1 KiB-contiguous loads; here every load takes 8 whole rows and the MFMA
+  // operands come back with one LDS read per 16-byte chunk. Slot byte
+  // 1024 h + 16 (8 r + (c ^ r)) holds chunk c of tile row 8 h + r (r < 8), so
+  // the reads of 8 consecutive lanes (rows r = 0..7, one chunk each) fall in 8
+  // different 16-byte bank groups.
+  constexpr bool kKLds = kFp8 && !kNHD && D == 128 && !kPrefill && PKV_KRING_8BIT && PKV_DECODE_PAIRS;
+  char* const kring = pkv_dyn_lds + (kWgParts ? wg_merge_lds_bytes(W, D) : 0) + wv * kKRingWaveBytes;
+  auto load_ring = [&](int slot, R& r, size_t row0, int rows) {
+    if constexpr (kKLds) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k_cache + row0 * D, rows * rs);
+      char* const kl = kring + slot * (16 * D);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + (lane >> 3), chunk = (lane & 7) ^ (lane >> 3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(kl + h * 1024), 16, row * rs + chunk * 16, 0, 0,
+                                                 kCacheNT);
+      }
+      // the tile's V and scale loads (kRingVSLoads of them) are issued after
+      // its K loads: read_k's wait counts on that order
+      __builtin_amdgcn_sched_barrier(0);
+      load_block_fp8<D, kNHD, false>(r, a.k_cache + row0 * D, a.v_cache + row0 * D, a.k_scales + row0 * 4,
+                                     a.v_scales + row0 * 4, rows, q4, ln, rs);
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (kFp8) {
+      (void)slot;
       load_block_fp8<D, kNHD>(r, a.k_cache + row0 * D, a.v_cache + row0 * D, a.k_scales + row0 * 4,
                               a.v_scales + row0 * 4, rows, q4, ln, rs);
     } else {
+      (void)slot;
       load_block<T, D>(r, a.k_cache + row0 * S::kRowBytes, a.v_cache + row0 * S::kRowBytes, rows, q4, ln, rs);
+    }
+  };
+  // Loads into LDS are not waited for by the compiler, so before a pair's K
+  // is read the wave drains its own loads down to those issued after that
+  // pair's last K load: the last tile's V and scale loads, then the next
+  // pair's loads (issued first, so that two pairs stay in flight)
+  constexpr int kRingVSLoads = 4 + 2;  // V: four 8-byte row loads; scales: two 16-byte loads (HND)
+  constexpr int kRingNewer = kRingVSLoads + 2 * (2 + kRingVSLoads);
+  static_assert(kRingNewer < 64, "vmcnt field");
+  auto wait_ring_k = [&]() __attribute__((always_inline)) {
+    if constexpr (kKLds) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      // vmcnt <= kRingNewer (bits 3:0 and 15:14), expcnt and lgkmcnt: no wait
+      __builtin_amdgcn_s_waitcnt(((kRingNewer & 0x30) << 10) | 0xF70 | (kRingNewer & 0xF));
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+  };
+  // the ring slot's K into the MFMA operand registers: lane (q4, r) takes
+  // chunks q4 and q4 + 4 of tile row r
+  auto read_k = [&](int slot, R& r) __attribute__((always_inline)) {
+    if constexpr (kKLds) {
+      const char* const kl = kring + slot * (16 * D) + (ln >> 3) * 1024 + (ln & 7) * 128;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kl + 16 * ((q4 + 4 * c) ^ (ln & 7)));
+    } else {
+      (void)slot;
+      (void)r;
     }
   };
 
@@ -1315,7 +1375,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 #pragma unroll
       for (int u = 0; u < 2 * (kNP - 1); ++u) {
         const size_t tile = block_src(u, ring_rows[u]);
-        load_ring(ring[u], tile, ring_rows[u]);
+        load_ring(u, ring[u], tile, ring_rows[u]);
       }
       // 8-bit caches: the new row, read right after the table, is quantized
       // while the first tiles are in flight (only the quantized row stays live)
@@ -1328,19 +1388,25 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const size_t tile = block_src(t0 + 2 * (pp + kNP - 1) + u, ring_rows[nxt + u]);
-            load_ring(ring[nxt + u], tile, ring_rows[nxt + u]);
+            load_ring(nxt + u, ring[nxt + u], tile, ring_rows[nxt + u]);
           }
           __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
-          if (t0 + 2 * pp < nblk)
+          if (t0 + 2 * pp < nblk) {  // wave-uniform
+            // the LDS-ring K of this pair (its slots were last read a pair ago)
+            wait_ring_k();
+            read_k(cur, ring[cur]);
+            read_k(cur + 1, ring[cur + 1]);
             process_pair(ring[cur], ring_rows[cur], t0 + 2 * pp, ring[cur + 1], ring_rows[cur + 1], t0 + 2 * pp + 1);
+          }
         }
       }
+      if constexpr (kKLds) __builtin_amdgcn_s_waitcnt(0xF70);  // no load into LDS outlives the loop
     }
   } else if (nblk > 0) {  // wave-uniform; nblk == 0 only for an empty sequence
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
       const size_t tile = block_src(u, ring_rows[u]);
-      load_ring(ring[u], tile, ring_rows[u]);
+      load_ring(u, ring[u], tile, ring_rows[u]);
     }
     // several ring rotations per loop iteration: only the first block after
     // the back-edge may see a conservative wait
@@ -1351,7 +1417,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
         const int u = uu % kRing;
         const int slot = (u + kAhead) % kRing;
         const size_t tile = block_src(t0 + uu + kAhead, ring_rows[slot]);
-        load_ring(ring[slot], tile, ring_rows[slot]);
+        load_ring(slot, ring[slot], tile, ring_rows[slot]);
         __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any wait below
         if (t0 + uu < nblk) process(ring[u], ring_rows[u], t0 + uu);
       }
@@ -2549,6 +2615,9 @@ int decode_waves(int64_t waves, int32_t num_kv_heads) {
 template <typename T, int D, int kQ, bool kNHD>
 pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases, hipStream_t stream) {
   static_assert(kDecodeWaves<kModeSplit> == kDecodeWaves<kModeStep>, "one bound for both modes");
+  // dynamic LDS of the per-wave K ring (8-bit caches of head size 128, HND)
+  constexpr bool kRingLds = kQ != 0 && !kNHD && D == 128 && PKV_KRING_8BIT && PKV_DECODE_PAIRS;
+  auto ring_bytes = [](int waves) { return kRingLds ? static_cast<size_t>(waves) * kKRingWaveBytes : size_t(0); };
   // waves = consecutive KV heads of one partition
   const int w = decode_waves(static_cast<int64_t>(a.num_parts) * a.num_kv_heads * a.head_groups * num_seqs,
                              a.num_kv_heads);
@@ -2561,8 +2630,8 @@ pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases,
         std::array<int, PKV_DECODE_WAVES + 1> r{};
         for (int v = 2; v <= PKV_DECODE_WAVES; v *= 2) {
           int nb = 0;
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64 * v, wg_merge_lds_bytes(v, D)) !=
-              hipSuccess)
+          const size_t lds = wg_merge_lds_bytes(v, D) + (kRingLds ? static_cast<size_t>(v) * kKRingWaveBytes : 0);
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64 * v, lds) != hipSuccess)
             nb = 0;  // unknown: the grouped mapping is not used
           r[v] = nb;
         }
@@ -2573,15 +2642,17 @@ pkv_status launch_decode(const DecodeArgs& a, int32_t num_seqs, unsigned phases,
       if (wp > 1) {
         const dim3 g(static_cast<unsigned>(ceil_div64(a.num_parts, wp)),
                      static_cast<unsigned>(a.num_kv_heads * a.head_groups), num_seqs);
-        hipLaunchKernelGGL(kernel, g, dim3(64 * wp), wg_merge_lds_bytes(wp, D), stream, a);
+        hipLaunchKernelGGL(kernel, g, dim3(64 * wp), wg_merge_lds_bytes(wp, D) + ring_bytes(wp), stream, a);
         return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
       }
     }
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64 * w), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeStep, kQ, kNHD>), grid, dim3(64 * w), ring_bytes(w), stream,
+                       a);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
   if (phases & kPartitions)
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kQ, kNHD>), grid, dim3(64 * w), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kModeSplit, kQ, kNHD>), grid, dim3(64 * w), ring_bytes(w),
+                       stream, a);
   if ((phases & kMerge) && a.num_parts > 1) {
     const int64_t waves = static_cast<int64_t>(num_seqs) * a.num_heads;
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3(static_cast<unsigned>(ceil_div64(waves, 4))), dim3(256), 0, stream,
