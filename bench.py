@@ -59,10 +59,11 @@ def copy_calibration(args, torch, dev):
 def settle(fn, torch, settle_ms):
     """Repeat `fn` untimed until the GPU has run it for `settle_ms` (batches of
     about 5 ms, host clock around each synchronised batch); returns the count.
-    MFMA-bound kernels start below their sustained clock: the 70B prefill
-    launch measured ~25% slower over its first ~60 ms of back-to-back work than
-    afterwards, while the HBM-bound launches run at their final rate from the
-    second one on."""
+    Launches start below their sustained rate: the 70B prefill launch (MFMA
+    bound) measured ~25% slower over its first ~60 ms of back-to-back work
+    than afterwards; the 70B 8-bit decode launch ran at its final rate for
+    about 2 ms, then 10-20% slower (INT8) or 2-5% slower (E4M3) until about
+    15 ms in (16-bit: within 1% throughout)."""
     if settle_ms <= 0:
         return 0
     torch.cuda.synchronize()
@@ -433,8 +434,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--settle-ms", type=float, default=None,
-                    help="--op prefill: after the warm-up, repeat the launch untimed for this long before the "
-                         "timed steps (default 200: its MFMA-bound launches speed up with the clock)")
+                    help="after the warm-up, repeat the step (or launch) untimed for this long before the timed "
+                         "steps (default 200: launches reach their sustained rate after some ms of work)")
     ap.add_argument("--config", default="llama3_70b")
     ap.add_argument("--layers", type=int, default=0, help="layers to loop (0 = the configuration's count)")
     ap.add_argument("--partition-blocks", type=int, default=0, help="blocks per partition (0 = library choice)")
@@ -594,6 +595,9 @@ def main():
         step()
     torch.cuda.synchronize()
     assert all(torch.isfinite(o).all().item() for o in outs[:2]), "non-finite attention output"
+    settle_ms = 200.0 if args.settle_ms is None else args.settle_ms
+    settled = settle(step, torch, settle_ms)
+    log(f"settle: {settled} untimed steps over {settle_ms:.0f} ms")
 
     # timed region: K steps back to back, bracketed by events on the launch stream
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -702,6 +706,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": settle_ms, "steps": settled},
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "ms_per_step_min": round(float(np.min(step_ms)), 4),

@@ -3,7 +3,7 @@ per-row scales) against the CPU reference.
 
 The quantizing append (separate kernel and fused into the decode step) must
 match the reference bit for bit: codes and fp32 scales. Attention over the
-FP8 cache is compared with the reference attention over the dequantized
+8-bit cache is compared with the reference attention over the dequantized
 values (code * scale, exact in float64) at the 16-bit tolerance
 |gpu - ref| <= 2e-3 + 1e-2 |ref|: the kernel converts codes exactly, so only
 fp32 accumulation, the weight split and output rounding separate the two.
@@ -208,6 +208,63 @@ def test_fp8_attention_and_fused_step(torch_dev, q_dtype, shape, fmt):
         assert_caches_equal(torch, d, kc, vc, ks, vs, "fp8 fused step")
         check_close(oracle.upcast(outs[0], q_dtype), ref, f"fp8 fused {shape} pb={pb}")
         assert outs[0].tobytes() == outs[1].tobytes()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_8bit_query_rows_wide_range_and_non_finite(torch_dev, fmt):
+    """Query rows far from unit scale, through the split path and the fused
+    step: rows with one element 4096 times the rest, elements spread over
+    2^-40 .. 2^10, rows scaled by 2^-100 and 2^40, and zero rows stay within
+    the 16-bit tolerance of the reference (the scores stay in fp32 range and
+    the softmax takes their maximum out first); a row holding NaN or +-Inf
+    gives NaN in all of its outputs, as the reference does."""
+    torch, dev = torch_dev
+    cfg = wl.DecodeConfig("qrows8", 0, 1, 4, 32, 2, 128, 16, "bf16", context_lens=(40, 100, 17, 300))
+    wk = wl.make_host_workload_fp8(cfg, seed=6100)
+    q = oracle.upcast(wk.q, "bf16")
+    rng = np.random.default_rng(6101)
+    B, Hq, D = q.shape
+    for h0 in (0, 16):  # the first heads of both KV heads' groups
+        q[:, h0, 5] = 4096.0 * np.abs(q[:, h0]).max(axis=1)   # one outlier element
+        q[:, h0 + 1] *= np.exp2(rng.uniform(-40, 10, size=(B, D)))  # log-spread magnitudes
+        q[:, h0 + 2] *= 2.0 ** -100
+        q[:, h0 + 3] *= 2.0 ** 40
+        q[:, h0 + 4] = 0.0
+    bad = {(0, 6): np.nan, (1, 6): np.inf, (2, 22): -np.inf, (3, 22): np.nan}
+    for (b, h), val in bad.items():
+        q[b, h, 17] = val
+    wk.q = wl.f32_to_bf16_bits(q.astype(np.float32))
+    ref, kc, vc, ks, vs = oracle_fp8(wk, fmt)
+    finite = np.ones((B, Hq), bool)
+    for b, h in bad:
+        finite[b, h] = False
+
+    def check(out, what):
+        got = oracle.upcast(wl.torch_to_raw(out, "bf16"), "bf16")
+        assert np.isnan(got[~finite]).all(), f"{what}: a non-finite query row gave a non-NaN output"
+        check_close(got[finite], ref[finite], what)
+
+    for pb in (0, 2):
+        note(f"{fmt} query rows far from unit scale, pb={pb}: split path")
+        d = to_dev(torch, dev, wk)
+        slots = pkv.slot_mapping_from_tables(wk.block_tables, wk.context_lens - 1, 16)
+        pkv.kv_append_fp8(d["kn"], d["vn"], torch.from_numpy(slots).to(dev), d["kc"], d["vc"], d["ks"], d["vs"],
+                          fmt=fmt)
+        out = torch.full_like(d["q"], 7.0)
+        ws = pkv.alloc_workspace(d["q"], d["kc"], d["t"], pb)
+        pkv.paged_decode_attention_fp8(d["q"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"], cfg.scale,
+                                       out, ws, pb, fmt=fmt)
+        torch.cuda.synchronize()
+        check(out, f"{fmt} split pb={pb}")
+        note(f"{fmt} query rows far from unit scale, pb={pb}: fused step")
+        d = to_dev(torch, dev, wk)
+        ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], pb)
+        out = torch.full_like(d["q"], 7.0)
+        pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                            cfg.scale, out, ws, pb, fmt=fmt)
+        torch.cuda.synchronize()
+        assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} fused step")
+        check(out, f"{fmt} fused pb={pb}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
