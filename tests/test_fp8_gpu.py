@@ -296,6 +296,35 @@ def test_8bit_fused_step_grouped_workgroups_ragged(torch_dev, fmt, pb):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_8bit_fused_step_grouped_grid_with_a_tail(torch_dev, fmt):
+    """65 sequences x 4 KV heads, lengths 17 .. 128 and partitions of 4
+    tiles: on a 256-CU MI355X the fused step's 8-bit workgroups are
+    partition-grouped with two partitions each, 260 workgroups. Their head
+    pairs run back to back on one XCD (linear ids L and L + 8); the 260 mod
+    16 = 4 workgroups past the last full run of 16 pair up on consecutive
+    ids instead."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(71)
+    lens = tuple([65, 128, 17, 80, 127] + rng.integers(65, 129, size=60).tolist())
+    cfg = wl.DecodeConfig("tail8", 0, 1, 65, 28, 4, 128, 16, "bf16", context_lens=lens)
+    wk = wl.make_host_workload_fp8(cfg, seed=7100)
+    ref, kc, vc, ks, vs = oracle_fp8(wk, fmt)
+    note(f"{fmt} fused step, grouped grid with a tail of workgroups")
+    d = to_dev(torch, dev, wk)
+    ws = pkv.alloc_step_workspace(d["q"], d["kc"], d["t"], 4)
+    outs = []
+    for _ in range(2):
+        out = torch.full_like(d["q"], float("nan"))
+        pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                            cfg.scale, out, ws, 4, fmt=fmt)
+        torch.cuda.synchronize()
+        outs.append(wl.torch_to_raw(out, "bf16"))
+    assert_caches_equal(torch, d, kc, vc, ks, vs, f"{fmt} grouped fused step with a tail")
+    check_close(oracle.upcast(outs[0], "bf16"), ref, f"{fmt} grouped fused step with a tail")
+    assert outs[0].tobytes() == outs[1].tobytes()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_8bit_fused_step_multi_round_ragged(torch_dev, fmt):
     """The fused step over 8-bit caches on a grid of several rounds of
     workgroups: 64 ragged sequences (zero lengths included) x 4 KV heads,
