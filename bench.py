@@ -428,9 +428,8 @@ def run_prefill(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # 30 timed steps: the first step after the warm-up's synchronisation runs a few percent
-    # slow, which over 10 steps took 1-2% off the mean (8-bit 70B: 5837-5876 GB/s at 10
-    # steps, 5958 at 30, 5983 at 100, against a median step of 5983)
+    # 30 timed steps (about 200 ms on the 70B shape), after the settle phase below: a slow
+    # stretch of a few ms then weighs less in the mean than over 10 steps
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--settle-ms", type=float, default=None,
