@@ -402,6 +402,20 @@ def test_8bit_full_size_70b_every_sequence(torch_dev, fmt):
     check_full_size_8bit(torch, dev, cfg, list(range(cfg.num_seqs)), fmt, f"{fmt} 70B")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("cfg_name", ["llama3_8b_layer", "mha_contrast"])
+def test_8bit_full_size_small_launches_every_sequence(torch_dev, cfg_name, fmt):
+    """The 8B layer and the MHA contrast over 8-bit caches, every sequence.
+    The 8B layer's fused step merges four partition groups per unit through
+    global memory, with its KV head pairs' workgroups renumbered onto one
+    XCD; the MHA shape (one query head per KV head) keeps the plain
+    numbering."""
+    torch, dev = torch_dev
+    cfg = wl.CONFIG_BY_NAME[cfg_name]
+    note(f"{fmt} full-size {cfg.name} layer, fused step: every sequence")
+    check_full_size_8bit(torch, dev, cfg, list(range(cfg.num_seqs)), fmt, f"{fmt} {cfg.name}")
+
+
 def test_fp8_full_size_ragged_every_partition_count(torch_dev):
     """The ragged Qwen2.5-7B batch over E4M3 caches: at least 16 sequences,
     one of every partition count the launch produces."""
