@@ -605,7 +605,8 @@ struct MergeSpace {
 template <int D, int kR, typename WriteOut>
 __device__ __forceinline__ void fused_merge(const MergeSpace a, size_t unit, int p, int nparts, int lane,
                                             f32x4 (&acc)[kR][D / 16], const float (&m_run)[kR],
-                                            const float (&l_tot)[kR], const float (&inv)[kR], WriteOut& write_out) {
+                                            const float (&l_tot)[kR], const float (&inv)[kR], WriteOut& write_out,
+                                            const bool (&row_ok)[kR]) {
   constexpr int kE = D / 16;
   constexpr int kChunks = kE;  // 16-byte chunks per lane: 4*E floats
   const int ln = lane & 15;
@@ -630,9 +631,10 @@ __device__ __forceinline__ void fused_merge(const MergeSpace a, size_t unit, int
         const int idx = 4 * k + e;  // value index i * E + mt
         v[e] = acc[rg][idx % kE][idx / kE] * inv[rg];
       }
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                   __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                             ro, (p * kChunks + k) * 1024 + lane * 16, 0, kCacheDeviceCoherent);
+      if (row_ok[rg])  // a lane holds one query row's values: padding rows are neither stored nor read
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                     __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                               ro, (p * kChunks + k) * 1024 + lane * 16, 0, kCacheDeviceCoherent);
     }
     if (lane < 16)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run[rg] + __builtin_amdgcn_logf(l_tot[rg])), rl,
@@ -662,9 +664,12 @@ __device__ __forceinline__ void fused_merge(const MergeSpace a, size_t unit, int
             __builtin_amdgcn_raw_buffer_load_b32(rl, (pp0 + u) * 64 + ln * 4, 0, kCacheDeviceCoherent));
 #pragma unroll
         for (int k = 0; k < kChunks; ++k) {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b128(ro, ((pp0 + u) * kChunks + k) * 1024 + lane * 16, 0,
-                                                               kCacheDeviceCoherent);
-          ov[u][k] = u32x4{x[0], x[1], x[2], x[3]};
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (row_ok[rg])
+            x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              ro, ((pp0 + u) * kChunks + k) * 1024 + lane * 16, 0,
+                                              kCacheDeviceCoherent));
+          ov[u][k] = x;
         }
       }
 #pragma unroll
@@ -1582,7 +1587,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
         l_tot[0] = L;
         inv[0] = 1.0f / L;
       }
-      fused_merge<D, kR>(ms, unit, xr, ngroups, lane, acc, m_run, l_tot, inv, write_out);
+      fused_merge<D, kR>(ms, unit, xr, ngroups, lane, acc, m_run, l_tot, inv, write_out, head_ok);
       return;
     }
   }
@@ -1603,7 +1608,7 @@ __global__ __launch_bounds__((64 * kDecodeWaves<kMode>)) void decode_partition_k
   } else {
     const size_t unit = (static_cast<size_t>(b) * a.num_kv_heads + j) * units_per_head + ui;
     fused_merge<D, kR>(MergeSpace{a.ws_o, a.ws_lse, a.counters, a.num_parts}, unit, p, nparts, lane, acc, m_run,
-                       l_tot, inv, write_out);
+                       l_tot, inv, write_out, head_ok);
   }
 }
 
@@ -2281,7 +2286,7 @@ __global__ __launch_bounds__(64 * kW) void prefill_lds_kernel(DecodeArgs a) {
   }
   const size_t unit = ((static_cast<size_t>(b) * a.num_kv_heads + j) * a.q_tiles + ui) * kW + w;  // one per wave
   fused_merge<D, kR>(MergeSpace{a.ws_o, a.ws_lse, a.counters, a.num_parts}, unit, p, nparts, lane, acc, m_run, l_tot,
-                     inv, write_out);
+                     inv, write_out, head_ok);
 }
 
 // ---------------------------------------------------------------------------
