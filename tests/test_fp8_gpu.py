@@ -325,6 +325,54 @@ def test_8bit_fused_step_grouped_grid_with_a_tail(torch_dev, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_8bit_fused_step_replays_under_graph_capture(torch_dev, fmt):
+    """Two layers' 8-bit fused steps over the grouped grid with a tail (65
+    sequences x 4 KV heads, partitions of 4 tiles: partition-grouped
+    workgroups, head pairs on one XCD) captured in one graph and replayed
+    three times, with eager work on the same stream between the replays:
+    every replay's outputs and both layers' code and scale pools equal the
+    eager run's bit for bit."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(72)
+    lens = tuple([65, 128, 17, 80, 127] + rng.integers(65, 129, size=60).tolist())
+    cfg = wl.DecodeConfig("graph8", 0, 2, 65, 28, 4, 128, 16, "bf16", context_lens=lens)
+    wk = wl.make_host_workload_fp8(cfg, seed=7200)
+    ref, kc, vc, ks, vs = oracle_fp8(wk, fmt)
+    layers = [to_dev(torch, dev, wk) for _ in range(2)]
+    ws = [pkv.alloc_step_workspace(layers[0]["q"], layers[0]["kc"], layers[0]["t"], 4) for _ in range(2)]
+    outs = [torch.empty_like(layers[0]["q"]) for _ in range(2)]
+
+    def steps():
+        for layer in range(2):
+            d = layers[layer]
+            pkv.decode_step_fp8(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], d["ks"], d["vs"], d["t"], d["lens"],
+                                cfg.scale, outs[layer], ws[layer], 4, fmt=fmt)
+
+    note(f"{fmt} fused step: eager reference, then graph capture and replays")
+    steps()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    pools = [[x.clone() for x in (d["kc"], d["vc"], d["ks"], d["vs"])] for d in layers]
+    check_close(oracle.upcast(wl.torch_to_raw(eager[0], "bf16"), "bf16"), ref, f"{fmt} graph eager")
+    assert_caches_equal(torch, layers[0], kc, vc, ks, vs, f"{fmt} graph eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan"))  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer in range(2):
+            assert torch.equal(outs[layer], eager[layer]), f"{fmt} replay {r} layer {layer} differs"
+            for x, y in zip((layers[layer][k] for k in ("kc", "vc", "ks", "vs")), pools[layer]):
+                # bytes, not values: the scale pools hold NaN in their unused rows
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"{fmt} replay {r} layer {layer}: pools differ"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_8bit_fused_step_multi_round_ragged(torch_dev, fmt):
     """The fused step over 8-bit caches on a grid of several rounds of
     workgroups: 64 ragged sequences (zero lengths included) x 4 KV heads,
