@@ -1,0 +1,57 @@
+"""Host-side behaviour of bench.py that needs no GPU: the one-GPU guard and
+the settle phase that runs before the timed steps."""
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def run_bench(args, env_extra=None):
+    env = dict(os.environ, **(env_extra or {}))
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          env=env, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = run_bench(["--gpus", "2"])
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_a_multi_rank_launch_is_refused():
+    r = run_bench([], {"WORLD_SIZE": "2"})
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+class _Clock:
+    """Stand-in for the torch module: synchronize() does nothing."""
+
+    @staticmethod
+    def synchronize():
+        pass
+
+
+def test_settle_repeats_the_step_for_the_requested_time():
+    calls = []
+
+    def step():
+        calls.append(1)
+        time.sleep(0.002)
+
+    t0 = time.perf_counter()
+    n = bench.settle(step, type("T", (), {"cuda": _Clock}), 40.0)
+    took = (time.perf_counter() - t0) * 1e3
+    assert n == len(calls) and n >= 5
+    assert 30.0 <= took <= 400.0
+
+
+def test_settle_of_zero_runs_nothing():
+    calls = []
+    assert bench.settle(lambda: calls.append(1), None, 0.0) == 0
+    assert calls == []
