@@ -143,6 +143,21 @@ def pools_after(wkd, fp8, dt):
     return [wl_raw(wkd.k_cache[0], dt), wl_raw(wkd.v_cache[0], dt)]
 
 
+def decode_alg_bytes(lens, Hq, Hkv, D, esz, bs, fp8, fused):
+    """Algorithmic bytes of one decode launch over one layer, as
+    (K/V bytes, launch bytes): every cached K/V row read once (8-bit caches:
+    the codes plus one fp32 scale per row), the queries read and the outputs
+    written, the block-table entries each sequence reads plus its length, and
+    for the fused step the new token's K/V read and its row written."""
+    B = len(lens)
+    sum_n = int(sum(int(n) for n in lens))
+    kv_layer = 2 * Hkv * (D + 4) * sum_n if fp8 else 2 * Hkv * D * esz * sum_n
+    q_out = 2 * B * Hq * D * esz
+    tables = 4 * sum(-(-int(n) // bs) for n in lens) + 4 * B
+    append = 2 * B * Hkv * D * esz + (2 * B * Hkv * (D + 4) if fp8 else 2 * B * Hkv * D * esz)
+    return kv_layer, kv_layer + q_out + tables + (append if fused else 0)
+
+
 def oracle_check(snap, out0, after, cfg, layout, fp8, fmt, budget_s, min_seqs=32):
     """The CPU reference on layer 0, timed, and compared with the GPU.
 
@@ -527,9 +542,9 @@ def main():
     slots_d = torch.from_numpy(slots).to(dev)
     outs = [torch.empty_like(wkd.q[l]) for l in range(L)]
     stream = torch.cuda.current_stream()
-    # K/V bytes read per layer: codes + one fp32 scale per row for 8-bit caches
-    sum_n = int(lens.sum())
-    kv_layer = 2 * Hkv * (D + 4) * sum_n if fp8 else 2 * Hkv * D * esz * sum_n
+    # K/V bytes read per layer (8-bit caches: codes + one fp32 scale per row)
+    # and the algorithmic bytes of one launch
+    kv_layer, part_alg = decode_alg_bytes(lens, Hq, Hkv, D, esz, bs, fp8, fused)
     step_kv = kv_layer * L
 
     if args.op == "stream":
@@ -657,11 +672,6 @@ def main():
     part_avg_ms = total_ms / (args.steps * L) if fused else event_avg_ms
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; partition kernel avg {part_avg_ms * 1e3:.1f} us")
 
-    # algorithmic bytes
-    q_out = 2 * B * Hq * D * esz
-    tables = 4 * sum(-(-int(n) // bs) for n in lens) + 4 * B
-    append = 2 * B * Hkv * D * esz + (2 * B * Hkv * (D + 4) if fp8 else 2 * B * Hkv * D * esz)  # fused step only
-    part_alg = kv_layer + q_out + tables + (append if fused else 0)
     gbs = step_kv / (ms_per_step * 1e-3) / 1e9
     achieved = part_alg / (part_avg_ms * 1e-3) / 1e9
 
